@@ -1,0 +1,496 @@
+"""Pins that tie the fp64 oracle to the pages and to mathematics.
+
+Nothing here calls the GPU library. Each test checks the oracle against
+something other than itself: a brute-force evaluation of the textbook
+(non-max-subtracted) formula in 50-digit arithmetic, closed forms, invariants
+of the definition, reductions between the three entry points, and values the
+pages print.
+"""
+import json
+import math
+import os
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import metrics
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+mpmath.mp.dps = 50
+
+
+# ---------------------------------------------------------------------------
+# Brute force: the textbook formula P = exp(S) / sum exp(S) with no max
+# subtraction, in 50-digit arithmetic, with the key set of each row built by
+# explicit loops from the definitions of the causal mask, the boolean mask
+# (1 = excluded), GQA (kv head = q head // group), sequence lengths, block
+# lists and top-k lists.
+# ---------------------------------------------------------------------------
+
+def _naive_row(qv, keys, kf, vf, scale):
+    if not keys:
+        return None, None
+    s = [mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(float(a)) * mpmath.mpf(float(b))
+                                         for a, b in zip(qv, kf(j))) for j in keys]
+    ex = [mpmath.e ** x for x in s]
+    den = mpmath.fsum(ex)
+    out = []
+    for d in range(len(vf(keys[0]))):
+        out.append(mpmath.fsum(ex[n] * mpmath.mpf(float(vf(j)[d])) for n, j in enumerate(keys)) / den)
+    return [float(x) for x in out], float(mpmath.log(den))
+
+
+def _compare(o, lse, ref_rows, Dv):
+    for r, (ro, rl) in enumerate(ref_rows):
+        if ro is None:
+            assert np.all(o[r] == 0.0)
+            assert lse[r] == -np.inf
+        else:
+            np.testing.assert_allclose(o[r], ro, rtol=1e-13, atol=1e-14)
+            assert abs(lse[r] - rl) <= 1e-13 * max(1.0, abs(rl))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("use_mask", [False, True])
+@pytest.mark.parametrize("use_seqlens", [False, True])
+def test_dense_matches_textbook_formula(causal, use_mask, use_seqlens):
+    g = np.random.default_rng(11 + 2 * causal + 4 * use_mask + 8 * use_seqlens)
+    B, Hq, Hkv, Sq, Skv, D, Dv = 2, 4, 2, 5, 7, 3, 4
+    q = g.standard_normal((B, Hq, Sq, D))
+    k = g.standard_normal((B, Hkv, Skv, D))
+    v = g.standard_normal((B, Hkv, Skv, Dv))
+    mask = (g.random((B, Hq, Sq, Skv)) < 0.3).astype(np.uint8) if use_mask else None
+    sq = np.array([5, 3], np.int32) if use_seqlens else None
+    sk = np.array([6, 7], np.int32) if use_seqlens else None
+    scale = 0.7
+    o, lse = oracle.attn_dense(q, k, v, scale=scale, causal=causal, mask=mask, seqlens_q=sq,
+                               seqlens_k=sk)
+    o = o.reshape(-1, Dv)
+    lse = lse.reshape(-1)
+    refs = []
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(Sq):
+                Lq = sq[b] if use_seqlens else Sq
+                Lk = sk[b] if use_seqlens else Skv
+                keys = []
+                if i < Lq:
+                    for j in range(Lk):
+                        if causal and j > i + Lk - Lq:
+                            continue
+                        if use_mask and mask[b, h, i, j]:
+                            continue
+                        keys.append(j)
+                refs.append(_naive_row(q[b, h, i], keys, lambda j: k[b, h // G, j],
+                                       lambda j: v[b, h // G, j], scale))
+    _compare(o, lse, refs, Dv)
+
+
+def test_blocksparse_matches_textbook_formula():
+    g = np.random.default_rng(5)
+    B, Hq, Hkv, S, D, Dv, bq, bk = 2, 2, 1, 11, 3, 2, 4, 3
+    q = g.standard_normal((B, Hq, S, D))
+    k = g.standard_normal((B, Hkv, S, D))
+    v = g.standard_normal((B, Hkv, S, Dv))
+    nqb, nkb = 3, 4
+    lists = np.array([[2, -1, 0], [-1, -1, -1], [3, 1, -1]], np.int32)  # -1 anywhere
+    seq = np.array([11, 7], np.int32)
+    o, lse = oracle.attn_blocksparse(q, k, v, lists, scale=0.9, block_q=bq, block_k=bk, seqlens=seq)
+    o = o.reshape(-1, Dv)
+    lse = lse.reshape(-1)
+    refs = []
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(S):
+                keys = []
+                if i < seq[b]:
+                    for x in sorted(int(x) for x in lists[i // bq] if x >= 0):
+                        keys += [j for j in range(x * bk, min(x * bk + bk, seq[b]))]
+                refs.append(_naive_row(q[b, h, i], keys, lambda j: k[b, 0, j], lambda j: v[b, 0, j], 0.9))
+    assert nkb * bk >= S
+    _compare(o, lse, refs, Dv)
+
+
+def test_topk_matches_textbook_formula():
+    g = np.random.default_rng(7)
+    T, S, W, Hq, Dqk, Dv = 5, 7, 4, 3, 5, 3
+    q = g.standard_normal((T, Hq, Dqk))
+    k = g.standard_normal((S, Dqk))
+    v = g.standard_normal((S, Dv))
+    idx = np.array([[3, -1, 0, 6], [-1, -1, -1, -1], [1, 2, 5, 4], [6, -1, -1, -1], [0, 5, -1, 2]],
+                   np.int32)
+    o, lse = oracle.attn_topk(q, k, v, idx, scale=0.4)
+    o = o.reshape(-1, Dv)
+    lse = lse.reshape(-1)
+    refs = []
+    for t in range(T):
+        keys = sorted(int(j) for j in idx[t] if j >= 0)
+        for h in range(Hq):
+            refs.append(_naive_row(q[t, h], keys, lambda j: k[j], lambda j: v[j], 0.4))
+    _compare(o, lse, refs, Dv)
+
+
+# ---------------------------------------------------------------------------
+# Softmax properties (verification page, softmax-property checks: rows sum
+# to one, no negative weight, the largest score gets the largest weight),
+# read off by passing V = identity so that O is the weight matrix P itself.
+# ---------------------------------------------------------------------------
+
+def test_softmax_properties_via_identity_values():
+    g = np.random.default_rng(3)
+    S, D = 16, 8
+    q = g.standard_normal((1, 2, S, D)) * 3
+    k = g.standard_normal((1, 2, S, D))
+    v = np.broadcast_to(np.eye(S), (1, 2, S, S)).copy()
+    for causal in (False, True):
+        P, _ = oracle.attn_dense(q, k, v, scale=0.5, causal=causal)
+        P = P.reshape(-1, S)
+        assert np.abs(P.sum(-1) - 1.0).max() < 1e-12
+        assert P.min() >= 0.0
+        s = np.einsum("bhid,bhjd->bhij", q, k).reshape(-1, S) * 0.5
+        if causal:
+            tri = np.tile(np.triu(np.ones((S, S), bool), 1), (2, 1))
+            s[tri] = -np.inf
+        assert np.array_equal(P.argmax(-1), s.argmax(-1))
+        assert np.all(P.max(-1) > P.mean(-1))
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and special cases (verification page, boundary-condition
+# tests: single token, extreme values, empty sequences).
+# ---------------------------------------------------------------------------
+
+def test_single_key_returns_that_value_exactly():
+    g = np.random.default_rng(4)
+    q = g.standard_normal((1, 1, 1, 128)).astype(np.float32)
+    k = g.standard_normal((1, 1, 1, 128)).astype(np.float32)
+    v = g.standard_normal((1, 1, 1, 128)).astype(np.float32)
+    o, lse = oracle.attn_dense(q, k, v, scale=1 / math.sqrt(128))
+    assert np.array_equal(o[0, 0, 0], v[0, 0, 0].astype(np.float64))
+    s = (1 / math.sqrt(128)) * float(np.dot(q[0, 0, 0].astype(np.float64), k[0, 0, 0].astype(np.float64)))
+    assert abs(lse[0, 0, 0] - s) <= 1e-15 * abs(s) + 1e-300
+
+
+def test_causal_first_row_sees_only_first_key():
+    g = np.random.default_rng(8)
+    q, k, v = (g.standard_normal((2, 3, 9, 4)) for _ in range(3))
+    o, _ = oracle.attn_dense(q, k, v, scale=1.0, causal=True)
+    assert np.array_equal(o[:, :, 0], v[:, :, 0])
+
+
+def test_two_keys_closed_form():
+    # scores 0 and ln 3 -> weights 1/4 and 3/4, LSE = ln 4.
+    q = np.array([[[[1.0]]]])
+    k = np.array([[[[0.0], [math.log(3.0)]]]])
+    v = np.array([[[[1.0, 0.0], [0.0, 1.0]]]])
+    o, lse = oracle.attn_dense(q, k, v, scale=1.0)
+    np.testing.assert_allclose(o[0, 0, 0], [0.25, 0.75], rtol=0, atol=2e-16)
+    assert abs(lse[0, 0, 0] - math.log(4.0)) < 4e-16
+
+
+def test_equal_scores_average_the_values():
+    g = np.random.default_rng(9)
+    S = 12
+    q = np.zeros((1, 1, S, 5))
+    k = g.standard_normal((1, 1, S, 5))
+    v = g.standard_normal((1, 1, S, 3))
+    o, lse = oracle.attn_dense(q, k, v, scale=0.3, causal=True)
+    for i in range(S):
+        np.testing.assert_allclose(o[0, 0, i], v[0, 0, :i + 1].mean(0), rtol=1e-14, atol=1e-15)
+        assert abs(lse[0, 0, i] - math.log(i + 1)) < 1e-14
+
+
+def test_repeated_keys_identity():
+    # Duplicating every key row doubles each weight's mass: O is the same as
+    # attention over the unique keys with the duplicate values averaged, and
+    # LSE grows by ln 2 (verification page, regression data: repeated keys).
+    g = np.random.default_rng(10)
+    q = g.standard_normal((1, 2, 6, 4))
+    k1 = g.standard_normal((1, 2, 5, 4))
+    va, vb = g.standard_normal((1, 2, 5, 3)), g.standard_normal((1, 2, 5, 3))
+    o2, l2 = oracle.attn_dense(q, np.concatenate([k1, k1], 2), np.concatenate([va, vb], 2), scale=0.8)
+    o1, l1 = oracle.attn_dense(q, k1, (va + vb) / 2, scale=0.8)
+    np.testing.assert_allclose(o2, o1, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(l2, l1 + math.log(2.0), rtol=0, atol=1e-13)
+
+
+def test_extreme_logits_do_not_overflow():
+    q = np.array([[[[1.0]]]])
+    k = np.array([[[[1e4], [-1e4]]]])
+    v = np.array([[[[3.0, -2.0], [7.0, 5.0]]]])
+    o, lse = oracle.attn_dense(q, k, v, scale=1.0)
+    assert np.array_equal(o[0, 0, 0], v[0, 0, 0])
+    assert lse[0, 0, 0] == 1e4
+    # The verification page's extreme-value inputs: zeros, 1e3, 1e-10, N * 1e2.
+    g = np.random.default_rng(12)
+    cases = [(np.zeros((1, 1, 4, 128)),) * 3,
+             (np.full((1, 1, 4, 128), 1e3), np.full((1, 1, 4, 128), 1e3), np.ones((1, 1, 4, 128))),
+             (np.full((1, 1, 4, 128), 1e-10), np.full((1, 1, 4, 128), 1e-10), np.ones((1, 1, 4, 128))),
+             (g.standard_normal((1, 1, 4, 128)) * 1e2, g.standard_normal((1, 1, 4, 128)) * 1e2,
+              g.standard_normal((1, 1, 4, 128)))]
+    for q, k, v in cases:
+        o, lse = oracle.attn_dense(q, k, v, scale=1 / math.sqrt(128))
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    # all-equal huge logits: a plain average of the values
+    o, _ = oracle.attn_dense(*cases[1][:2], cases[1][2] * np.arange(4).reshape(1, 1, 4, 1),
+                             scale=1 / math.sqrt(128))
+    np.testing.assert_allclose(o[0, 0, :, 0], np.full(4, 1.5), rtol=1e-15)
+
+
+def test_empty_key_sets_give_zero_and_neg_inf():
+    g = np.random.default_rng(13)
+    q, k, v = (g.standard_normal((1, 2, 4, 3)) for _ in range(3))
+    mask = np.zeros((4, 4), np.uint8)
+    mask[2] = 1
+    o, lse = oracle.attn_dense(q, k, v, scale=1.0, mask=mask)
+    assert np.all(o[:, :, 2] == 0) and np.all(lse[:, :, 2] == -np.inf)
+    assert np.all(np.isfinite(lse[:, :, [0, 1, 3]]))
+    # Skv = 0: every row empty
+    o, lse = oracle.attn_dense(q, k[:, :, :0], v[:, :, :0], scale=1.0)
+    assert o.shape == (1, 2, 4, 3) and np.all(o == 0) and np.all(lse == -np.inf)
+    # Sq = 0: nothing to compute
+    o, lse = oracle.attn_dense(q[:, :, :0], k, v, scale=1.0)
+    assert o.shape == (1, 2, 0, 3) and lse.shape == (1, 2, 0)
+    # padded rows of a short batch entry
+    o, lse = oracle.attn_dense(q, k, v, scale=1.0, seqlens_q=np.array([2], np.int32),
+                               seqlens_k=np.array([2], np.int32))
+    assert np.all(o[:, :, 2:] == 0) and np.all(lse[:, :, 2:] == -np.inf)
+    # block lists with no valid slot, top-k rows with no valid index
+    o, lse = oracle.attn_blocksparse(q, k, v, np.full((1, 2), -1, np.int32), scale=1.0, block_q=4,
+                                     block_k=4)
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+    o, lse = oracle.attn_topk(q[0], k[0, 0], v[0, 0], np.full((2, 3), -1, np.int32), scale=1.0)
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+def test_precondition_violations_are_rejected():
+    g = np.random.default_rng(14)
+    q, k, v = g.standard_normal((2, 1, 3)), g.standard_normal((4, 3)), g.standard_normal((4, 2))
+    with pytest.raises(oracle.OracleError, match="duplicate"):
+        oracle.attn_topk(q, k, v, np.array([[1, 1], [0, -1]], np.int32), scale=1.0)
+    with pytest.raises(oracle.OracleError, match="range"):
+        oracle.attn_topk(q, k, v, np.array([[4, 0], [0, -1]], np.int32), scale=1.0)
+    q4, k4, v4 = (g.standard_normal((1, 1, 8, 2)) for _ in range(3))
+    with pytest.raises(oracle.OracleError, match="duplicate"):
+        oracle.attn_blocksparse(q4, k4, v4, np.array([[0, 0]], np.int32), scale=1.0, block_q=8,
+                                block_k=4)
+    with pytest.raises(oracle.OracleError, match="range"):
+        oracle.attn_blocksparse(q4, k4, v4, np.array([[2, -1]], np.int32), scale=1.0, block_q=8,
+                                block_k=4)
+
+
+# ---------------------------------------------------------------------------
+# The online-softmax recurrence (verification page, loop-invariant proof
+# outline: running max, rescaled running sum and accumulator, final division)
+# written independently here over random key-block splits, and the merge of
+# two partial states over disjoint key sets, must both reproduce the oracle.
+# ---------------------------------------------------------------------------
+
+def _online(qv, K, V, scale, cuts):
+    m, l, acc = -np.inf, 0.0, np.zeros(V.shape[1])
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        s = scale * (K[a:b] @ qv)
+        m_new = max(m, s.max())
+        alpha = math.exp(m - m_new) if m != -np.inf else 0.0
+        p = np.exp(s - m_new)
+        l = alpha * l + p.sum()
+        acc = alpha * acc + p @ V[a:b]
+        m = m_new
+    return acc / l, m + math.log(l), (m, l, acc)
+
+
+def test_online_recurrence_and_merge_match_oracle():
+    g = np.random.default_rng(15)
+    S, D, Dv = 300, 16, 8
+    q = g.standard_normal((1, 1, 7, D)) * 2
+    k = g.standard_normal((1, 1, S, D))
+    v = g.standard_normal((1, 1, S, Dv))
+    o_ref, lse_ref = oracle.attn_dense(q, k, v, scale=0.25)
+    for r in range(7):
+        cuts = np.unique(np.concatenate([[0, S], g.integers(1, S, size=g.integers(1, 20))]))
+        o, lse, _ = _online(q[0, 0, r], k[0, 0], v[0, 0], 0.25, cuts)
+        np.testing.assert_allclose(o, o_ref[0, 0, r], rtol=1e-13, atol=1e-13)
+        assert abs(lse - lse_ref[0, 0, r]) < 1e-13
+        c = int(g.integers(1, S))
+        _, _, (m1, l1, a1) = _online(q[0, 0, r], k[0, 0, :c], v[0, 0, :c], 0.25, [0, c])
+        _, _, (m2, l2, a2) = _online(q[0, 0, r], k[0, 0, c:], v[0, 0, c:], 0.25, [0, S - c])
+        m = max(m1, m2)
+        lm = l1 * math.exp(m1 - m) + l2 * math.exp(m2 - m)
+        om = (a1 * math.exp(m1 - m) + a2 * math.exp(m2 - m)) / lm
+        np.testing.assert_allclose(om, o_ref[0, 0, r], rtol=1e-13, atol=1e-13)
+        assert abs(m + math.log(lm) - lse_ref[0, 0, r]) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# Reductions between the entry points.
+# ---------------------------------------------------------------------------
+
+def test_topk_with_prefix_lists_equals_causal_dense():
+    g = np.random.default_rng(16)
+    T, H, D, Dv = 9, 3, 6, 4
+    q = g.standard_normal((T, H, D))
+    k = g.standard_normal((T, D))
+    v = g.standard_normal((T, Dv))
+    idx = np.full((T, T), -1, np.int32)
+    for t in range(T):
+        idx[t, :t + 1] = g.permutation(t + 1)
+    o1, l1 = oracle.attn_topk(q, k, v, idx, scale=0.6)
+    o2, l2 = oracle.attn_dense(q.transpose(1, 0, 2)[None], np.broadcast_to(k, (1, 1, T, D)),
+                               np.broadcast_to(v, (1, 1, T, Dv)), scale=0.6, causal=True)
+    assert np.array_equal(o1, o2[0].transpose(1, 0, 2))
+    assert np.array_equal(l1, l2[0].T)
+
+
+def test_blocksparse_all_blocks_equals_dense():
+    g = np.random.default_rng(17)
+    B, Hq, Hkv, S, D = 2, 4, 2, 40, 8
+    q = g.standard_normal((B, Hq, S, D))
+    k = g.standard_normal((B, Hkv, S, D))
+    v = g.standard_normal((B, Hkv, S, D))
+    lists = np.array([g.permutation(5) for _ in range(5)], np.int32)  # 5 blocks of 8
+    o1, l1 = oracle.attn_blocksparse(q, k, v, lists, scale=0.3, block_q=8, block_k=8)
+    o2, l2 = oracle.attn_dense(q, k, v, scale=0.3)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    seq = np.array([40, 21], np.int32)
+    o1, l1 = oracle.attn_blocksparse(q, k, v, lists, scale=0.3, block_q=8, block_k=8, seqlens=seq)
+    o2, l2 = oracle.attn_dense(q, k, v, scale=0.3, seqlens_q=seq, seqlens_k=seq)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_gqa_equals_mha_on_repeated_heads():
+    g = np.random.default_rng(18)
+    B, Hq, Hkv, S, D = 2, 6, 2, 10, 4
+    q = g.standard_normal((B, Hq, S, D))
+    k = g.standard_normal((B, Hkv, S, D))
+    v = g.standard_normal((B, Hkv, S, D))
+    o1, l1 = oracle.attn_dense(q, k, v, scale=0.5, causal=True)
+    G = Hq // Hkv
+    o2, l2 = oracle.attn_dense(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), scale=0.5,
+                               causal=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_zero_mask_equals_no_mask():
+    g = np.random.default_rng(19)
+    q, k, v = (g.standard_normal((1, 2, 8, 4)) for _ in range(3))
+    a = oracle.attn_dense(q, k, v, scale=0.5, causal=True)
+    b = oracle.attn_dense(q, k, v, scale=0.5, causal=True, mask=np.zeros((8, 8), np.uint8))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_topk_permutation_invariance_is_bitwise():
+    g = np.random.default_rng(20)
+    T, S, W, H, D, Dv = 6, 50, 12, 2, 8, 8
+    q = g.standard_normal((T, H, D)) * 3
+    k = g.standard_normal((S, D))
+    v = g.standard_normal((S, Dv))
+    idx = np.full((T, W), -1, np.int32)
+    for t in range(T):
+        n = int(g.integers(1, W + 1))
+        idx[t, :n] = g.choice(S, n, replace=False)
+    o1, l1 = oracle.attn_topk(q, k, v, idx, scale=0.35)
+    perm = np.array([g.permutation(row) for row in idx])
+    o2, l2 = oracle.attn_topk(q, k, v, perm, scale=0.35)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_row_subset_equals_full_run():
+    g = np.random.default_rng(21)
+    q, k, v = (g.standard_normal((2, 2, 7, 5)) for _ in range(3))
+    o, l = oracle.attn_dense(q, k, v, scale=0.5, causal=True)
+    rows = np.array([27, 0, 13, 5])
+    o2, l2 = oracle.attn_dense(q, k, v, scale=0.5, causal=True, rows=rows)
+    assert np.array_equal(o2, o.reshape(-1, 5)[rows]) and np.array_equal(l2, l.reshape(-1)[rows])
+
+
+def test_threads_do_not_change_results():
+    g = np.random.default_rng(22)
+    q, k, v = (g.standard_normal((1, 3, 33, 8)) for _ in range(3))
+    a = oracle.attn_dense(q, k, v, scale=0.5, causal=True, nthreads=1)
+    b = oracle.attn_dense(q, k, v, scale=0.5, causal=True, nthreads=7)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_low_precision_inputs_are_upconverted_exactly():
+    g = np.random.default_rng(23)
+    q = torch.from_numpy(g.standard_normal((1, 1, 5, 8), dtype=np.float32)).to(torch.bfloat16)
+    k = torch.from_numpy(g.standard_normal((1, 1, 5, 8), dtype=np.float32)).to(torch.float16)
+    v = torch.from_numpy(g.standard_normal((1, 1, 5, 8), dtype=np.float32)).to(torch.bfloat16)
+    a = oracle.attn_dense(q, k, v, scale=0.5)
+    b = oracle.attn_dense(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale=0.5)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------
+# Comparator pins and page-printed values.
+# ---------------------------------------------------------------------------
+
+def test_bf16_rounding_floor_closed_form():
+    # rel-L2 of RNE-rounding a Gaussian to bf16 (8 significant bits):
+    # 2^-7 * sqrt(3 / (8 ln 2)) / sqrt(12)
+    x = np.random.default_rng(24).standard_normal(2_000_000)
+    r = metrics.rel_l2(metrics.round_to(x, torch.bfloat16), x)
+    closed = 2.0 ** -7 * math.sqrt(3.0 / (8.0 * math.log(2.0))) / math.sqrt(12.0)
+    assert abs(r - closed) / closed < 0.01
+    # the noise floor of the row gain over Dv elements: elem_rms * sqrt(3/Dv)
+    Dv = 512
+    rows = np.random.default_rng(25).standard_normal((4000, Dv))
+    F = metrics.bf16_floor(rows)
+    assert abs(F - r * math.sqrt(3.0 / Dv)) / F < 0.05
+
+
+def test_metrics_detect_planted_errors():
+    ref = np.random.default_rng(26).standard_normal((100, 64))
+    assert metrics.rel_l2(ref, ref) == 0.0
+    gained = ref * (1 + 1e-3)
+    assert abs(metrics.rms(metrics.row_gain(gained, ref)) - 1e-3) < 1e-12
+    rep = metrics.allclose_report(ref + 2e-4, ref, atol=1e-4, rtol=0.0)
+    assert rep["fail_frac"] == 1.0
+    l = np.array([0.0, -np.inf, 1.0])
+    assert metrics.lse_report(np.array([0.0, 0.0, 1.0]), l)["neginf_mismatch"] == 1
+
+
+def _p2_inputs(n_tokens, peak_dims, seed=77):
+    """Top-k MLA inputs at the page's shape for a sample of tokens: K for all
+    S keys, Q only for the sampled tokens, key sets = self + min(W-1, t)
+    distinct earlier keys."""
+    T = S = 4096
+    W, H, Dqk, Dv = 2048, 128, 576, 512
+    g = np.random.default_rng(seed)
+    k32 = g.standard_normal((S, Dqk), dtype=np.float32)
+    toks = np.sort(g.choice(T, size=n_tokens, replace=False))
+    q32 = g.standard_normal((n_tokens, H, Dqk), dtype=np.float32)
+    q32[:, :, :peak_dims] += np.float32(0.25) * k32[toks][:, None, :peak_dims]
+    idx = np.full((n_tokens, W), -1, np.int32)
+    for n, t in enumerate(toks):
+        m = min(W - 1, int(t))
+        idx[n, 0] = t
+        idx[n, 1:1 + m] = np.sort(g.choice(int(t), size=m, replace=False)) if m else []
+    q = torch.from_numpy(q32).to(torch.bfloat16)
+    k = torch.from_numpy(k32).to(torch.bfloat16)
+    return q, k, idx, toks, 1.0 / math.sqrt(Dqk), Dv
+
+
+def test_page_self_weight_and_floor_are_reproduced():
+    """Peaked inputs at the sparse-MLA page's shape reproduce its printed
+    self-weight median / p90 and its 1.66e-3 bf16 output floor."""
+    sw = json.load(open(os.path.join(GOLDEN, "p2_self_weight.json")))
+    fl = json.load(open(os.path.join(GOLDEN, "p2_bf16_floor.json")))
+    q, k, idx, toks, scale, Dv = _p2_inputs(64, peak_dims=576)
+    o, lse = oracle.attn_topk(q, k, k[:, :Dv], idx, scale=scale)
+    qd = q.double().numpy()
+    kd = k.double().numpy()
+    s_self = scale * np.einsum("thd,td->th", qd, kd[toks])
+    w = np.exp(s_self - lse)
+    # The page's inputs come from its own indexer; with uniformly drawn key
+    # sets the median lands within 0.04 of the printed 0.17 (the printed p90
+    # of 0.41 is not reproduced by uniform key sets, which give about 0.5,
+    # so it is not asserted).
+    assert abs(np.median(w) - sw["median"]) < 0.04
+    assert np.all((w > 0) & (w < 1))
+    floor = metrics.rel_l2(metrics.round_to(o, torch.bfloat16), o)
+    assert abs(floor - fl["value"]) < 0.03 * fl["value"]
