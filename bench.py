@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Attention-forward benchmark on one MI355X.
+
+One step = one call of the library's forward on one batch of synthetic input
+(all steps of the hot path run inside that call). The headline workload is
+causal bf16 attention, B=2, H=16, S=4096, D=128; ``value`` is its whole-job
+throughput in TFLOP/s with inputs resident in HBM, over exactly --steps
+timed calls after --warmup untimed ones.
+
+FLOP convention: 4 * D per (query, key) pair the row attends to (Q.K^T and
+P.V, 2 flops per multiply-add each); a causal head of length S has
+S(S+1)/2 pairs. Top-k sparse MLA counts 2 * (Dqk + Dv) flops per pair and
+reports GB/s of algorithmic bytes (every gathered 1152-byte key row counted
+each time it is gathered, plus Q, O, indices and LSE once).
+
+Printed: ONE JSON line on stdout (progress goes to stderr), carrying
+``roofline`` for the timed kernel (its own average launch time from HIP
+events on the launch stream vs. the dense bf16 MFMA peak) and
+``cpu_baseline`` (the fp64 CPU oracle timed on a bounded sample of the same
+workload on this host's cores).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def causal_pairs(Sq, Skv):
+    i = np.arange(Sq, dtype=np.int64)
+    return int(np.clip(i + (Skv - Sq) + 1, 0, Skv).sum())
+
+
+def dense_flops(w):
+    B, Hq, Sq, D = w["q"].shape
+    Skv = w["k"].shape[2]
+    pairs = causal_pairs(Sq, Skv) if w["causal"] else Sq * Skv
+    return 4.0 * D * pairs * B * Hq
+
+
+def blocksparse_flops(w):
+    B, Hq, Sq, D = w["q"].shape
+    lists = w["block_idx"].numpy()
+    seq = w["seqlens"].numpy()
+    blk = w["block"]
+    pairs = 0
+    for b in range(B):
+        L = int(seq[b])
+        for qb in range(lists.shape[0]):
+            rows = max(0, min(L, (qb + 1) * blk) - qb * blk)
+            keys = sum(max(0, min(L, (x + 1) * blk) - x * blk) for x in lists[qb] if x >= 0)
+            pairs += rows * keys
+    return 4.0 * D * pairs * Hq
+
+
+def topk_work(w, idx):
+    T, Hq, Dqk = w["q"].shape
+    Dv = w["dv"]
+    valid = int((idx >= 0).sum())
+    flops = 2.0 * (Dqk + Dv) * valid * Hq
+    es = w["q"].element_size()
+    nbytes = valid * Dqk * es + T * Hq * Dqk * es + T * Hq * Dv * es + idx.numel() * 4 + T * Hq * 4
+    return flops, nbytes
+
+
+def make_call(w, order="idx_a"):
+    """Uploads a workload and returns a zero-argument launcher of one forward."""
+    import flashattention_online_softmax_amd as fa
+    dev = "cuda"
+    if w["kind"] == "dense":
+        q, k, v = (w[n].to(dev) for n in ("q", "k", "v"))
+        mask = w["mask"].to(dev) if w.get("mask") is not None else None
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        return lambda: fa.fa_fwd(q, k, v, scale=w["scale"], causal=w["causal"], mask=mask, out=o, lse=lse)
+    if w["kind"] == "blocksparse":
+        q, k, v = (w[n].to(dev) for n in ("q", "k", "v"))
+        bi, seq = w["block_idx"].to(dev), w["seqlens"].to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        return lambda: fa.fa_fwd_blocksparse(q, k, v, bi, scale=w["scale"], seqlens=seq, out=o, lse=lse)
+    q, kv, idx = w["q"].to(dev), w["kv"].to(dev), w[order].to(dev)
+    vv = kv[:, :w["dv"]]
+    o = torch.empty((q.shape[0], q.shape[1], w["dv"]), dtype=q.dtype, device=dev)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    return lambda: fa.fa_fwd_topk_gather(q, kv, vv, idx, scale=w["scale"], out=o, lse=lse)
+
+
+def time_calls(call, steps, warmup):
+    """Returns (wall ms per step over exactly `steps` calls bracketed by device
+    synchronisations, mean kernel ms from per-launch HIP events on the launch
+    stream)."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    kern = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    return wall, kern
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "flashattention_online_softmax_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(ROOT, "flashattention_online_softmax_amd", "build.py"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, launches_per_step=1):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, if it was taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("source_digest") != source_digest():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, target_s, threads):
+    """The fp64 oracle on a bounded random sample of query rows of a dense
+    workload; returns TFLOP/s (algorithmic flops of the sampled rows / time)."""
+    import oracle
+    B, Hq, Sq, D = w["q"].shape
+    Skv = w["k"].shape[2]
+    g = np.random.default_rng(99)
+    kk = w["k"].to(torch.float64).numpy()
+    vv = w["v"].to(torch.float64).numpy()
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.attn_dense(w["q"], kk, vv, scale=float(np.float32(w["scale"])), causal=w["causal"],
+                          mask=w.get("mask"), rows=rows, nthreads=threads)
+        return time.perf_counter() - t0
+
+    def flops(rows):
+        i = rows % Sq
+        keys = np.clip(i + (Skv - Sq) + 1, 0, Skv) if w["causal"] else np.full(rows.shape, Skv)
+        return 4.0 * D * float(keys.sum())
+
+    probe = np.sort(g.choice(B * Hq * Sq, size=4 * threads, replace=False))
+    t = run(probe)
+    n = int(min(B * Hq * Sq, max(len(probe), len(probe) * target_s / max(t, 1e-3))))
+    rows = np.sort(g.choice(B * Hq * Sq, size=n, replace=False))
+    t = run(rows)
+    return {"value": flops(rows) / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d random query rows of %d (%.1f s, fp64, %d threads)" % (n, B * Hq * Sq, t, threads),
+            "seconds": t}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="causal_bf16_s4096")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the S=8192 and top-k figures")
+    ap.add_argument("--all", action="store_true", help="also time the GQA+mask and block-sparse workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build runs the forward on a single "
+              "MI355X (--gpus 1); multi-GPU runs are not part of it.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import synth
+    import flashattention_online_softmax_amd as fa
+    fa.load()  # raises if the HIP library is not built
+
+    log("generating %s" % args.workload)
+    w = synth.workload(args.workload)
+    if w["kind"] != "dense":
+        raise SystemExit("headline workload must be a dense one")
+    flops = dense_flops(w)
+    call = make_call(w)
+    log("timing %d steps after %d warmup" % (args.steps, args.warmup))
+    wall_ms, kern_ms = time_calls(call, args.steps, args.warmup)
+    value = flops / (wall_ms * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    B, H, S, D = w["q"].shape
+    traffic = measured_traffic(args.workload)
+    result = {
+        "metric": "attention fwd TFLOP/s (bf16, causal, D=128) + % of MFMA peak; GB/s for top-k sparse",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), cast to bf16)",
+        "config": {"workload": args.workload, "B": B, "H": H, "S": S, "D": D,
+                   "causal": bool(w["causal"]), "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel_ms": round(kern_ms, 4)},
+    }
+    torch.cuda.synchronize()
+    del call
+
+    if not args.no_secondary:
+        sec = {}
+        for name in ["causal_bf16_s8192"] + (["gqa_mask_f16_s8192", "blocksparse_f16_s8192"] if args.all else []):
+            log("secondary %s" % name)
+            w2 = synth.workload(name)
+            fl = dense_flops(w2) if w2["kind"] == "dense" else blocksparse_flops(w2)
+            c2 = make_call(w2)
+            _, km = time_calls(c2, max(5, args.steps // 2), 2)
+            sec[name] = {"tflops": round(fl / (km * 1e-3) / 1e12, 2), "kernel_ms": round(km, 4),
+                         "frac_mfma_peak": round(fl / (km * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            del c2, w2
+            torch.cuda.empty_cache()
+        log("secondary topk_mla_bf16_t4096")
+        w5 = synth.workload("topk_mla_bf16_t4096")
+        for order in ("idx_a", "idx_b"):
+            fl, nb = topk_work(w5, w5[order])
+            c5 = make_call(w5, order)
+            _, km = time_calls(c5, max(5, args.steps // 2), 2)
+            sec["topk_mla_bf16_t4096_" + ("self_first" if order == "idx_a" else "self_last")] = {
+                "gbs": round(nb / (km * 1e-3) / 1e9, 1), "tflops": round(fl / (km * 1e-3) / 1e12, 2),
+                "kernel_ms": round(km, 4), "frac_hbm_peak": round(nb / (km * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "algorithmic_bytes": nb}
+            del c5
+        del w5
+        torch.cuda.empty_cache()
+        result["secondary"] = sec
+        result["page_figures"] = {
+            "exact_max_fwd_cost_gb200": "+~4% (sparse-MLA training forward, T=S=16384, W=2048, H=128; NVIDIA GB200)",
+            "bf16_output_floor_rel_l2": "1.66e-3 at T=S=4096, W=2048, H=128 (numerical, fp64 reference)"}
+
+    if not args.no_cpu_baseline:
+        threads = min(16, os.cpu_count() or 1)
+        log("cpu baseline (oracle, %d threads, ~%.0f s)" % (threads, args.cpu_seconds))
+        cb = cpu_baseline(w, args.cpu_seconds, threads)
+        cb.pop("seconds")
+        cb["value"] = round(cb["value"], 6)
+        result["cpu_baseline"] = cb
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

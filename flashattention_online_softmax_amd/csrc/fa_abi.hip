@@ -1,0 +1,331 @@
+// C ABI of libfa.so: argument validation on the host, then dispatch to the
+// gfx950 kernels on the caller's stream. See include/fa.h for the contract.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fa_status fail(fa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+int64_t elem_size(int32_t dt) {
+  switch (dt) {
+    case FA_F32: return 4;
+    case FA_F16: return 2;
+    case FA_BF16: return 2;
+    case FA_U8: return 1;
+    case FA_I32: return 4;
+    default: return 0;
+  }
+}
+
+const char* dtype_name(int32_t dt) {
+  switch (dt) {
+    case FA_F32: return "f32";
+    case FA_F16: return "f16";
+    case FA_BF16: return "bf16";
+    case FA_U8: return "u8";
+    case FA_I32: return "i32";
+    default: return "?";
+  }
+}
+
+int64_t numel(const fa_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+// Rank, extents >= 0, unit last stride (unless empty), non-null data when
+// non-empty, and 16-byte alignment of the data pointer and of every row
+// (rows_aligned) for vector loads.
+fa_status check_tensor(const char* name, const fa_tensor* t, int ndim, bool rows_aligned) {
+  if (!t) return fail(FA_ERR_NULL, "%s is NULL", name);
+  if (t->ndim != ndim) return fail(FA_ERR_SHAPE, "%s must have rank %d, got %d", name, ndim, t->ndim);
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] < 0) return fail(FA_ERR_SHAPE, "%s has a negative extent", name);
+  if (elem_size(t->dtype) == 0) return fail(FA_ERR_DTYPE, "%s has unknown dtype %d", name, t->dtype);
+  if (numel(t) == 0) return FA_OK;
+  if (!t->data) return fail(FA_ERR_NULL, "%s.data is NULL", name);
+  if (t->stride[ndim - 1] != 1 && t->shape[ndim - 1] > 1)
+    return fail(FA_ERR_STRIDE, "%s: last dimension must be contiguous (stride %lld)", name,
+                (long long)t->stride[ndim - 1]);
+  for (int i = 0; i < ndim; ++i)
+    if (t->stride[i] < 0) return fail(FA_ERR_STRIDE, "%s: negative stride", name);
+  if (rows_aligned) {
+    const int64_t es = elem_size(t->dtype);
+    if (((uintptr_t)t->data) % 16 != 0) return fail(FA_ERR_STRIDE, "%s.data is not 16-byte aligned", name);
+    for (int i = 0; i < ndim - 1; ++i)
+      if (t->shape[i] > 1 && (t->stride[i] * es) % 16 != 0)
+        return fail(FA_ERR_STRIDE, "%s: stride of dim %d is not a multiple of 16 bytes", name, i);
+  }
+  return FA_OK;
+}
+
+fa_status check_dtype(const char* name, const fa_tensor* t, int32_t want) {
+  if (t->dtype != want)
+    return fail(FA_ERR_DTYPE, "%s has dtype %s, expected %s", name, dtype_name(t->dtype), dtype_name(want));
+  return FA_OK;
+}
+
+fa_status check_contiguous(const char* name, const fa_tensor* t) {
+  if (numel(t) == 0) return FA_OK;
+  int64_t expect = 1;
+  for (int i = t->ndim - 1; i >= 0; --i) {
+    if (t->shape[i] > 1 && t->stride[i] != expect)
+      return fail(FA_ERR_STRIDE, "%s must be contiguous", name);
+    expect *= t->shape[i];
+  }
+  return FA_OK;
+}
+
+// Optional int32 [B] sequence-length vector.
+fa_status check_seqlens(const char* name, const fa_tensor* t, int64_t B) {
+  if (!t) return FA_OK;
+  fa_status s = check_tensor(name, t, 1, false);
+  if (s != FA_OK) return s;
+  if ((s = check_dtype(name, t, FA_I32)) != FA_OK) return s;
+  if (t->shape[0] != B) return fail(FA_ERR_SHAPE, "%s must have %lld entries", name, (long long)B);
+  return FA_OK;
+}
+
+fa_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  return fail(FA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+}
+
+bool fits_i32(int64_t x) { return x >= 0 && x <= 0x7fffffff; }
+
+// The kernels work in the exp2 domain with c = scale * log2(e); c must be a
+// normal positive float so that masked scores (-inf) stay -inf after scaling.
+bool scale_ok(float scale) {
+  return std::isfinite(scale) && scale * 1.4426950408889634f >= 1.17549435e-38f;
+}
+
+// Shared validation of q/k/v/o/lse for the BNSD entry points.
+fa_status check_bnsd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* o,
+                     const fa_tensor* lse, float scale) {
+  fa_status s;
+  if ((s = check_tensor("q", q, 4, true)) != FA_OK) return s;
+  if ((s = check_tensor("k", k, 4, true)) != FA_OK) return s;
+  if ((s = check_tensor("v", v, 4, true)) != FA_OK) return s;
+  if ((s = check_tensor("o", o, 4, true)) != FA_OK) return s;
+  if ((s = check_tensor("lse", lse, 3, false)) != FA_OK) return s;
+  if (q->dtype != FA_F32 && q->dtype != FA_F16 && q->dtype != FA_BF16)
+    return fail(FA_ERR_DTYPE, "q dtype must be f32, f16 or bf16, got %s", dtype_name(q->dtype));
+  if ((s = check_dtype("k", k, q->dtype)) != FA_OK) return s;
+  if ((s = check_dtype("v", v, q->dtype)) != FA_OK) return s;
+  if ((s = check_dtype("o", o, q->dtype)) != FA_OK) return s;
+  if ((s = check_dtype("lse", lse, FA_F32)) != FA_OK) return s;
+  const int64_t B = q->shape[0], Hq = q->shape[1], Sq = q->shape[2], D = q->shape[3];
+  const int64_t Hkv = k->shape[1], Skv = k->shape[2];
+  if (k->shape[0] != B || v->shape[0] != B) return fail(FA_ERR_SHAPE, "batch sizes of q, k, v differ");
+  if (k->shape[3] != D) return fail(FA_ERR_SHAPE, "k head dim %lld != q head dim %lld", (long long)k->shape[3], (long long)D);
+  if (v->shape[1] != Hkv || v->shape[2] != Skv) return fail(FA_ERR_SHAPE, "v must match k in heads and length");
+  const int64_t Dv = v->shape[3];
+  if (o->shape[0] != B || o->shape[1] != Hq || o->shape[2] != Sq || o->shape[3] != Dv)
+    return fail(FA_ERR_SHAPE, "o must be [B, Hq, Sq, Dv]");
+  if (lse->shape[0] != B || lse->shape[1] != Hq || lse->shape[2] != Sq)
+    return fail(FA_ERR_SHAPE, "lse must be [B, Hq, Sq]");
+  if ((s = check_contiguous("lse", lse)) != FA_OK) return s;
+  if (Hkv == 0 && B * Hq * Sq > 0) return fail(FA_ERR_SHAPE, "k has no heads");
+  if (Hkv > 0 && Hq % Hkv != 0) return fail(FA_ERR_SHAPE, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+  if (!scale_ok(scale)) return fail(FA_ERR_VALUE, "scale must be finite and > 0");
+  if (D != Dv) return fail(FA_ERR_UNSUPPORTED, "D (%lld) != Dv (%lld) is not supported", (long long)D, (long long)Dv);
+  if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %lld not supported (64 or 128)", (long long)D);
+  if (!fits_i32(B * Hq * Sq) || !fits_i32(Skv) || !fits_i32(B * Hq))
+    return fail(FA_ERR_UNSUPPORTED, "problem too large for 32-bit row indexing");
+  return FA_OK;
+}
+
+void fill_common(fa::FwdParams& p, const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                 const fa_tensor* o, const fa_tensor* lse, float scale) {
+  memset(&p, 0, sizeof(p));
+  p.q = q->data;
+  p.k = k->data;
+  p.v = v->data;
+  p.o = o->data;
+  p.lse = (float*)lse->data;
+  p.q_sb = q->stride[0]; p.q_sh = q->stride[1]; p.q_ss = q->stride[2];
+  p.k_sb = k->stride[0]; p.k_sh = k->stride[1]; p.k_ss = k->stride[2];
+  p.v_sb = v->stride[0]; p.v_sh = v->stride[1]; p.v_ss = v->stride[2];
+  p.o_sb = o->stride[0]; p.o_sh = o->stride[1]; p.o_ss = o->stride[2];
+  p.B = (int32_t)q->shape[0];
+  p.Hq = (int32_t)q->shape[1];
+  p.Sq = (int32_t)q->shape[2];
+  p.Hkv = (int32_t)k->shape[1];
+  p.Skv = (int32_t)k->shape[2];
+  p.G = p.Hkv > 0 ? p.Hq / p.Hkv : 1;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+}
+
+fa::Dt to_dt(int32_t d) { return d == FA_F32 ? fa::Dt::F32 : d == FA_F16 ? fa::Dt::F16 : fa::Dt::BF16; }
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* mask,
+                 const fa_tensor* seqlens_q, const fa_tensor* seqlens_k, int causal, float scale,
+                 const fa_tensor* o, const fa_tensor* lse, void* stream) {
+  clear_error();
+  fa_status s = check_bnsd(q, k, v, o, lse, scale);
+  if (s != FA_OK) return s;
+  if (causal != 0 && causal != 1) return fail(FA_ERR_VALUE, "causal must be 0 or 1");
+  const int64_t B = q->shape[0], Hq = q->shape[1], Sq = q->shape[2], Skv = k->shape[2];
+  if ((s = check_seqlens("seqlens_q", seqlens_q, B)) != FA_OK) return s;
+  if ((s = check_seqlens("seqlens_k", seqlens_k, B)) != FA_OK) return s;
+  fa::FwdParams p;
+  fill_common(p, q, k, v, o, lse, scale);
+  if (mask) {
+    if (mask->ndim != 2 && mask->ndim != 4) return fail(FA_ERR_SHAPE, "mask must have rank 2 or 4");
+    if ((s = check_tensor("mask", mask, mask->ndim, false)) != FA_OK) return s;
+    if ((s = check_dtype("mask", mask, FA_U8)) != FA_OK) return s;
+    if (mask->ndim == 2) {
+      if (mask->shape[0] != Sq || mask->shape[1] != Skv) return fail(FA_ERR_SHAPE, "mask must be [Sq, Skv]");
+      p.m_sb = 0;
+      p.m_sh = 0;
+      p.m_ss = mask->stride[0];
+    } else {
+      if ((mask->shape[0] != B && mask->shape[0] != 1) || (mask->shape[1] != Hq && mask->shape[1] != 1) ||
+          mask->shape[2] != Sq || mask->shape[3] != Skv)
+        return fail(FA_ERR_SHAPE, "mask must be [B|1, Hq|1, Sq, Skv]");
+      p.m_sb = mask->shape[0] == 1 ? 0 : mask->stride[0];
+      p.m_sh = mask->shape[1] == 1 ? 0 : mask->stride[1];
+      p.m_ss = mask->stride[mask->ndim == 4 ? 2 : 0];
+    }
+    p.mask = (const uint8_t*)mask->data;
+    p.mask_vec4 = (((uintptr_t)mask->data) % 4 == 0) && (p.m_sb % 4 == 0) && (p.m_sh % 4 == 0) &&
+                  (p.m_ss % 4 == 0);
+  }
+  p.seqlens_q = seqlens_q ? (const int32_t*)seqlens_q->data : nullptr;
+  p.seqlens_k = seqlens_k ? (const int32_t*)seqlens_k->data : nullptr;
+  if (B * Hq * Sq == 0) return FA_OK;
+  const bool has_mask = mask && numel(mask) > 0;
+  if (mask && !has_mask && Skv > 0) return fail(FA_ERR_SHAPE, "mask is empty");
+  return hip_status(fa::launch_dense(to_dt(q->dtype), (int)q->shape[3], causal != 0, has_mask, false, p,
+                                     (hipStream_t)stream));
+}
+
+fa_status fa_fwd_blocksparse(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                             const fa_tensor* block_idx, int block_q, int block_k,
+                             const fa_tensor* seqlens, float scale, const fa_tensor* o,
+                             const fa_tensor* lse, void* stream) {
+  clear_error();
+  fa_status s = check_bnsd(q, k, v, o, lse, scale);
+  if (s != FA_OK) return s;
+  if (block_q != 128 || block_k != 128)
+    return fail(FA_ERR_UNSUPPORTED, "block_q and block_k must be 128 (got %d, %d)", block_q, block_k);
+  const int64_t B = q->shape[0], Hq = q->shape[1], Sq = q->shape[2], Hkv = k->shape[1];
+  if ((s = check_seqlens("seqlens", seqlens, B)) != FA_OK) return s;
+  if (!block_idx) return fail(FA_ERR_NULL, "block_idx is NULL");
+  if (block_idx->ndim != 2 && block_idx->ndim != 4) return fail(FA_ERR_SHAPE, "block_idx must have rank 2 or 4");
+  if ((s = check_tensor("block_idx", block_idx, block_idx->ndim, false)) != FA_OK) return s;
+  if ((s = check_dtype("block_idx", block_idx, FA_I32)) != FA_OK) return s;
+  fa::FwdParams p;
+  fill_common(p, q, k, v, o, lse, scale);
+  const int nd = block_idx->ndim;
+  const int64_t nqb = block_idx->shape[nd - 2], max_sel = block_idx->shape[nd - 1];
+  if (nqb < (Sq + block_q - 1) / block_q) return fail(FA_ERR_SHAPE, "block_idx has %lld query blocks, need %lld", (long long)nqb, (long long)((Sq + block_q - 1) / block_q));
+  if (max_sel > 256) return fail(FA_ERR_UNSUPPORTED, "maxSel %lld > 256", (long long)max_sel);
+  if (nd == 4) {
+    if ((block_idx->shape[0] != B && block_idx->shape[0] != 1) || (block_idx->shape[1] != Hkv && block_idx->shape[1] != 1))
+      return fail(FA_ERR_SHAPE, "block_idx must be [B|1, Hkv|1, nQB, maxSel]");
+    p.bi_sb = block_idx->shape[0] == 1 ? 0 : block_idx->stride[0];
+    p.bi_sh = block_idx->shape[1] == 1 ? 0 : block_idx->stride[1];
+  }
+  p.bi_sq = block_idx->stride[nd - 2];
+  p.max_sel = (int32_t)max_sel;
+  p.block_idx = (const int32_t*)block_idx->data;
+  p.seqlens_q = seqlens ? (const int32_t*)seqlens->data : nullptr;
+  p.seqlens_k = p.seqlens_q;
+  if (B * Hq * Sq == 0) return FA_OK;
+  if (max_sel > 0 && !block_idx->data) return fail(FA_ERR_NULL, "block_idx.data is NULL");
+  return hip_status(fa::launch_dense(to_dt(q->dtype), (int)q->shape[3], false, false, true, p, (hipStream_t)stream));
+}
+
+fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                             const fa_tensor* idx, float scale, const fa_tensor* o,
+                             const fa_tensor* lse, void* stream) {
+  clear_error();
+  fa_status s;
+  if ((s = check_tensor("q", q, 3, true)) != FA_OK) return s;
+  if ((s = check_tensor("k", k, 2, true)) != FA_OK) return s;
+  if ((s = check_tensor("v", v, 2, true)) != FA_OK) return s;
+  if ((s = check_tensor("idx", idx, 2, false)) != FA_OK) return s;
+  if ((s = check_tensor("o", o, 3, true)) != FA_OK) return s;
+  if ((s = check_tensor("lse", lse, 2, false)) != FA_OK) return s;
+  if (q->dtype != FA_F16 && q->dtype != FA_BF16)
+    return fail(FA_ERR_DTYPE, "q dtype must be f16 or bf16, got %s", dtype_name(q->dtype));
+  if ((s = check_dtype("k", k, q->dtype)) != FA_OK) return s;
+  if ((s = check_dtype("v", v, q->dtype)) != FA_OK) return s;
+  if ((s = check_dtype("o", o, q->dtype)) != FA_OK) return s;
+  if ((s = check_dtype("idx", idx, FA_I32)) != FA_OK) return s;
+  if ((s = check_dtype("lse", lse, FA_F32)) != FA_OK) return s;
+  const int64_t T = q->shape[0], Hq = q->shape[1], Dqk = q->shape[2];
+  const int64_t S = k->shape[0], Dv = v->shape[1], W = idx->shape[1];
+  if (k->shape[1] != Dqk) return fail(FA_ERR_SHAPE, "k must be [S, Dqk]");
+  if (v->shape[0] != S) return fail(FA_ERR_SHAPE, "v must have as many rows as k");
+  if (idx->shape[0] != T) return fail(FA_ERR_SHAPE, "idx must be [T, W]");
+  if (o->shape[0] != T || o->shape[1] != Hq || o->shape[2] != Dv) return fail(FA_ERR_SHAPE, "o must be [T, Hq, Dv]");
+  if (lse->shape[0] != T || lse->shape[1] != Hq) return fail(FA_ERR_SHAPE, "lse must be [T, Hq]");
+  if ((s = check_contiguous("lse", lse)) != FA_OK) return s;
+  if (!scale_ok(scale)) return fail(FA_ERR_VALUE, "scale must be finite and > 0");
+  if (Dqk != 576 || Dv != 512) return fail(FA_ERR_UNSUPPORTED, "only Dqk = 576, Dv = 512 is supported");
+  if (Hq % 32 != 0) return fail(FA_ERR_UNSUPPORTED, "Hq (%lld) must be a multiple of 32", (long long)Hq);
+  if (W > 4096) return fail(FA_ERR_UNSUPPORTED, "W (%lld) > 4096", (long long)W);
+  if (!fits_i32(T * Hq) || !fits_i32(S) || !fits_i32(W)) return fail(FA_ERR_UNSUPPORTED, "problem too large");
+  if (T * Hq == 0) return FA_OK;
+  if (W > 0 && !idx->data) return fail(FA_ERR_NULL, "idx.data is NULL");
+  fa::TopkParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q->data;
+  p.k = k->data;
+  p.v = v->data;
+  p.o = o->data;
+  p.lse = (float*)lse->data;
+  p.idx = (const int32_t*)idx->data;
+  p.q_st = q->stride[0]; p.q_sh = q->stride[1];
+  p.k_ss = k->stride[0]; p.v_ss = v->stride[0];
+  p.o_st = o->stride[0]; p.o_sh = o->stride[1];
+  p.idx_st = idx->stride[0];
+  p.T = (int32_t)T; p.Hq = (int32_t)Hq; p.S = (int32_t)S; p.W = (int32_t)W;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(fa::launch_topk(to_dt(q->dtype), p, (hipStream_t)stream));
+}
+
+const char* fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL";
+    case FA_ERR_DTYPE: return "FA_ERR_DTYPE";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE";
+    case FA_ERR_STRIDE: return "FA_ERR_STRIDE";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_VALUE: return "FA_ERR_VALUE";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    default: return "FA_ERR_UNKNOWN";
+  }
+}
+
+const char* fa_last_error(void) { return g_err; }
+
+int fa_version(void) { return 100; }
+
+}  // extern "C"

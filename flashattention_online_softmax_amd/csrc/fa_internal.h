@@ -1,0 +1,61 @@
+// Internal interface between the C-ABI layer (fa_abi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+enum class Dt : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Parameters of the dense / block-sparse forward kernels. All strides are in
+// elements. Shapes are already validated by the host layer.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;              // [B, Hq, Sq] contiguous
+  const uint8_t* mask;     // nullable; element (b, hq, i, j) at b*m_sb + hq*m_sh + i*m_ss + j
+  const int32_t* seqlens_q;  // nullable [B]
+  const int32_t* seqlens_k;  // nullable [B]
+  const int32_t* block_idx;  // block-sparse only: (b, hkv, qb, slot) at b*bi_sb + hkv*bi_sh + qb*bi_sq + slot
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int64_t m_sb, m_sh, m_ss;
+  int64_t bi_sb, bi_sh, bi_sq;
+  int32_t B, Hq, Hkv, G, Sq, Skv;
+  int32_t max_sel;         // block-sparse slots per query block
+  int32_t mask_vec4;       // 1: mask rows may be read 4 bytes at a time
+  int32_t n_mblocks;       // query blocks per head
+  int32_t n_hgroups;       // head groups per KV head (G / heads per workgroup)
+  float scale;             // softmax scale (LSE is reported in these units)
+  float scale_log2;        // scale * log2(e): scores enter exp2 through one FMA
+};
+
+// Top-k gathered MLA forward parameters.
+struct TopkParams {
+  const void* q;     // [T, Hq, Dqk]
+  const void* k;     // [S, Dqk]
+  const void* v;     // [S, Dv]
+  void* o;           // [T, Hq, Dv]
+  float* lse;        // [T, Hq]
+  const int32_t* idx;  // [T, W]
+  int64_t q_st, q_sh;
+  int64_t k_ss, v_ss;
+  int64_t o_st, o_sh;
+  int64_t idx_st;
+  int32_t T, Hq, S, W;
+  int32_t n_htiles;  // head tiles per token
+  float scale;
+  float scale_log2;
+};
+
+// Launchers: enqueue on `stream`, return the HIP status of the launch.
+hipError_t launch_dense(Dt dt, int D, bool causal, bool has_mask, bool sparse,
+                        FwdParams& p, hipStream_t stream);
+hipError_t launch_topk(Dt dt, TopkParams& p, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,171 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) attention forward library libfa.so.
+ *
+ * What every entry point computes, per output row r with key set K_r:
+ *
+ *   s_j   = scale * <q_r, k_j>                          for j in K_r
+ *   O_r   = sum_j softmax(s)_j * v_j                     (stored in q's dtype)
+ *   LSE_r = ln sum_j exp(s_j)                            (fp32)
+ *
+ * evaluated tile by tile with an online softmax: a running row maximum m, a
+ * running row sum l of exp(s - m) and an output accumulator rescaled by
+ * exp(m_old - m_new) whenever m grows (every growth, i.e. an exact running
+ * maximum). This is the standard-vs-tiled attention equivalence and the loop
+ * invariant of the "FlashAttention correctness verification" page (sections
+ * on the tiled computation and on formal verification), with the exact-max
+ * rule of the flash-attention SM100 sparse-MLA page (background and
+ * threshold-branch sections). Rows whose key set is empty produce O_r = 0
+ * and LSE_r = -inf.
+ *
+ * Numerics: Q.K^T and P.V run on MFMA with fp32 accumulation; for fp16/bf16
+ * inputs P is rounded to the input dtype (round to nearest even) before P.V
+ * while the row sum l accumulates the unrounded fp32 p; O = acc / l is rounded
+ * to the output dtype. fp32 inputs keep P in fp32.
+ *
+ * Conventions shared by all entry points
+ *  - Tensors are described by fa_tensor: a device pointer, dtype, rank,
+ *    shape and strides in ELEMENTS. The last dimension must be contiguous
+ *    (stride 1). Row strides of Q/K/V/O must keep every row 16-byte aligned
+ *    (multiples of 8 elements for 16-bit types, 4 for fp32) and the data
+ *    pointers must be 16-byte aligned.
+ *  - The caller owns every buffer. The library allocates nothing, keeps no
+ *    pointer after returning and has no global mutable state except a
+ *    thread-local error string.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and the call returns without waiting. The caller synchronises.
+ *  - Arguments are validated on the host before anything is launched. On any
+ *    error nothing is launched, the status is returned and fa_last_error()
+ *    describes it. No C++ exception crosses this interface.
+ *  - A problem with no output rows (B, Hq, Sq or T equal to 0) returns FA_OK
+ *    and launches nothing.
+ *  - Unchecked preconditions (documented, not validated because they live in
+ *    device memory): indices inside their range or negative; valid indices
+ *    distinct within one row / list; seqlens[b] <= the sequence length.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_dtype {
+  FA_F32 = 0,
+  FA_F16 = 1,
+  FA_BF16 = 2,
+  FA_U8 = 3,
+  FA_I32 = 4
+} fa_dtype;
+
+typedef struct fa_tensor {
+  void* data;        /* device pointer (may be NULL only when the tensor is empty) */
+  int32_t dtype;     /* an fa_dtype value */
+  int32_t ndim;      /* 1..4 */
+  int64_t shape[4];  /* shape[0..ndim) */
+  int64_t stride[4]; /* strides in elements; the last one must be 1 */
+} fa_tensor;
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA_ERR_DTYPE = 2,       /* wrong or mismatched dtype */
+  FA_ERR_SHAPE = 3,       /* rank or extents do not fit together */
+  FA_ERR_STRIDE = 4,      /* non-contiguous last dim, misaligned pointer or row */
+  FA_ERR_UNSUPPORTED = 5, /* valid request outside what this build implements */
+  FA_ERR_VALUE = 6,       /* non-finite scale, bad flag, bad block size value */
+  FA_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
+} fa_status;
+
+/*
+ * Dense attention forward, with optional causal mask, boolean mask, GQA head
+ * broadcast and per-batch sequence lengths.
+ *
+ *  q    [B, Hq, Sq, D]   fp32 / fp16 / bf16 (BNSD, strided)
+ *  k    [B, Hkv, Skv, D] same dtype as q; Hq % Hkv == 0; query head h reads
+ *                        KV head h / (Hq / Hkv) (the GQA layout of the
+ *                        ops-transformer pytest page, section 5.1)
+ *  v    [B, Hkv, Skv, Dv] same dtype; Dv == D
+ *  mask NULL, or uint8 [Sq, Skv] shared by every batch and head, or
+ *       uint8 [B|1, Hq|1, Sq, Skv] (size-1 dims broadcast; their stride is
+ *       ignored). Non-zero = the position is excluded (the atten_mask
+ *       convention of the Ascend FlashAttentionScore README, parameter table).
+ *  seqlens_q, seqlens_k  NULL or int32 [B]: rows i >= seqlens_q[b] have no
+ *       keys (O = 0, LSE = -inf); keys j >= seqlens_k[b] are excluded (the
+ *       per-batch actual_seq_lengths of the PyPTO BSA README, section 1).
+ *  causal  0 or 1. Key j is excluded when j > i + (Lk - Lq), Lq/Lk being the
+ *       (sequence-length-cut) query/key lengths: bottom-right alignment.
+ *  scale   finite float > 0 multiplying q.k (the scale of the attention
+ *       formula); scale * log2(e) must be a normal float.
+ *  o    [B, Hq, Sq, Dv] in q's dtype (BNSD, strided)
+ *  lse  fp32 [B, Hq, Sq], contiguous; natural-log LSE of the scaled scores.
+ *
+ * Supported: D == Dv in {64, 128}. Masked/excluded keys are never read
+ * into the P.V product with a non-zero weight.
+ */
+fa_status fa_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                 const fa_tensor* mask, const fa_tensor* seqlens_q,
+                 const fa_tensor* seqlens_k, int causal, float scale,
+                 const fa_tensor* o, const fa_tensor* lse, void* stream);
+
+/*
+ * Block-sparse attention forward (the Mask2Idx block lists of the PyPTO BSA
+ * README, sections 1 and 3.2, read here directly by the kernel instead of
+ * being compacted into new K/V tensors).
+ *
+ *  q, k, v, o, lse as in fa_fwd (same dtypes, GQA rule and layouts).
+ *  block_idx  int32 [nQB, maxSel] shared by every batch and KV head, or
+ *       int32 [B|1, Hkv|1, nQB, maxSel]; nQB >= ceil(Sq / block_q).
+ *       Row qb lists the KV blocks that query block qb attends to; a slot
+ *       holding a negative value is unused and contributes nothing (it may
+ *       sit anywhere in the list). Valid entries must lie in
+ *       [0, ceil(Skv / block_k)) and be distinct within a row (unchecked).
+ *  block_q, block_k  must both be 128.
+ *  seqlens  NULL or int32 [B], applied to queries and keys alike: rows
+ *       i >= seqlens[b] produce O = 0 and LSE = -inf, keys j >= seqlens[b]
+ *       are excluded.
+ *  maxSel must be <= 256.
+ */
+fa_status fa_fwd_blocksparse(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                             const fa_tensor* block_idx, int block_q, int block_k,
+                             const fa_tensor* seqlens, float scale, const fa_tensor* o,
+                             const fa_tensor* lse, void* stream);
+
+/*
+ * Top-k gathered sparse attention forward with one shared KV head (the
+ * sparse-MLA forward of the flash-attention SM100 page, background section:
+ * every row attends only to its W indexer-chosen keys). The running maximum
+ * is always exact (rescale threshold 0), so the largest weight of a row is
+ * exactly 1 before the P.V product.
+ *
+ *  q   [T, Hq, Dqk] fp16 / bf16 (strided; last dim contiguous)
+ *  k   [S, Dqk] same dtype (the latent+rope key rows)
+ *  v   [S, Dv] same dtype; may alias k (v.data == k.data with the same row
+ *      stride, i.e. V = the first Dv columns of K, the MLA latent)
+ *  idx int32 [T, W], last dim contiguous; idx[t, s] in [0, S) names a key,
+ *      negative = unused slot (anywhere in the row)
+ *  o   [T, Hq, Dv] in q's dtype (strided)
+ *  lse fp32 [T, Hq], contiguous
+ *
+ * Supported: Dqk == 576, Dv == 512, Hq a multiple of 32, W <= 4096.
+ */
+fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                             const fa_tensor* idx, float scale, const fa_tensor* o,
+                             const fa_tensor* lse, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* fa_status_str(fa_status s);
+
+/* Detail of the last error returned on this thread ("" if none). Valid until
+ * the next call into the library on the same thread. */
+const char* fa_last_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,10 +1,13 @@
 """Seeded synthetic inputs shared by the tests, the smoke check and the bench.
 
 This module only draws inputs; it holds none of the attention arithmetic.
-All draws come from numpy's PCG64 generator in a fixed order (Q, K, V, then
-mask / row selection / block lists / indices), as float32, and are rounded
-to the target dtype with round-to-nearest-even (torch ``.to``). The same
-CPU tensors feed both the GPU library (after upload) and the oracle.
+Every workload seed is split with numpy's SeedSequence into one child stream
+per input in a fixed order (Q, K, V, then mask / row selection / block lists
+/ indices); large tensors are drawn in fixed 4M-element chunks, each from its
+own grandchild PCG64 stream, on a thread pool (the values depend only on the
+seed and the shape, never on the thread count). Draws are float32 and are
+rounded to the target dtype with round-to-nearest-even (torch ``.to``). The
+same CPU tensors feed both the GPU library (after upload) and the oracle.
 
 Named workloads (sizes as the pages' configurations give them):
 
@@ -21,20 +24,64 @@ Named workloads (sizes as the pages' configurations give them):
                        self key + min(W-1, t) earlier keys per token
   causal_bf16_s8192    bf16 BNSD, B=2, H=16, S=8192, D=128, causal
 """
+import concurrent.futures
 import math
+import os
 
 import numpy as np
 import torch
 
+CHUNK = 1 << 22
+_POOL = concurrent.futures.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+
 DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
-def rng(seed: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(seed))
+class Stream:
+    """A seeded source of inputs: each call to ``child()`` hands out the next
+    independent stream, in call order."""
+
+    def __init__(self, seed):
+        self._ss = seed if isinstance(seed, np.random.SeedSequence) else np.random.SeedSequence(seed)
+        self._n = 0
+
+    def child(self) -> np.random.SeedSequence:
+        c = np.random.SeedSequence(self._ss.entropy, spawn_key=self._ss.spawn_key + (self._n,))
+        self._n += 1
+        return c
+
+    def gen(self) -> np.random.Generator:
+        return np.random.Generator(np.random.PCG64(self.child()))
+
+    # numpy Generator API used by the helpers below, on a fresh child stream
+    def choice(self, *a, **k):
+        return self.gen().choice(*a, **k)
+
+    def random(self, *a, **k):
+        return self.gen().random(*a, **k)
+
+    def integers(self, *a, **k):
+        return self.gen().integers(*a, **k)
 
 
-def normal(g: np.random.Generator, shape) -> np.ndarray:
-    return g.standard_normal(size=shape, dtype=np.float32)
+def rng(seed: int) -> Stream:
+    return Stream(seed)
+
+
+def normal(g: Stream, shape) -> np.ndarray:
+    """float32 N(0, 1) draws of ``shape`` from the next child stream of ``g``."""
+    ss = g.child()
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = np.empty(n, dtype=np.float32)
+    nchunks = (n + CHUNK - 1) // CHUNK
+    kids = ss.spawn(nchunks)
+
+    def fill(i):
+        a, b = i * CHUNK, min(n, (i + 1) * CHUNK)
+        np.random.Generator(np.random.PCG64(kids[i])).standard_normal(size=b - a, dtype=np.float32, out=out[a:b])
+
+    list(_POOL.map(fill, range(nchunks)))
+    return out.reshape(shape)
 
 
 def cast(x: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
@@ -46,10 +93,18 @@ def bernoulli_mask(g, Sq, Skv, density, keep_diagonal=True) -> torch.Tensor:
     """uint8 [Sq, Skv]; each entry is 1 (masked) with probability ``density``;
     mask[i, i] = 0 when ``keep_diagonal``."""
     m = np.empty((Sq, Skv), dtype=np.uint8)
-    step = 1024
-    for r0 in range(0, Sq, step):
+    ss = g.child()
+    step = max(1, CHUNK // max(Skv, 1))
+    starts = list(range(0, Sq, step))
+    kids = ss.spawn(len(starts))
+
+    def fill(i):
+        r0 = starts[i]
         r1 = min(Sq, r0 + step)
-        m[r0:r1] = g.random(size=(r1 - r0, Skv), dtype=np.float32) < density
+        gi = np.random.Generator(np.random.PCG64(kids[i]))
+        m[r0:r1] = gi.random(size=(r1 - r0, Skv), dtype=np.float32) < density
+
+    list(_POOL.map(fill, range(len(starts))))
     if keep_diagonal:
         d = np.arange(min(Sq, Skv))
         m[d, d] = 0
@@ -59,15 +114,16 @@ def bernoulli_mask(g, Sq, Skv, density, keep_diagonal=True) -> torch.Tensor:
 def pick_rows(g, nrows_total, frac) -> np.ndarray:
     """floor(frac * nrows_total) distinct flattened row ids, sorted."""
     n = int(math.floor(frac * nrows_total))
-    return np.sort(g.choice(nrows_total, size=n, replace=False)).astype(np.int64)
+    return np.sort(g.gen().choice(nrows_total, size=n, replace=False)).astype(np.int64)
 
 
 def causal_block_lists(g, nqb, max_sel) -> torch.Tensor:
     """int32 [nqb, max_sel]: query block i keeps KV block i plus min(max_sel-1, i)
     distinct earlier blocks drawn uniformly; ascending; unused slots -1."""
     out = np.full((nqb, max_sel), -1, dtype=np.int32)
+    gg = g.gen()
     for i in range(nqb):
-        extra = g.choice(i, size=min(max_sel - 1, i), replace=False) if i > 0 else np.array([], np.int64)
+        extra = gg.choice(i, size=min(max_sel - 1, i), replace=False) if i > 0 else np.array([], np.int64)
         sel = np.sort(np.concatenate([extra, [i]]).astype(np.int32))
         out[i, :sel.size] = sel
     return torch.from_numpy(out)
@@ -83,6 +139,7 @@ def topk_indices(g, T, S, W):
     """
     a = np.full((T, W), -1, dtype=np.int32)
     b = np.full((T, W), -1, dtype=np.int32)
+    g = g.gen()
     for t in range(T):
         n = min(W - 1, t, S - 1) if S > 0 else 0
         if n == t:

@@ -1,0 +1,160 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/fa.h declares, and rejects invalid arguments on the host before any
+launch (no GPU is touched: every call here fails validation or is empty)."""
+import ctypes
+import math
+import os
+
+import pytest
+import torch
+
+import flashattention_online_softmax_amd as fa
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        from flashattention_online_softmax_amd import build
+        build.build()
+    return fa.load()
+
+
+def T(shape, dtype=fa.FA_BF16, stride=None, data=FAKE):
+    t = fa.FaTensor()
+    t.data = data
+    t.dtype = dtype
+    t.ndim = len(shape)
+    if stride is None:
+        stride, s = [], 1
+        for n in reversed(shape):
+            stride.insert(0, s)
+            s *= n
+    for i, (n, st) in enumerate(zip(shape, stride)):
+        t.shape[i] = n
+        t.stride[i] = st
+    return t
+
+
+def R(t):
+    return None if t is None else ctypes.byref(t)
+
+
+def name(lib, s):
+    return lib.fa_status_str(s).decode()
+
+
+def call_fwd(lib, q, k, v, o, lse, mask=None, sq=None, sk=None, causal=0, scale=0.1):
+    return name(lib, lib.fa_fwd(R(q), R(k), R(v), R(mask), R(sq), R(sk), causal, scale, R(o), R(lse), None))
+
+
+def good(B=2, Hq=4, Hkv=2, S=64, D=128, dt=fa.FA_BF16):
+    return (T([B, Hq, S, D], dt), T([B, Hkv, S, D], dt), T([B, Hkv, S, D], dt),
+            T([B, Hq, S, D], dt), T([B, Hq, S], fa.FA_F32))
+
+
+def test_exports_every_declared_function(lib):
+    names = fa.declared_functions()
+    assert {"fa_fwd", "fa_fwd_blocksparse", "fa_fwd_topk_gather", "fa_status_str",
+            "fa_last_error", "fa_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.fa_version() == 100
+
+
+def test_status_names(lib):
+    assert [name(lib, i) for i in range(8)] == [
+        "FA_OK", "FA_ERR_NULL", "FA_ERR_DTYPE", "FA_ERR_SHAPE", "FA_ERR_STRIDE",
+        "FA_ERR_UNSUPPORTED", "FA_ERR_VALUE", "FA_ERR_HIP"]
+
+
+def test_fa_fwd_validation(lib):
+    q, k, v, o, lse = good()
+    assert call_fwd(lib, None, k, v, o, lse) == "FA_ERR_NULL"
+    assert call_fwd(lib, q, k, v, o, lse, causal=2) == "FA_ERR_VALUE"
+    assert call_fwd(lib, q, k, v, o, lse, scale=float("nan")) == "FA_ERR_VALUE"
+    assert call_fwd(lib, q, k, v, o, lse, scale=-1.0) == "FA_ERR_VALUE"
+    assert call_fwd(lib, q, k, v, o, lse, scale=0.0) == "FA_ERR_VALUE"
+    assert call_fwd(lib, q, T([2, 2, 64, 128], fa.FA_F16), v, o, lse) == "FA_ERR_DTYPE"
+    assert call_fwd(lib, q, k, v, o, T([2, 4, 64], fa.FA_BF16)) == "FA_ERR_DTYPE"
+    assert call_fwd(lib, q, T([2, 3, 64, 128]), T([2, 3, 64, 128]), o, lse) == "FA_ERR_SHAPE"
+    assert b"multiple of Hkv" in lib.fa_last_error()
+    assert call_fwd(lib, *good(D=96)) == "FA_ERR_UNSUPPORTED"
+    assert call_fwd(lib, *good(dt=fa.FA_I32)) == "FA_ERR_DTYPE"
+    assert call_fwd(lib, q, k, v, T([2, 4, 64, 64]), lse) == "FA_ERR_SHAPE"
+    assert call_fwd(lib, q, k, v, o, T([2, 4, 64], fa.FA_F32, stride=[512, 1, 4])) == "FA_ERR_STRIDE"
+    # last dim not contiguous / misaligned pointer / misaligned row stride
+    assert call_fwd(lib, T([2, 4, 64, 128], stride=[65536, 16384, 256, 2]), k, v, o, lse) == "FA_ERR_STRIDE"
+    assert call_fwd(lib, T([2, 4, 64, 128], data=FAKE + 2), k, v, o, lse) == "FA_ERR_STRIDE"
+    assert call_fwd(lib, T([2, 4, 64, 128], stride=[4 * 64 * 130, 64 * 130, 130, 1]), k, v, o, lse) == "FA_ERR_STRIDE"
+    # mask / seqlens
+    assert call_fwd(lib, q, k, v, o, lse, mask=T([64, 64], fa.FA_F16)) == "FA_ERR_DTYPE"
+    assert call_fwd(lib, q, k, v, o, lse, mask=T([64, 63], fa.FA_U8)) == "FA_ERR_SHAPE"
+    assert call_fwd(lib, q, k, v, o, lse, mask=T([3, 1, 64, 64], fa.FA_U8)) == "FA_ERR_SHAPE"
+    assert call_fwd(lib, q, k, v, o, lse, sq=T([2], fa.FA_F32)) == "FA_ERR_DTYPE"
+    assert call_fwd(lib, q, k, v, o, lse, sk=T([3], fa.FA_I32)) == "FA_ERR_SHAPE"
+
+
+def test_empty_problems_launch_nothing(lib):
+    # no output rows: FA_OK without touching the device (no GPU here)
+    assert call_fwd(lib, *good(B=0)) == "FA_OK"
+    q, k, v, o, lse = good(S=0)
+    assert call_fwd(lib, q, k, v, o, lse) == "FA_OK"
+    assert lib.fa_last_error() == b""
+
+
+def test_blocksparse_validation(lib):
+    q, k, v, o, lse = good(S=256)
+    bi = T([2, 16], fa.FA_I32)
+
+    def bs(bi=bi, bq=128, bk=128, seq=None, q=q):
+        return name(lib, lib.fa_fwd_blocksparse(R(q), R(k), R(v), R(bi), bq, bk, R(seq), 0.1, R(o), R(lse), None))
+
+    assert bs(bq=64) == "FA_ERR_UNSUPPORTED"
+    assert bs(bi=None) == "FA_ERR_NULL"
+    assert bs(bi=T([1, 16], fa.FA_I32)) == "FA_ERR_SHAPE"  # too few query blocks
+    assert bs(bi=T([2, 300], fa.FA_I32)) == "FA_ERR_UNSUPPORTED"
+    assert bs(bi=T([2, 16], fa.FA_F32)) == "FA_ERR_DTYPE"
+    assert bs(bi=T([3, 2, 2, 16], fa.FA_I32)) == "FA_ERR_SHAPE"
+    assert bs(seq=T([2], fa.FA_U8)) == "FA_ERR_DTYPE"
+    q0, k0, v0, o0, l0 = good(B=0, S=256)
+    assert name(lib, lib.fa_fwd_blocksparse(R(q0), R(k0), R(v0), R(bi), 128, 128, None, 0.1, R(o0), R(l0), None)) == "FA_OK"
+
+
+def test_topk_validation(lib):
+    def tk(q=T([8, 128, 576]), k=T([16, 576]), v=None, idx=T([8, 32], fa.FA_I32),
+           o=T([8, 128, 512]), lse=T([8, 128], fa.FA_F32), scale=0.04):
+        if v is None:
+            v = T([16, 512], stride=[576, 1])
+        return name(lib, lib.fa_fwd_topk_gather(R(q), R(k), R(v), R(idx), scale, R(o), R(lse), None))
+
+    assert tk(q=T([8, 128, 576], fa.FA_F32), k=T([16, 576], fa.FA_F32), v=T([16, 512], fa.FA_F32),
+              o=T([8, 128, 512], fa.FA_F32)) == "FA_ERR_DTYPE"
+    assert tk(idx=T([8, 32], fa.FA_U8)) == "FA_ERR_DTYPE"
+    assert tk(q=T([8, 128, 512]), k=T([16, 512])) == "FA_ERR_UNSUPPORTED"
+    assert tk(q=T([8, 100, 576]), o=T([8, 100, 512]), lse=T([8, 100], fa.FA_F32)) == "FA_ERR_UNSUPPORTED"
+    assert tk(idx=T([8, 5000], fa.FA_I32)) == "FA_ERR_UNSUPPORTED"
+    assert tk(idx=T([7, 32], fa.FA_I32)) == "FA_ERR_SHAPE"
+    assert tk(v=T([15, 512])) == "FA_ERR_SHAPE"
+    assert tk(scale=float("inf")) == "FA_ERR_VALUE"
+    assert tk(q=T([0, 128, 576]), idx=T([0, 32], fa.FA_I32), o=T([0, 128, 512]),
+              lse=T([0, 128], fa.FA_F32)) == "FA_OK"
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        fa.fa_fwd(q, q, q, scale=1.0)
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        fa.fa_fwd_topk_gather(torch.zeros(1, 32, 576, dtype=torch.bfloat16),
+                              torch.zeros(4, 576, dtype=torch.bfloat16),
+                              torch.zeros(4, 512, dtype=torch.bfloat16),
+                              torch.zeros(1, 4, dtype=torch.int32), scale=1.0)
+
+
+def test_describe_marshals_shape_and_strides():
+    t = torch.zeros(2, 3, 5, 8).transpose(1, 2)
+    d = fa.describe(t)
+    assert d.ndim == 4 and list(d.shape[:4]) == [2, 5, 3, 8] and list(d.stride[:4]) == [120, 8, 40, 1]
+    assert d.dtype == fa.FA_F32

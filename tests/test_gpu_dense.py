@@ -1,0 +1,184 @@
+"""GPU parity of fa_fwd (dense, causal, boolean mask, GQA, sequence lengths)
+against the fp64 oracle, element by element, on seeded inputs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import flashattention_online_softmax_amd as fa
+import oracle
+import synth
+from fa_testutil import absv, check, f32, gpu, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def run_dense(case, q, k, v, scale, causal=False, mask=None, sq=None, sk=None):
+    o, lse = fa.fa_fwd(*gpu(q, k, v), scale=scale, causal=causal, mask=gpu(mask),
+                       seqlens_q=gpu(sq), seqlens_k=gpu(sk))
+    torch.cuda.synchronize()
+    kw = dict(scale=f32(scale), causal=causal, mask=mask, seqlens_q=sq, seqlens_k=sk)
+    o_ref, lse_ref = oracle.attn_dense(q, k, v, **kw)
+    o_abs, _ = oracle.attn_dense(q, k, absv(v), **kw)
+    return check(case, o, lse, o_ref, lse_ref, q.dtype, o_abs)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_ragged(dtype, D, causal):
+    # 300 rows/keys: several 64-key tiles, a ragged tail, a partial query block
+    _, q, k, v = synth.dense_inputs(100 + D + causal, 2, 4, 4, 300, 300, D, D, dtype)
+    run_dense("dense_%s_D%d_causal%d" % (dtype, D, causal), q, k, v, 1 / math.sqrt(D), causal)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_gqa_causal_mask(dtype):
+    g, q, k, v = synth.dense_inputs(7, 2, 8, 2, 333, 333, 128, 128, dtype)
+    mask = synth.bernoulli_mask(g, 333, 333, 0.05)
+    run_dense("gqa_mask_%s" % dtype, q, k, v, 1 / math.sqrt(128), True, mask)
+
+
+def test_mask_4d_broadcasts_and_empty_rows():
+    g, q, k, v = synth.dense_inputs(8, 2, 3, 1, 130, 200, 64, 64, "f16")
+    m = torch.from_numpy((g.random((2, 1, 130, 200)) < 0.3).astype(np.uint8))
+    m[1, 0, 5] = 1  # a fully masked row -> O = 0, LSE = -inf
+    rep = run_dense("mask4d_b1", q, k, v, 0.125, False, m)
+    m2 = torch.from_numpy((g.random((1, 3, 130, 200)) < 0.5).astype(np.uint8))
+    run_dense("mask4d_1h", q, k, v, 0.125, True, m2)
+    assert rep["rows"] == 2 * 3 * 130
+
+
+def test_zero_mask_is_bitwise_no_mask():
+    _, q, k, v = synth.dense_inputs(9, 1, 2, 2, 190, 190, 128, 128, "bf16")
+    qq, kk, vv = gpu(q, k, v)
+    a, la = fa.fa_fwd(qq, kk, vv, scale=0.1, causal=True)
+    b, lb = fa.fa_fwd(qq, kk, vv, scale=0.1, causal=True,
+                      mask=torch.zeros((190, 190), dtype=torch.uint8, device="cuda"))
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_seqlens_and_cross_lengths(dtype):
+    _, q, k, v = synth.dense_inputs(10, 3, 2, 2, 257, 400, 128, 128, dtype)
+    sq = torch.tensor([257, 100, 0], dtype=torch.int32)
+    sk = torch.tensor([400, 77, 5], dtype=torch.int32)
+    run_dense("seqlens_causal_%s" % dtype, q, k, v, 0.09, True, None, sq, sk)
+    run_dense("seqlens_%s" % dtype, q, k, v, 0.09, False, None, sq, sk)
+    run_dense("cross_causal_%s" % dtype, q[:, :, :100], k, v, 0.09, True)  # Sq < Skv
+
+
+def test_strided_bsnd_views():
+    g = synth.rng(11)
+    q = synth.cast(synth.normal(g, (2, 150, 4, 128)), torch.bfloat16)  # [B, S, H, D]
+    k = synth.cast(synth.normal(g, (2, 150, 4, 128)), torch.bfloat16)
+    v = synth.cast(synth.normal(g, (2, 150, 4, 128)), torch.bfloat16)
+    qg, kg, vg = (t.cuda().transpose(1, 2) for t in (q, k, v))  # BNSD views, not contiguous
+    o, lse = fa.fa_fwd(qg, kg, vg, scale=0.088, causal=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_dense(q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2),
+                                       scale=f32(0.088), causal=True)
+    o_abs, _ = oracle.attn_dense(q.transpose(1, 2), k.transpose(1, 2), v.abs().transpose(1, 2),
+                                 scale=f32(0.088), causal=True)
+    check("strided_bsnd", o, lse, o_ref, lse_ref, torch.bfloat16, o_abs)
+
+
+def test_out_of_range_memory_is_never_read():
+    # K/V rows past Skv (and past seqlens_k) hold NaN: they must not leak.
+    _, q, k, v = synth.dense_inputs(12, 1, 2, 2, 100, 100, 128, 128, "f16")
+    kp = torch.full((1, 2, 164, 128), float("nan"), dtype=torch.float16, device="cuda")
+    vp = torch.full((1, 2, 164, 128), float("nan"), dtype=torch.float16, device="cuda")
+    kp[:, :, :100] = k.cuda()
+    vp[:, :, :100] = v.cuda()
+    o, lse = fa.fa_fwd(q.cuda(), kp[:, :, :100], vp[:, :, :100], scale=0.1, causal=False)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_dense(q, k, v, scale=f32(0.1))
+    o_abs, _ = oracle.attn_dense(q, k, v.abs(), scale=f32(0.1))
+    check("nan_tail", o, lse, o_ref, lse_ref, torch.float16, o_abs)
+    kp[:, :, 60:100] = float("nan")
+    vp[:, :, 60:100] = float("nan")
+    sk = torch.tensor([60], dtype=torch.int32)
+    o, lse = fa.fa_fwd(q.cuda(), kp[:, :, :100], vp[:, :, :100], scale=0.1, seqlens_k=sk.cuda())
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_dense(q, k, v, scale=f32(0.1), seqlens_k=sk)
+    o_abs, _ = oracle.attn_dense(q, k, v.abs(), scale=f32(0.1), seqlens_k=sk)
+    check("nan_past_seqlen", o, lse, o_ref, lse_ref, torch.float16, o_abs)
+
+
+def test_extreme_rows_fp16():
+    g, q, k, v = synth.dense_inputs(13, 1, 4, 4, 256, 256, 128, 128, "f16")
+    q32 = q.float()
+    q32[0, 1, ::7] *= 30.0
+    q = q32.half()
+    run_dense("extreme_x30_f16", q, k, v, 1 / math.sqrt(128), True)
+
+
+def test_single_key_and_single_row():
+    _, q, k, v = synth.dense_inputs(14, 1, 1, 1, 1, 1, 128, 128, "bf16")
+    o, lse = fa.fa_fwd(*gpu(q, k, v), scale=0.3)
+    torch.cuda.synchronize()
+    assert torch.equal(o.cpu(), v)  # one key: O = V exactly
+    _, q, k, v = synth.dense_inputs(15, 1, 1, 1, 64, 64, 64, 64, "f32")
+    o, _ = fa.fa_fwd(*gpu(q, k, v), scale=0.3, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o.cpu()[0, 0, 0], v[0, 0, 0])  # first causal row sees key 0 only
+
+
+def test_empty_problems():
+    _, q, k, v = synth.dense_inputs(16, 1, 2, 2, 8, 8, 64, 64, "bf16")
+    qq, kk, vv = gpu(q, k, v)
+    o, lse = fa.fa_fwd(qq[:, :, :0], kk, vv, scale=1.0)  # Sq = 0
+    assert o.shape == (1, 2, 0, 64)
+    o, lse = fa.fa_fwd(qq, kk[:, :, :0], vv[:, :, :0], scale=1.0)  # Skv = 0
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    o, lse = fa.fa_fwd(qq[:0], kk[:0], vv[:0], scale=1.0)  # B = 0
+    assert o.shape == (0, 2, 8, 64)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, checked on sampled rows computed one by one by the
+# oracle, in the launch configuration the benchmark times.
+# ---------------------------------------------------------------------------
+
+def _full_dense(name, n_rows, must_rows=()):
+    w = synth.workload(name)
+    q, k, v = w["q"], w["k"], w["v"]
+    mask = w.get("mask")
+    o, lse = fa.fa_fwd(*gpu(q, k, v), scale=w["scale"], causal=w["causal"], mask=gpu(mask))
+    torch.cuda.synchronize()
+    B, Hq, Sq, D = q.shape
+    g = np.random.default_rng(1234)
+    must = list(must_rows)
+    if "scaled_rows" in w:
+        must += list(g.choice(w["scaled_rows"].numpy(), size=64, replace=False))
+    rows = sample_rows(g, B * Hq * Sq, n_rows, must + [0, B * Hq * Sq - 1, Sq - 1, Sq])
+    kw = dict(scale=f32(w["scale"]), causal=w["causal"], mask=mask, rows=rows)
+    o_ref, lse_ref = oracle.attn_dense(q, k, v, **kw)
+    o_abs, _ = oracle.attn_dense(q, k, v.abs(), **kw)
+    o_s = o.reshape(-1, D)[torch.from_numpy(rows).cuda()]
+    l_s = lse.reshape(-1)[torch.from_numpy(rows).cuda()]
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+    return check("full_" + name, o_s, l_s, o_ref, lse_ref, q.dtype, o_abs, {"sampled_rows": len(rows)})
+
+
+def test_full_dense_f32_s128():
+    w = synth.workload("dense_f32_s128")
+    o, lse = fa.fa_fwd(*gpu(w["q"], w["k"], w["v"]), scale=w["scale"])
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_dense(w["q"], w["k"], w["v"], scale=f32(w["scale"]))
+    o_abs, _ = oracle.attn_dense(w["q"], w["k"], w["v"].abs(), scale=f32(w["scale"]))
+    check("full_dense_f32_s128", o, lse, o_ref, lse_ref, torch.float32, o_abs)
+
+
+def test_full_causal_bf16_s4096():
+    _full_dense("causal_bf16_s4096", 384)
+
+
+def test_full_causal_bf16_s8192():
+    _full_dense("causal_bf16_s8192", 256)
+
+
+def test_full_gqa_mask_f16_s8192():
+    _full_dense("gqa_mask_f16_s8192", 256)
