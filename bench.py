@@ -186,6 +186,9 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time the GQA+mask and block-sparse workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the benchmark, run --steps plain device copies of this many "
+                         "bytes (the reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -196,6 +199,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_bytes:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        wall, kern = time_calls(lambda: dst.copy_(src), args.steps, args.warmup)
+        print(json.dumps({"copy_bytes": args.copy_bytes, "kernel_ms": kern,
+                          "gbs_read_plus_write": 2 * args.copy_bytes / (kern * 1e-3) / 1e9}))
+        return
 
     import synth
     import flashattention_online_softmax_amd as fa
