@@ -10,7 +10,9 @@
 // Work decomposition (MI355X): one workgroup of NW waves owns MPH consecutive
 // query rows of HP query heads that share one KV head (HP > 1 packs GQA heads
 // so that a single K/V tile in LDS serves them all). Every wave owns QT tiles
-// of 32 query rows. Workgroups are numbered so that the longest causal tiles
+// of 32 query rows. With 8 waves of 32 rows a wave needs < 256 registers, so
+// two waves share each SIMD and one wave's softmax (VALU) overlaps the
+// other's MFMA work. Workgroups are numbered so that the longest causal tiles
 // start first and every KV head maps to one XCD (consecutive workgroup ids go
 // to consecutive XCDs and the KV-head index is the fastest-varying part).
 //
@@ -141,7 +143,7 @@ __device__ __forceinline__ int dense_tiles(const Work& wk, int mph, int bn) {
 // 16-bit kernel (fp16 / bf16), D in {64, 128}.
 // ---------------------------------------------------------------------------
 template <class T, int D, int QT, int NW, int HP, bool CAUSAL, bool MASK, bool SPARSE>
-__global__ void __launch_bounds__(NW * 64) fwd16_kernel(const FwdParams p) {
+__global__ void __launch_bounds__(NW * 64, NW / 4) fwd16_kernel(const FwdParams p) {
   constexpr int WPH = NW / HP;
   constexpr int MPH = WPH * QT * 32;
   constexpr int DS = D / 16;  // MFMA k-steps over D for S^T
@@ -349,10 +351,14 @@ __global__ void __launch_bounds__(NW * 64) fwd16_kernel(const FwdParams p) {
           rs += e;
         }
       l_run[t] = l_run[t] * alpha + rs;
+      // alpha is exactly 1 for a row whose max did not move: skip the
+      // rescale when that holds for every row of the wave.
+      if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[t][dt][i] *= alpha;
+          for (int i = 0; i < 16; ++i) oacc[t][dt][i] *= alpha;
+      }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int kt = ks >> 1, j = ks & 1;
@@ -571,7 +577,7 @@ void set_grid(FwdParams& p, dim3& grid) {
 
 template <class T, int D, bool CAUSAL, bool MASK>
 hipError_t launch16_dense(FwdParams& p, hipStream_t st) {
-  constexpr int NW = 4, QT = 2, HP = 1;
+  constexpr int NW = 8, QT = 1, HP = 1;
   dim3 grid;
   set_grid<NW, QT, HP>(p, grid);
   hipLaunchKernelGGL((fwd16_kernel<T, D, QT, NW, HP, CAUSAL, MASK, false>), grid, dim3(NW * 64), 0, st, p);
@@ -580,14 +586,15 @@ hipError_t launch16_dense(FwdParams& p, hipStream_t st) {
 
 template <class T, int D>
 hipError_t launch16_sparse(FwdParams& p, hipStream_t st) {
-  constexpr int NW = 4;
+  // 128 query rows per head (one query block); with an even GQA group two
+  // heads of the group share each K/V tile.
   dim3 grid;
   if (p.G % 2 == 0) {
-    set_grid<NW, 2, 2>(p, grid);
-    hipLaunchKernelGGL((fwd16_kernel<T, D, 2, NW, 2, false, false, true>), grid, dim3(NW * 64), 0, st, p);
+    set_grid<8, 1, 2>(p, grid);
+    hipLaunchKernelGGL((fwd16_kernel<T, D, 1, 8, 2, false, false, true>), grid, dim3(512), 0, st, p);
   } else {
-    set_grid<NW, 1, 1>(p, grid);
-    hipLaunchKernelGGL((fwd16_kernel<T, D, 1, NW, 1, false, false, true>), grid, dim3(NW * 64), 0, st, p);
+    set_grid<4, 1, 1>(p, grid);
+    hipLaunchKernelGGL((fwd16_kernel<T, D, 1, 4, 1, false, false, true>), grid, dim3(256), 0, st, p);
   }
   return hipGetLastError();
 }
