@@ -34,6 +34,13 @@ def build(verbose: bool = False) -> str:
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stderr)
+    # A kernel template whose host-side instantiation is silently rejected
+    # leaves its launch stub undefined; catch that here rather than at load.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("undefined kernel launch stubs in libfa.so:\n  " + "\n  ".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -35,6 +35,11 @@ struct F16 {
     f32x2 v = {x, y};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
   }
+  // acc + the two packed values (v_dot2c_f32_f16 against (1, 1)).
+  static __device__ __forceinline__ float sum2(uint32_t packed, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), one, acc, false);
+  }
 };
 
 struct BF16 {
@@ -46,6 +51,11 @@ struct BF16 {
   static __device__ __forceinline__ uint32_t pack2(float x, float y) {
     f32x2 v = {x, y};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+  // acc + the two packed values (v_dot2c_f32_bf16 against (1, 1)).
+  static __device__ __forceinline__ float sum2(uint32_t packed, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
   }
 };
 
@@ -63,9 +73,31 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// max(a, b, c) in one instruction. The operands are never NaN here (finite
+// scores or -inf), so the IEEE quieting that fmaxf chains otherwise pay for
+// with extra canonicalising instructions is not needed.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr float kLn2 = 0.69314718055994531f;
+
+// LDS pointer from a byte address. The mask (LDS is below 256 KB) tells the
+// compiler the address is non-negative, which lets it fold constant offsets
+// into the instructions' immediate offset field.
+__device__ __forceinline__ const lds_u16* lds_ptr(uint32_t byte_addr) {
+  return (const lds_u16*)(size_t)(byte_addr & 0x3FFFFu);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16) from an LDS pointer.
+__device__ __forceinline__ u32x2 lds_read_tr16(const lds_u16* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
 
 // Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
 // every lane reads 4 consecutive 16-bit elements at its own address; result
