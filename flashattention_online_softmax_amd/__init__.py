@@ -7,8 +7,10 @@ Work is enqueued on torch's current stream. There is no CPU path: without the
 built library or on a CPU tensor these functions raise.
 
 Functions (same names as the C entry points):
-  fa_fwd(q, k, v, scale=..., causal=False, mask=None, seqlens_q=None, seqlens_k=None)
-  fa_fwd_blocksparse(q, k, v, block_idx, scale=..., block_q=128, block_k=128, seqlens=None)
+  fa_fwd(q, k, v, scale=..., causal=False, mask=None, seqlens_q=None, seqlens_k=None,
+         rescale_threshold=8.0)
+  fa_fwd_blocksparse(q, k, v, block_idx, scale=..., block_q=128, block_k=128, seqlens=None,
+                     rescale_threshold=8.0)
   fa_fwd_topk_gather(q, k, v, idx, scale=...)
 each returning (o, lse).
 """
@@ -57,9 +59,10 @@ def load():
                           "%s is missing; build it with flashattention_online_softmax_amd.build" % LIB_PATH)
         lib = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER(FaTensor)
-        lib.fa_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P, P, ctypes.c_void_p]
+        lib.fa_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_int, ctypes.c_float, ctypes.c_float, P, P,
+                               ctypes.c_void_p]
         lib.fa_fwd_blocksparse.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_float,
-                                           P, P, ctypes.c_void_p]
+                                           ctypes.c_float, P, P, ctypes.c_void_p]
         lib.fa_fwd_topk_gather.argtypes = [P, P, P, P, ctypes.c_float, P, P, ctypes.c_void_p]
         for f in (lib.fa_fwd, lib.fa_fwd_blocksparse, lib.fa_fwd_topk_gather):
             f.restype = ctypes.c_int
@@ -110,10 +113,17 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def fa_fwd(q, k, v, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k=None, out=None,
-           lse=None, stream=None):
+# Rescale threshold (log2 units) of the dense and block-sparse entry points when
+# none is given: the lazy default of the flash-attention forward described on the
+# sparse-MLA page (threshold-branch section). 0 selects the exact running max.
+DEFAULT_RESCALE_THRESHOLD = 8.0
+
+
+def fa_fwd(q, k, v, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k=None,
+           rescale_threshold=DEFAULT_RESCALE_THRESHOLD, out=None, lse=None, stream=None):
     """Dense/causal/masked/GQA attention forward. q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D];
-    mask uint8/bool [Sq,Skv] or [B|1,Hq|1,Sq,Skv] (nonzero = excluded)."""
+    mask uint8/bool [Sq,Skv] or [B|1,Hq|1,Sq,Skv] (nonzero = excluded);
+    rescale_threshold in [0, 10] (0 = exact running max)."""
     lib = load()
     _need_gpu(q, k, v, mask, seqlens_q, seqlens_k)
     B, Hq, Sq, _ = q.shape
@@ -125,12 +135,13 @@ def fa_fwd(q, k, v, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k
         mask = mask.view(torch.uint8)
     _check(lib.fa_fwd(_ref(describe(q)), _ref(describe(k)), _ref(describe(v)), _ref(describe(mask)),
                       _ref(describe(seqlens_q)), _ref(describe(seqlens_k)), int(bool(causal)),
-                      float(scale), _ref(describe(out)), _ref(describe(lse)), _stream(stream)))
+                      float(scale), float(rescale_threshold), _ref(describe(out)), _ref(describe(lse)),
+                      _stream(stream)))
     return out, lse
 
 
 def fa_fwd_blocksparse(q, k, v, block_idx, *, scale, block_q=128, block_k=128, seqlens=None,
-                       out=None, lse=None, stream=None):
+                       rescale_threshold=DEFAULT_RESCALE_THRESHOLD, out=None, lse=None, stream=None):
     """Block-sparse attention forward; block_idx int32 [nQB, maxSel] or
     [B|1, Hkv|1, nQB, maxSel], negative = unused slot."""
     lib = load()
@@ -142,8 +153,8 @@ def fa_fwd_blocksparse(q, k, v, block_idx, *, scale, block_q=128, block_k=128, s
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     _check(lib.fa_fwd_blocksparse(_ref(describe(q)), _ref(describe(k)), _ref(describe(v)),
                                   _ref(describe(block_idx)), int(block_q), int(block_k),
-                                  _ref(describe(seqlens)), float(scale), _ref(describe(out)),
-                                  _ref(describe(lse)), _stream(stream)))
+                                  _ref(describe(seqlens)), float(scale), float(rescale_threshold),
+                                  _ref(describe(out)), _ref(describe(lse)), _stream(stream)))
     return out, lse
 
 

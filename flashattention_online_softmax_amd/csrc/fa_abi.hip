@@ -117,8 +117,12 @@ bool scale_ok(float scale) {
 }
 
 // Shared validation of q/k/v/o/lse for the BNSD entry points.
+// Largest rescale threshold accepted (log2 units): p stays <= 2^10, far
+// inside the fp16 range.
+constexpr float kMaxRescaleThreshold = 10.f;
+
 fa_status check_bnsd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* o,
-                     const fa_tensor* lse, float scale) {
+                     const fa_tensor* lse, float scale, float rescale_threshold) {
   fa_status s;
   if ((s = check_tensor("q", q, 4, true)) != FA_OK) return s;
   if ((s = check_tensor("k", k, 4, true)) != FA_OK) return s;
@@ -145,15 +149,20 @@ fa_status check_bnsd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
   if (Hkv == 0 && B * Hq * Sq > 0) return fail(FA_ERR_SHAPE, "k has no heads");
   if (Hkv > 0 && Hq % Hkv != 0) return fail(FA_ERR_SHAPE, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
   if (!scale_ok(scale)) return fail(FA_ERR_VALUE, "scale must be finite and > 0");
+  if (!(rescale_threshold >= 0.f && rescale_threshold <= kMaxRescaleThreshold))
+    return fail(FA_ERR_VALUE, "rescale_threshold must be in [0, %g]", (double)kMaxRescaleThreshold);
   if (D != Dv) return fail(FA_ERR_UNSUPPORTED, "D (%lld) != Dv (%lld) is not supported", (long long)D, (long long)Dv);
   if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %lld not supported (64 or 128)", (long long)D);
   if (!fits_i32(B * Hq * Sq) || !fits_i32(Skv) || !fits_i32(B * Hq))
     return fail(FA_ERR_UNSUPPORTED, "problem too large for 32-bit row indexing");
+  // K/V tiles are fetched with 32-bit per-lane offsets from the tile start.
+  if (k->stride[2] > (1 << 22) || v->stride[2] > (1 << 22))
+    return fail(FA_ERR_UNSUPPORTED, "k/v row stride above 2^22 elements is not supported");
   return FA_OK;
 }
 
 void fill_common(fa::FwdParams& p, const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
-                 const fa_tensor* o, const fa_tensor* lse, float scale) {
+                 const fa_tensor* o, const fa_tensor* lse, float scale, float rescale_threshold) {
   memset(&p, 0, sizeof(p));
   p.q = q->data;
   p.k = k->data;
@@ -172,6 +181,7 @@ void fill_common(fa::FwdParams& p, const fa_tensor* q, const fa_tensor* k, const
   p.G = p.Hkv > 0 ? p.Hq / p.Hkv : 1;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.rescale_thr = rescale_threshold;
 }
 
 fa::Dt to_dt(int32_t d) { return d == FA_F32 ? fa::Dt::F32 : d == FA_F16 ? fa::Dt::F16 : fa::Dt::BF16; }
@@ -182,16 +192,16 @@ extern "C" {
 
 fa_status fa_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* mask,
                  const fa_tensor* seqlens_q, const fa_tensor* seqlens_k, int causal, float scale,
-                 const fa_tensor* o, const fa_tensor* lse, void* stream) {
+                 float rescale_threshold, const fa_tensor* o, const fa_tensor* lse, void* stream) {
   clear_error();
-  fa_status s = check_bnsd(q, k, v, o, lse, scale);
+  fa_status s = check_bnsd(q, k, v, o, lse, scale, rescale_threshold);
   if (s != FA_OK) return s;
   if (causal != 0 && causal != 1) return fail(FA_ERR_VALUE, "causal must be 0 or 1");
   const int64_t B = q->shape[0], Hq = q->shape[1], Sq = q->shape[2], Skv = k->shape[2];
   if ((s = check_seqlens("seqlens_q", seqlens_q, B)) != FA_OK) return s;
   if ((s = check_seqlens("seqlens_k", seqlens_k, B)) != FA_OK) return s;
   fa::FwdParams p;
-  fill_common(p, q, k, v, o, lse, scale);
+  fill_common(p, q, k, v, o, lse, scale, rescale_threshold);
   if (mask) {
     if (mask->ndim != 2 && mask->ndim != 4) return fail(FA_ERR_SHAPE, "mask must have rank 2 or 4");
     if ((s = check_tensor("mask", mask, mask->ndim, false)) != FA_OK) return s;
@@ -224,10 +234,10 @@ fa_status fa_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
 
 fa_status fa_fwd_blocksparse(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
                              const fa_tensor* block_idx, int block_q, int block_k,
-                             const fa_tensor* seqlens, float scale, const fa_tensor* o,
-                             const fa_tensor* lse, void* stream) {
+                             const fa_tensor* seqlens, float scale, float rescale_threshold,
+                             const fa_tensor* o, const fa_tensor* lse, void* stream) {
   clear_error();
-  fa_status s = check_bnsd(q, k, v, o, lse, scale);
+  fa_status s = check_bnsd(q, k, v, o, lse, scale, rescale_threshold);
   if (s != FA_OK) return s;
   if (block_q != 128 || block_k != 128)
     return fail(FA_ERR_UNSUPPORTED, "block_q and block_k must be 128 (got %d, %d)", block_q, block_k);
@@ -238,7 +248,7 @@ fa_status fa_fwd_blocksparse(const fa_tensor* q, const fa_tensor* k, const fa_te
   if ((s = check_tensor("block_idx", block_idx, block_idx->ndim, false)) != FA_OK) return s;
   if ((s = check_dtype("block_idx", block_idx, FA_I32)) != FA_OK) return s;
   fa::FwdParams p;
-  fill_common(p, q, k, v, o, lse, scale);
+  fill_common(p, q, k, v, o, lse, scale, rescale_threshold);
   const int nd = block_idx->ndim;
   const int64_t nqb = block_idx->shape[nd - 2], max_sel = block_idx->shape[nd - 1];
   if (nqb < (Sq + block_q - 1) / block_q) return fail(FA_ERR_SHAPE, "block_idx has %lld query blocks, need %lld", (long long)nqb, (long long)((Sq + block_q - 1) / block_q));
@@ -326,6 +336,6 @@ const char* fa_status_str(fa_status s) {
 
 const char* fa_last_error(void) { return g_err; }
 
-int fa_version(void) { return 100; }
+int fa_version(void) { return 200; }
 
 }  // extern "C"

@@ -1,0 +1,652 @@
+// 16-bit (fp16 / bf16) attention forward kernels for gfx950, D in {64, 128}:
+// dense, causal, boolean-masked, GQA and block-sparse.
+//
+// Method: the online-softmax forward of the "FlashAttention correctness
+// verification" page (tiled computation and loop-invariant sections): per KV
+// tile S = scale * Q K^T, a running row max m, l' = l e^(m - m') + rowsum
+// e^(S - m'), O' = O e^(m - m') + e^(S - m') V, and finally O = O / l and
+// LSE = m + ln l. The running max is moved with a rescale threshold in log2
+// units (0 = exact running max; the lazy rescale of the flash-attention
+// sparse-MLA page, threshold-branch section, for t > 0).
+//
+// This file is compiled on its own into a gfx950 code object (see build.py:
+// the kernels need most of the register file as VGPRs next to 64 AGPRs, a
+// split the code object gets through its amdgpu-agpr-alloc attribute) and is
+// loaded by the library at run time. Kernels are extern "C" with names of the
+// form fa_fwd16_<dtype>_d<D>_w<waves>_h<heads>_c<causal>m<mask>s<sparse>.
+//
+// Work decomposition (MI355X): one workgroup of NW waves owns MPH consecutive
+// query rows of HP query heads that share one KV head (HP > 1 packs GQA heads
+// so that one K/V tile in LDS serves them all); every wave owns 32 query
+// rows. With 8 waves two share each SIMD. Workgroups are numbered so that the
+// longest causal row blocks start first and every KV head maps to one XCD.
+//
+// Per 64-key tile and wave:
+//   * K and V tiles are copied HBM -> LDS by global_load_lds_dwordx4 (no
+//     register staging) into three-deep rings, with an XOR swizzle of the
+//     16-byte chunks so that the MFMA operand reads hit distinct LDS banks.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16 (K from LDS as the A operand, Q^T
+//     resident in VGPRs as the B operand). Each lane owns one query column
+//     and 16 keys of it, so the row max and row sum are in-lane reductions
+//     plus one v_permlane32_swap between the wave halves.
+//   * p = exp2(s * scale*log2e - m) (one FMA + one v_exp_f32 per score), m
+//     being the reference max already in the exp2 domain; l accumulates the
+//     fp32 p; p is rounded to 16 bits into the B operand of the next MFMA.
+//   * O^T += V^T P^T on MFMA with the accumulators in AGPRs: V^T is read from
+//     the row-major V tile with ds_read_b64_tr_b16, in the key order in which
+//     the S^T accumulator holds P. A rescale is a per-lane multiply.
+// Epilogue: O = acc / l rounded to the output dtype, LSE = ln2 * (m + log2 l)
+// in fp32; rows with no key give O = 0 and LSE = -inf.
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_internal.h"
+#include "fa_tiles.h"
+
+namespace fa {
+namespace {
+
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane i fills LDS bytes [lds_addr + 16 i, +16).
+// Issued through inline assembly so that the compiler does not hold later
+// LDS reads of other buffers behind it; the kernel itself waits for these
+// copies (s_waitcnt vmcnt) before the barrier that publishes their data.
+__device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(gbase)
+      : "memory", "m0");
+}
+
+// A pointer whose value is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Waits until at most N vector-memory operations of this wave are in flight
+// (they retire in issue order for this counter).
+template <int N>
+__device__ __forceinline__ void wait_vmem_below() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that does not drain in-flight LDS copies (a full
+// __syncthreads fence would). Each wave first waits for its own LDS
+// operations; a wave that issued copies others read must wait for them
+// itself before it reaches the barrier.
+__device__ __forceinline__ void barrier_keep_copies() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Copies of 64-key tiles (rows kstart .. kstart+63 of one K or V head) into
+// LDS buffers of 64 rows x D elements stored with the 16-byte chunk swizzle.
+// One copy instruction fills 64 consecutive chunks (1 KB) of LDS, lane i
+// chunk 64n + i, so each lane fetches the logical chunk the swizzle keeps at
+// that position (the XOR is an involution). The per-lane byte offset inside a
+// tile is the same for every tile and is computed once. On the last, partial
+// tile, rows at or past Lk fetch row Lk - 1 instead (finite data whose scores
+// are masked), so nothing past the valid keys is ever read.
+template <int D, int NW, bool IS_V>
+struct TileCopy {
+  static constexpr int CH = D / 8;
+  static constexpr int NINST = BN * CH / 64;
+  static constexpr int PER_WAVE = NINST / NW;
+  static_assert(NINST % NW == 0, "tile copy must divide evenly over the waves");
+  const char* g;       // head base
+  uint32_t row_bytes;  // row stride in bytes (the library keeps it below 2^24)
+  uint32_t off[PER_WAVE];
+
+  __device__ __forceinline__ static int pos(int j) {
+    return (((int)threadIdx.x >> 6) * PER_WAVE + j) * 64 + ((int)threadIdx.x & 63);
+  }
+  __device__ __forceinline__ static int chunk_row(int j) { return pos(j) / CH; }
+  __device__ __forceinline__ static uint32_t chunk_col_bytes(int j) {
+    const int row = pos(j) / CH, ph = pos(j) % CH;
+    return (uint32_t)((ph ^ (IS_V ? vswz<D>(row) : kswz<D>(row))) * 16);
+  }
+
+  // head is the same in every lane of the wave.
+  __device__ __forceinline__ TileCopy(const uint16_t* head, int64_t row_stride)
+      : g(uniform_ptr(head)), row_bytes((uint32_t)row_stride * 2u) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) off[j] = (uint32_t)chunk_row(j) * row_bytes + chunk_col_bytes(j);
+  }
+
+  // kstart, Lk and lds are the same in every lane of the wave.
+  __device__ __forceinline__ void issue(int kstart, int Lk, const uint16_t* lds) const {
+    kstart = __builtin_amdgcn_readfirstlane(kstart);
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(
+        lds_addr_of(lds) + (((int)threadIdx.x >> 6) * PER_WAVE) * 1024);
+    const char* base = g + (int64_t)kstart * row_bytes;
+    if (kstart + BN <= Lk) {
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j) lds_copy16(base, off[j], l0 + j * 1024);
+    } else {
+      const int last = Lk - 1 - kstart;
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j) {
+        const int over = max(chunk_row(j) - last, 0);
+        lds_copy16(base, off[j] - (uint32_t)over * row_bytes, l0 + j * 1024);
+      }
+    }
+  }
+};
+
+// MFMA issued through inline assembly so that this code, not the compiler,
+// picks the register file of each accumulator: the S^T accumulators live in
+// VGPRs (the softmax reads them), the O^T accumulators in AGPRs (only MFMAs
+// touch them inside the loop). On gfx950 VALU instructions keep issuing while
+// an MFMA with AGPR accumulators runs, but stall behind MFMAs that
+// accumulate in VGPRs.
+// Hazards the compiler cannot see through the asm are covered explicitly:
+// VALU reads of an MFMA result wait mfma_result_wait() first; the VGPR
+// operands written by VALU code are always produced one loop step before the
+// MFMA that reads them.
+template <class T>
+struct Mma;
+template <>
+struct Mma<BF16> {
+  static __device__ __forceinline__ void v0(f32x16& d, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void v(f32x16& d, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void a(f32x16& d, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  }
+  // VGPR accumulator, B operand held in AGPRs. The B operand is declared
+  // read-write (the instruction does not change it) so that the compiler
+  // keeps it in AGPRs instead of copying it there before every use.
+  static __device__ __forceinline__ void v0b(f32x16& d, u32x4 a, u32x4& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %1, 0" : "=&v"(d), "+a"(b) : "v"(a));
+  }
+  static __device__ __forceinline__ void vb(f32x16& d, u32x4 a, u32x4& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %1, %0" : "+v"(d), "+a"(b) : "v"(a));
+  }
+};
+template <>
+struct Mma<F16> {
+  static __device__ __forceinline__ void v0(f32x16& d, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void v(f32x16& d, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void a(f32x16& d, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  }
+  // VGPR accumulator, B operand held in AGPRs. The B operand is declared
+  // read-write (the instruction does not change it) so that the compiler
+  // keeps it in AGPRs instead of copying it there before every use.
+  static __device__ __forceinline__ void v0b(f32x16& d, u32x4 a, u32x4& b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %2, %1, 0" : "=&v"(d), "+a"(b) : "v"(a));
+  }
+  static __device__ __forceinline__ void vb(f32x16& d, u32x4 a, u32x4& b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %2, %1, %0" : "+v"(d), "+a"(b) : "v"(a));
+  }
+};
+
+// Wait states between the last 32x32x16 MFMA writing a register and a VALU
+// instruction touching it (more than the 8-pass MFMA needs). The registers
+// are operands of the wait so that the compiler places every access to them
+// after it.
+__device__ __forceinline__ void mfma_wait_v(f32x16 (&a)[2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a[0]), "+v"(a[1]));
+}
+template <int N>
+__device__ __forceinline__ void mfma_wait_a(f32x16 (&a)[N]) {
+  static_assert(N == 2 || N == 4, "d tiles");
+  if constexpr (N == 4)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a[0]), "+a"(a[1]));
+}
+// Wait states between VALU writes of accumulator registers and the next
+// MFMA reading them; the writes are placed before it.
+template <int N>
+__device__ __forceinline__ void acc_written(f32x16 (&a)[N]) {
+  if constexpr (N == 4)
+    asm volatile("s_nop 4" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]));
+  else
+    asm volatile("s_nop 4" : "+a"(a[0]), "+a"(a[1]));
+}
+
+// One loop step j of a wave (64-key tiles; a wave owns QT blocks of 32 query
+// rows and reads every K/V operand once for all of them):
+//   softmax(j): mask, row max, reference max update, p = exp2(s c - m), row
+//               sum, p rounded into the P operand;
+//   S(j+1):     S^T = K_{j+1} Q^T into the other score buffer;
+//   PV(j-1):    O^T += V_{j-1}^T P_{j-1}^T.
+// softmax(j) and PV(j-1) are independent: their instructions are interleaved
+// (per V operand, QT P V MFMAs and a slice of the softmax VALU work), then
+// S(j+1) refills the score registers. Operands are read AHEAD ahead.
+// Every step runs the same code (no diamonds around the MFMAs): a step past
+// this wave's last tile does an inactive softmax (P = 0, m and l unchanged),
+// the P V of step 0 multiplies P = 0 with a zeroed V slot, and the S of the
+// last step reads a slot whose result goes unused.
+//
+// Running max with a rescale threshold t (log2 units): a row's reference max
+// moves only when the tile's max exceeds it by more than t; then O and l are
+// rescaled by exp2(m_old - m_new). t = 0 is the exact running max (every
+// growth rescales, the largest p of the row is exactly 1); t > 0 is the lazy
+// rescale, with p <= 2^t.
+//
+// K and V tiles live in three-deep LDS rings (tile t in slot t % 3). Step j
+// copies K_{j+3} into the slot of K_j (last read by S(j) in step j-1) and
+// V_{j+1} into the slot of V_{j-2} (last read by PV(j-2) in step j-1). A
+// step ends by waiting for the copies of the step before and a workgroup
+// barrier, so a tile copied in step j is visible from step j+2 on, when it is
+// first read.
+template <class T, int D, int NW, int QT, int HP, bool CAUSAL, bool MASK, bool SPARSE>
+__device__ __forceinline__ void fwd16_body(const FwdParams& p) {
+  constexpr int WPH = NW / HP;
+  constexpr int MPH = WPH * QT * 32;
+  constexpr int DS = D / 16;  // MFMA k-steps over D for S^T
+  constexpr int DT = D / 32;  // 32-wide d tiles of O^T
+  constexpr int NS = 2 * DS;  // K operands per tile (2 key halves x DS)
+  constexpr int NP = 4 * DT;  // V operands per tile (4 key steps x DT)
+  static_assert(NS == NP, "K and V operand counts agree (D / 8 each)");
+  constexpr int TILE = BN * D;
+  constexpr int AHEAD = 3;    // operand pairs read ahead
+  constexpr int RING = AHEAD + 1;
+  static_assert(!SPARSE || MPH == 128, "block-sparse needs 128 query rows per head");
+
+  __shared__ __attribute__((aligned(16))) uint16_t s_kring[3 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t s_vring[3 * TILE];
+  __shared__ int s_kstart[SPARSE ? 512 : 1];
+  __shared__ int s_n;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  const int c = lane & 31;
+  const Work wk = decode_work<NW, QT, HP>(p);
+  const int diag = wk.Lk - wk.Lq;  // key j is visible to row i iff j <= i + diag
+
+  int n_iter;
+  if (SPARSE)
+    n_iter = build_sparse_tiles(p, wk, wk.wg_row0 / 128, s_kstart, &s_n);
+  else
+    n_iter = dense_tiles<CAUSAL>(wk, MPH, BN);
+  // Tiles this wave works on: none if its rows are past Lq; under the causal
+  // mask only the tiles that start at or before its last visible key.
+  int n_act = n_iter;
+  if (wk.row0 >= wk.Lq) {
+    n_act = 0;
+  } else if (CAUSAL && !SPARSE) {
+    const int last_key = min(wk.row0 + QT * 32 - 1, wk.Lq - 1) + diag;
+    n_act = last_key < 0 ? 0 : min(n_iter, last_key / BN + 1);
+  }
+  n_act = __builtin_amdgcn_readfirstlane(n_act);
+
+  const uint16_t* qg = (const uint16_t*)p.q + wk.b * p.q_sb + wk.hq * p.q_sh;
+  const uint16_t* kg = (const uint16_t*)p.k + wk.b * p.k_sb + wk.hkv * p.k_sh;
+  const uint16_t* vg = (const uint16_t*)p.v + wk.b * p.v_sb + wk.hkv * p.v_sh;
+
+  // Q^T operands (B operand of S^T = K Q^T, kept in AGPRs): block b, lane
+  // holds Q[row0 + 32 b + c][16 ds + 8 h .. +7].
+  u32x4 qop[QT][DS];
+#pragma unroll
+  for (int b = 0; b < QT; ++b) {
+    const int qrow = wk.row0 + 32 * b + c;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (qrow < p.Sq) z = *(const u32x4*)(qg + (int64_t)qrow * p.q_ss + 16 * ds + 8 * h);
+      qop[b][ds] = z;
+    }
+  }
+
+  f32x16 oacc[QT][DT];
+#pragma unroll
+  for (int b = 0; b < QT; ++b)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[b][dt][i] = 0.f;
+#pragma unroll
+  for (int b = 0; b < QT; ++b) acc_written(oacc[b]);  // O^T lives in AGPRs from here on
+  float m_ref[QT], l_run[QT];
+  f32x16 sc[QT][2];      // [block][kt]: scores of the tile the next softmax works on
+  u32x4 pp[2][QT][4];    // [parity][block][k-step]: P operand of a tile
+#pragma unroll
+  for (int b = 0; b < QT; ++b) {
+    m_ref[b] = -INFINITY;
+    l_run[b] = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[b][kt][i] = 0.f;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) pp[par][b][ks] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  auto tile_start = [&](int it) __attribute__((always_inline)) { return SPARSE ? s_kstart[it] : it * BN; };
+
+  const TileCopy<D, NW, false> kcopy(kg, p.k_ss);
+  const TileCopy<D, NW, true> vcopy(vg, p.v_ss);
+  constexpr int NCOPY = TileCopy<D, NW, false>::PER_WAVE + TileCopy<D, NW, true>::PER_WAVE;
+
+  // Per-lane element offsets of the MFMA operands inside a tile.
+  // K operand r (A operand of S^T): key half kt = r & 1 (rows 32 kt + c),
+  // logical chunk 2 (r >> 1) + h.
+  int koff[DS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) koff[ds] = c * D + (((2 * ds + h) ^ kswz<D>(c)) << 3);
+  // V operand r (tr-read, see lds_read_tr16): key step ks = r / DT (keys
+  // 16 ks .. +15, lane rows vrow and vrow + 8), d tile dt = r % DT.
+  const int vrow = 4 * h + ((lane & 15) >> 2);
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int voff[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int col = 32 * dt + vcol;
+    voff[dt] = vrow * D + (((col >> 3) ^ vswz<D>(vrow)) << 3) + (col & 7);
+  }
+  auto kread = [&](const lds_u16* kb, int r) __attribute__((always_inline)) -> u32x4 {
+    return *(const __attribute__((address_space(3))) u32x4*)(kb + (r & 1) * 32 * D + koff[r >> 1]);
+  };
+  auto vread = [&](const lds_u16* const (&vb)[DT], int r) __attribute__((always_inline)) -> u32x4 {
+    const int dt = r % DT, ks = r / DT;
+    const int rb = ((ks >> 1) * 32 + (ks & 1) * 16) * D;  // vswz depends on row % 4 only
+    const u32x2 lo = lds_read_tr16(vb[dt] + rb);
+    const u32x2 hi = lds_read_tr16(vb[dt] + rb + 8 * D);
+    const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+    return v;
+  };
+
+  // Masking of tile j's scores of block b (causal diagonal, ragged edges,
+  // boolean mask).
+  auto mask_tile = [&](f32x16 (&sv)[2], int b, int j) __attribute__((always_inline)) {
+    const int kstart = tile_start(j);
+    const int brow0 = wk.row0 + 32 * b;
+    const int qrow = brow0 + c;
+    const bool edge = (kstart + BN > wk.Lk) || (brow0 + 32 > wk.Lq) ||
+                      (CAUSAL && kstart + BN - 1 > brow0 + diag);
+    if (!MASK && !edge) return;
+    uint32_t mbits[2][4];
+    if (MASK) {
+      const uint8_t* mrow = p.mask + wk.b * p.m_sb + wk.hq * p.m_sh + (int64_t)qrow * p.m_ss;
+      // 4 consecutive mask bytes per (kt, g).
+      const bool vec = p.mask_vec4 && (kstart + BN <= p.Skv);
+      const bool rv = qrow < p.Sq;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int key0 = kstart + kt * 32 + 8 * g + 4 * h;
+          uint32_t bits = 0x01010101u;
+          if (rv) {
+            if (vec) {
+              bits = *(const uint32_t*)(mrow + key0);
+            } else {
+              bits = 0;
+              for (int e = 0; e < 4; ++e)
+                bits |= (uint32_t)((key0 + e < p.Skv) ? mrow[key0 + e] : 1) << (8 * e);
+            }
+          }
+          mbits[kt][g] = bits;
+        }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kstart + kt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+        bool ok = key < wk.Lk && qrow < wk.Lq;
+        if (CAUSAL) ok = ok && key <= qrow + diag;
+        if (MASK) ok = ok && ((mbits[kt][i >> 2] >> (8 * (i & 3))) & 0xffu) == 0u;
+        if (!ok) sv[kt][i] = -INFINITY;
+      }
+  };
+
+  // Softmax state of the step being processed, per block.
+  float mq[QT], mc[QT], alpha[QT], rs0[QT], rs1[QT];
+  bool upd_any = false;
+  // Quarter part (0..3) of block b's row max (three-input maxima).
+  auto row_max_4 = [&](const f32x16 (&sv)[2], int b, int part) __attribute__((always_inline)) {
+    const int kt = part >> 1, i0 = (part & 1) * 8;
+    const float t = max3(sv[kt][i0], sv[kt][i0 + 1], sv[kt][i0 + 2]);
+    const float u = max3(t, sv[kt][i0 + 3], sv[kt][i0 + 4]);
+    const float v = max3(u, sv[kt][i0 + 5], sv[kt][i0 + 6]);
+    mq[b] = part == 0 ? fmaxf(v, sv[kt][i0 + 7]) : max3(mq[b], v, sv[kt][i0 + 7]);
+    asm volatile("" ::"v"(mq[b]));
+  };
+  // Reference-max update of block b. An inactive step (no tile of this wave)
+  // leaves m alone; below n_iter its scores come from real K rows, are finite,
+  // and give P = 0 for the P V of the next step; the last step's P is never
+  // used.
+  auto max_update = [&](int b, bool act) __attribute__((always_inline)) {
+    const float mx = half_max(mq[b]) * p.scale_log2;
+    const bool upd = act && mx > m_ref[b] + p.rescale_thr;
+    const float m_new = upd ? mx : m_ref[b];
+    alpha[b] = upd ? fast_exp2(m_ref[b] - m_new) : 1.f;
+    upd_any = upd_any || upd;
+    m_ref[b] = m_new;
+    mc[b] = !act ? INFINITY : (m_new == -INFINITY ? 0.f : m_new);
+    rs0[b] = 0.f;
+    rs1[b] = 0.f;
+  };
+  // Exponentials of block b's scores e, e+1 (e even) into its P operand.
+  auto exp_pair = [&](const f32x16 (&sv)[2], u32x4 (&pop)[4], int b, int e) __attribute__((always_inline)) {
+    const int kt = e >> 4, ii = e & 15;
+    const float x0 = fast_exp2(__builtin_fmaf(sv[kt][ii], p.scale_log2, -mc[b]));
+    const float x1 = fast_exp2(__builtin_fmaf(sv[kt][ii + 1], p.scale_log2, -mc[b]));
+    pop[e >> 3][(e & 7) >> 1] = T::pack2(x0, x1);
+    if ((e >> 1) & 1)
+      rs1[b] += x0 + x1;
+    else
+      rs0[b] += x0 + x1;
+    // Pin the results here: otherwise the compiler sinks the exponentials
+    // below the MFMAs they are meant to overlap.
+    asm volatile("" ::"v"(pop[e >> 3][(e & 7) >> 1]), "v"(rs0[b]), "v"(rs1[b]));
+  };
+  // Softmax slice s of a step (0 .. 21 QT - 1): block maxima, updates, then
+  // exponential pairs alternating between blocks.
+  constexpr int NSLICE = 21 * QT;
+  auto slice = [&](f32x16 (&sv)[QT][2], u32x4 (&pop)[QT][4], int s, bool act) __attribute__((always_inline)) {
+    if (s < 4 * QT) {
+      row_max_4(sv[s / 4], s / 4, s % 4);
+    } else if (s < 5 * QT) {
+      max_update(s - 4 * QT, act);
+    } else {
+      const int t = s - 5 * QT;  // 0 .. 16 QT - 1
+      const int b = t % QT, e = 2 * (t / QT);
+      exp_pair(sv[b], pop[b], b, e);
+    }
+  };
+
+  // S = K Q^T of the tile in kt_buf into sn, K operands read AHEAD ahead.
+  auto scores = [&](f32x16 (&sn)[QT][2], const uint16_t* kt_buf) __attribute__((always_inline)) {
+    const lds_u16* kb = lds_ptr(lds_addr_of(kt_buf));
+    u32x4 kq[RING];
+#pragma unroll
+    for (int r = 0; r < AHEAD; ++r) kq[r] = kread(kb, r);
+#pragma unroll
+    for (int r = 0; r < NS; ++r) {
+      if (r + AHEAD < NS) kq[(r + AHEAD) % RING] = kread(kb, r + AHEAD);
+#pragma unroll
+      for (int b = 0; b < QT; ++b) {
+        // key half r & 1, k-step r >> 1
+        if (r < 2)
+          Mma<T>::v0b(sn[b][r & 1], kq[r % RING], qop[b][r >> 1]);
+        else
+          Mma<T>::vb(sn[b][r & 1], kq[r % RING], qop[b][r >> 1]);
+      }
+    }
+    // Results complete before the compiler may touch the registers again.
+#pragma unroll
+    for (int b = 0; b < QT; ++b) mfma_wait_v(sn[b]);
+  };
+
+  // softmax(j) on sv into pop, interleaved V operand by V operand with
+  // PV(j-1) (pprev, V tile in vt_buf), whose MFMAs accumulate in AGPRs and so
+  // leave the VALU free.
+  auto softmax_pv = [&](f32x16 (&sv)[QT][2], u32x4 (&pop)[QT][4], const u32x4 (&pprev)[QT][4],
+                        const uint16_t* vt_buf, bool act, bool o_live) __attribute__((always_inline)) {
+    const lds_u16* vb[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vb[dt] = lds_ptr(lds_addr_of(vt_buf) + 2 * voff[dt]);
+    u32x4 vq[RING];
+#pragma unroll
+    for (int r = 0; r < AHEAD; ++r) vq[r] = vread(vb, r);
+    upd_any = false;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < NP; ++r) {
+      if (r + AHEAD < NP) vq[(r + AHEAD) % RING] = vread(vb, r + AHEAD);
+      // d tile r % DT, key step r / DT
+#pragma unroll
+      for (int b = 0; b < QT; ++b) Mma<T>::a(oacc[b][r % DT], vq[r % RING], pprev[b][r / DT]);
+#pragma unroll
+      for (int s = (NSLICE * r) / NP; s < (NSLICE * (r + 1)) / NP; ++s) slice(sv, pop, s, act);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Rescale of O and l when a reference max moved (O is only ever touched
+    // by MFMAs otherwise). An inactive step's row sum is dropped, not
+    // multiplied by zero: its scores may be anything.
+    if (o_live && __builtin_amdgcn_ballot_w64(upd_any) != 0) {
+#pragma unroll
+      for (int b = 0; b < QT; ++b) {
+        mfma_wait_a(oacc[b]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[b][dt][i] *= alpha[b];
+        acc_written(oacc[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < QT; ++b) l_run[b] = act ? __builtin_fmaf(l_run[b], alpha[b], rs0[b] + rs1[b]) : l_run[b];
+  };
+
+  // Prologue. V slot 2 is read by the PV(-1) of step 0 (with P = 0), so it
+  // must hold finite values: zero it. Then K_0, K_1, K_2 and V_0 in flight.
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    uint16_t* v2 = s_vring + 2 * TILE;
+    for (int i = tid * 8; i < TILE; i += NW * 64 * 8) *(u32x4*)&v2[i] = z;
+  }
+  __syncthreads();
+  if (n_iter > 0) {
+    kcopy.issue(tile_start(0), wk.Lk, s_kring);
+    vcopy.issue(tile_start(0), wk.Lk, s_vring);
+  }
+  if (n_iter > 1) kcopy.issue(tile_start(1), wk.Lk, s_kring + TILE);
+  if (n_iter > 2) kcopy.issue(tile_start(2), wk.Lk, s_kring + 2 * TILE);
+  // Make the compiler wait for the Q loads here, once: it does not see the
+  // copies above, and otherwise would wait for its Q loads (vmcnt(0), which
+  // drains copies in flight) at their first use inside the loop.
+#pragma unroll
+  for (int b = 0; b < QT; ++b)
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) asm volatile("s_nop 4" : "+a"(qop[b][ds]));
+  wait_vmem();
+  __syncthreads();
+  // S(0).
+  scores(sc, s_kring);
+  // Nobody may overwrite K_0's slot (step 0 copies K_3 there) before every
+  // wave has read it.
+  barrier_keep_copies();
+
+  // One loop step; PAR = j & 1 selects the buffers.
+  auto step = [&](auto par_tag, int j) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par_tag)::value;
+    bool copied = false;
+    if (j + 3 < n_iter) {
+      kcopy.issue(tile_start(j + 3), wk.Lk, s_kring + (j % 3) * TILE);
+      copied = true;
+    }
+    if (j + 1 < n_iter) {
+      vcopy.issue(tile_start(j + 1), wk.Lk, s_vring + ((j + 1) % 3) * TILE);
+      copied = true;
+    }
+    const bool act = j < n_act;
+    if (act) {
+#pragma unroll
+      for (int b = 0; b < QT; ++b) mask_tile(sc[b], b, j);
+    }
+    softmax_pv(sc, pp[PAR], pp[PAR ^ 1], s_vring + ((j + 2) % 3) * TILE, act, j > 0);
+    // S(j+1) reuses the score registers (the softmax above consumed them).
+    // In the last step there is no tile j+1 and the result goes unused; the
+    // slot read is in bounds either way.
+    scores(sc, s_kring + ((j + 1) % 3) * TILE);
+    if (copied)
+      wait_vmem_below<NCOPY>();
+    else
+      wait_vmem();
+    barrier_keep_copies();
+  };
+  for (int j = 0; j <= n_iter; j += 2) {
+    step(std::integral_constant<int, 0>(), j);
+    if (j + 1 > n_iter) break;
+    step(std::integral_constant<int, 1>(), j + 1);
+  }
+
+  // Epilogue.
+  uint16_t* og = (uint16_t*)p.o + wk.b * p.o_sb + wk.hq * p.o_sh;
+#pragma unroll
+  for (int b = 0; b < QT; ++b) {
+    mfma_wait_a(oacc[b]);
+    const int qrow = wk.row0 + 32 * b + c;
+    const float lt = half_sum(l_run[b]);
+    if (qrow < p.Sq) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      uint16_t* orow = og + (int64_t)qrow * p.o_ss;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 v;
+          v[0] = T::pack2(oacc[b][dt][4 * g] * inv, oacc[b][dt][4 * g + 1] * inv);
+          v[1] = T::pack2(oacc[b][dt][4 * g + 2] * inv, oacc[b][dt][4 * g + 3] * inv);
+          *(u32x2*)(orow + 32 * dt + 8 * g + 4 * h) = v;
+        }
+      if (h == 0)
+        p.lse[((int64_t)wk.b * p.Hq + wk.hq) * p.Sq + qrow] =
+            lt > 0.f ? (m_ref[b] + log2f(lt)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace fa
+
+// Kernel entry points (names are looked up by the library at run time):
+// fa_fwd16_<dtype>_d<D>_w<waves>_q<32-row blocks per wave>_h<heads>_c<causal>m<mask>s<sparse>.
+#define FA_FWD16_KERNEL(TN, T, D, NW, QT, HP, C, M, S)                                            \
+  extern "C" __global__ void __launch_bounds__(NW * 64, 1)                                          \
+      fa_fwd16_##TN##_d##D##_w##NW##_q##QT##_h##HP##_c##C##m##M##s##S(const fa::FwdParams p) {     \
+    fa::fwd16_body<fa::T, D, NW, QT, HP, C != 0, M != 0, S != 0>(p);                                \
+  }
+#define FA_FWD16_DTYPE_D(TN, T, D)                 \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 0, 0, 0)      \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 0, 1, 0)      \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 1, 0, 0)      \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 1, 1, 0)      \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 2, 0, 0, 1)      \
+  FA_FWD16_KERNEL(TN, T, D, 4, 1, 1, 0, 0, 1)
+
+FA_FWD16_DTYPE_D(f16, F16, 64)
+FA_FWD16_DTYPE_D(f16, F16, 128)
+FA_FWD16_DTYPE_D(bf16, BF16, 64)
+FA_FWD16_DTYPE_D(bf16, BF16, 128)

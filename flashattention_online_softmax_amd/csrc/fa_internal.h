@@ -33,6 +33,7 @@ struct FwdParams {
   int32_t n_hgroups;       // head groups per KV head (G / heads per workgroup)
   float scale;             // softmax scale (LSE is reported in these units)
   float scale_log2;        // scale * log2(e): scores enter exp2 through one FMA
+  float rescale_thr;       // running-max rescale threshold, log2 units (0 = exact)
 };
 
 // Top-k gathered MLA forward parameters.
@@ -52,6 +53,10 @@ struct TopkParams {
   float scale;
   float scale_log2;
 };
+
+// Kernel `name` of the 16-bit forward code object on the current device
+// (loaded on first use).
+hipError_t fwd16_function(const char* name, hipFunction_t* fn);
 
 // Launchers: enqueue on `stream`, return the HIP status of the launch.
 hipError_t launch_dense(Dt dt, int D, bool causal, bool has_mask, bool sparse,

@@ -1,0 +1,54 @@
+// Run-time loading of the 16-bit forward code object (built from
+// fa_fwd16.hip by build.py and embedded here as a byte array) and lookup of
+// its kernels by name, once per device.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "fa_internal.h"
+#include "fa_fwd16_hsaco.inc"
+
+namespace fa {
+namespace {
+
+struct DeviceModule {
+  hipModule_t module = nullptr;
+  std::unordered_map<std::string, hipFunction_t> functions;
+};
+
+std::mutex g_mutex;
+std::vector<DeviceModule> g_modules;
+
+}  // namespace
+
+hipError_t fwd16_function(const char* name, hipFunction_t* fn) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_mutex);
+  if ((int)g_modules.size() <= dev) g_modules.resize(dev + 1);
+  DeviceModule& dm = g_modules[dev];
+  if (!dm.module) {
+    e = hipModuleLoadData(&dm.module, kFwd16CodeObject);
+    if (e != hipSuccess) {
+      dm.module = nullptr;
+      return e;
+    }
+  }
+  auto it = dm.functions.find(name);
+  if (it != dm.functions.end()) {
+    *fn = it->second;
+    return hipSuccess;
+  }
+  hipFunction_t f = nullptr;
+  e = hipModuleGetFunction(&f, dm.module, name);
+  if (e != hipSuccess) return e;
+  dm.functions.emplace(name, f);
+  *fn = f;
+  return hipSuccess;
+}
+
+}  // namespace fa

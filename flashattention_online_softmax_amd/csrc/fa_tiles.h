@@ -1,0 +1,112 @@
+// Work decomposition and tile bookkeeping shared by the attention forward
+// kernels: workgroup-to-(batch, head, query block) mapping, the number of
+// 64-key tiles a query block visits (dense / causal / block-sparse), and the
+// LDS chunk swizzles of K and V tiles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+
+constexpr int BN = 64;  // keys per tile (16-bit path)
+
+// 16-byte chunk swizzles (chunk index XOR f(row)) of the K and V tiles.
+// K is read 16 bytes per lane by 32 lanes at 32 consecutive rows of one chunk
+// column; V is read 8 bytes per lane by ds_read_b64_tr_b16 at 4 consecutive
+// rows and 4 consecutive chunks per half wave.
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
+
+struct Work {
+  int b, hkv, hq, wg_row0, row0, Lq, Lk;
+};
+
+// Decodes blockIdx.x into (query block, head group, KV head, batch); the
+// last query block comes first (longest causal rows first) and the KV-head
+// index varies fastest, so all query heads of one KV head land on one XCD.
+template <int NW, int QT, int HP>
+__device__ __forceinline__ Work decode_work(const FwdParams& p) {
+  constexpr int WPH = NW / HP;
+  constexpr int MPH = WPH * QT * 32;
+  const int w = threadIdx.x >> 6;
+  const int BHkv = p.B * p.Hkv;
+  const int per_mb = BHkv * p.n_hgroups;
+  const int id = blockIdx.x;
+  const int mb_rank = id / per_mb;
+  const int r = id - mb_rank * per_mb;
+  const int mb = p.n_mblocks - 1 - mb_rank;
+  const int hg = r / BHkv;
+  const int bkv = r - hg * BHkv;
+  Work wk;
+  wk.b = bkv / p.Hkv;
+  wk.hkv = bkv - wk.b * p.Hkv;
+  const int hp = w / WPH, wi = w - (w / WPH) * WPH;
+  wk.hq = wk.hkv * p.G + hg * HP + hp;
+  wk.wg_row0 = mb * MPH;
+  wk.row0 = wk.wg_row0 + wi * QT * 32;
+  int lq = p.Sq, lk = p.Skv;
+  if (p.seqlens_q) lq = max(0, min(p.seqlens_q[wk.b], p.Sq));
+  if (p.seqlens_k) lk = max(0, min(p.seqlens_k[wk.b], p.Skv));
+  wk.Lq = lq;
+  wk.Lk = lk;
+  return wk;
+}
+
+// Block-sparse: compacts the valid entries of this query block's list into
+// key-tile start offsets in LDS (first the first halves of every listed
+// 128-key block, then the second halves that lie below Lk). Returns the
+// number of 64-key tiles. Executed by wave 0; all waves read the result after
+// the barrier.
+__device__ __forceinline__ int build_sparse_tiles(const FwdParams& p, const Work& wk, int qb,
+                                                  int* s_kstart, int* s_n) {
+  if ((threadIdx.x >> 6) == 0) {
+    const int lane = threadIdx.x & 63;
+    int n1 = 0, n2 = 0;
+    const int32_t* list = p.block_idx + wk.b * p.bi_sb + wk.hkv * p.bi_sh + (int64_t)qb * p.bi_sq;
+    // pass 1 counts first halves, pass 2 second halves
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int s0 = 0; s0 < p.max_sel; s0 += 64) {
+        const int s = s0 + lane;
+        int x = -1;
+        if (s < p.max_sel && wk.wg_row0 < wk.Lq) x = list[s];
+        const int k0 = x * 128 + pass * 64;
+        const bool ok = x >= 0 && k0 < wk.Lk;
+        const uint64_t bal = __ballot(ok);
+        const int pos = __popcll(bal & ((1ull << lane) - 1ull));
+        if (pass == 0) {
+          if (ok) s_kstart[n1 + pos] = k0;
+          n1 += __popcll(bal);
+        } else {
+          if (ok) s_kstart[n1 + n2 + pos] = k0;
+          n2 += __popcll(bal);
+        }
+      }
+    }
+    if (lane == 0) *s_n = n1 + n2;
+  }
+  __syncthreads();
+  return *s_n;
+}
+
+// Number of 64-key tiles of a dense (optionally causal) workgroup.
+template <bool CAUSAL>
+__device__ __forceinline__ int dense_tiles(const Work& wk, int mph, int bn) {
+  if (wk.wg_row0 >= wk.Lq) return 0;
+  int kend = wk.Lk;
+  if (CAUSAL) {
+    const int last_row = min(wk.wg_row0 + mph, wk.Lq) - 1;
+    kend = min(kend, last_row + (wk.Lk - wk.Lq) + 1);
+  }
+  return kend > 0 ? (kend + bn - 1) / bn : 0;
+}
+
+}  // namespace fa

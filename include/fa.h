@@ -7,15 +7,19 @@
  *   O_r   = sum_j softmax(s)_j * v_j                     (stored in q's dtype)
  *   LSE_r = ln sum_j exp(s_j)                            (fp32)
  *
- * evaluated tile by tile with an online softmax: a running row maximum m, a
- * running row sum l of exp(s - m) and an output accumulator rescaled by
- * exp(m_old - m_new) whenever m grows (every growth, i.e. an exact running
- * maximum). This is the standard-vs-tiled attention equivalence and the loop
- * invariant of the "FlashAttention correctness verification" page (sections
- * on the tiled computation and on formal verification), with the exact-max
- * rule of the flash-attention SM100 sparse-MLA page (background and
- * threshold-branch sections). Rows whose key set is empty produce O_r = 0
- * and LSE_r = -inf.
+ * evaluated tile by tile with an online softmax: a running row reference
+ * maximum m, a running row sum l of exp(s - m) and an output accumulator
+ * rescaled by exp(m_old - m_new) whenever m moves. This is the
+ * standard-vs-tiled attention equivalence and the loop invariant of the
+ * "FlashAttention correctness verification" page (sections on the tiled
+ * computation and on formal verification). When m moves is set by a rescale
+ * threshold t in log2 units, as on the flash-attention SM100 sparse-MLA page
+ * (background and threshold-branch sections): m moves to a tile's row max
+ * when that exceeds m by more than t. t = 0 is the exact running maximum
+ * (every growth rescales; the largest weight of a row is exactly 1 before the
+ * P.V product); t > 0 is the lazy rescale (weights up to 2^t, fewer
+ * rescales). Both give the same O and LSE up to rounding. Rows whose key set
+ * is empty produce O_r = 0 and LSE_r = -inf.
  *
  * Numerics: Q.K^T and P.V run on MFMA with fp32 accumulation; for fp16/bf16
  * inputs P is rounded to the input dtype (round to nearest even) before P.V
@@ -98,16 +102,20 @@ typedef enum fa_status {
  *       (sequence-length-cut) query/key lengths: bottom-right alignment.
  *  scale   finite float > 0 multiplying q.k (the scale of the attention
  *       formula); scale * log2(e) must be a normal float.
+ *  rescale_threshold  in [0, 10], log2 units: 0 = exact running max; the
+ *       sparse-MLA page's lazy default for the forward is 8.
  *  o    [B, Hq, Sq, Dv] in q's dtype (BNSD, strided)
  *  lse  fp32 [B, Hq, Sq], contiguous; natural-log LSE of the scaled scores.
  *
- * Supported: D == Dv in {64, 128}. Masked/excluded keys are never read
+ * Supported: D == Dv in {64, 128}; K/V row strides up to 2^22 elements.
+ * Masked/excluded keys are never read
  * into the P.V product with a non-zero weight.
  */
 fa_status fa_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
                  const fa_tensor* mask, const fa_tensor* seqlens_q,
                  const fa_tensor* seqlens_k, int causal, float scale,
-                 const fa_tensor* o, const fa_tensor* lse, void* stream);
+                 float rescale_threshold, const fa_tensor* o,
+                 const fa_tensor* lse, void* stream);
 
 /*
  * Block-sparse attention forward (the Mask2Idx block lists of the PyPTO BSA
@@ -125,11 +133,13 @@ fa_status fa_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
  *  seqlens  NULL or int32 [B], applied to queries and keys alike: rows
  *       i >= seqlens[b] produce O = 0 and LSE = -inf, keys j >= seqlens[b]
  *       are excluded.
+ *  rescale_threshold as in fa_fwd.
  *  maxSel must be <= 256.
  */
 fa_status fa_fwd_blocksparse(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
                              const fa_tensor* block_idx, int block_q, int block_k,
-                             const fa_tensor* seqlens, float scale, const fa_tensor* o,
+                             const fa_tensor* seqlens, float scale,
+                             float rescale_threshold, const fa_tensor* o,
                              const fa_tensor* lse, void* stream);
 
 /*

@@ -45,8 +45,9 @@ def name(lib, s):
     return lib.fa_status_str(s).decode()
 
 
-def call_fwd(lib, q, k, v, o, lse, mask=None, sq=None, sk=None, causal=0, scale=0.1):
-    return name(lib, lib.fa_fwd(R(q), R(k), R(v), R(mask), R(sq), R(sk), causal, scale, R(o), R(lse), None))
+def call_fwd(lib, q, k, v, o, lse, mask=None, sq=None, sk=None, causal=0, scale=0.1, thr=8.0):
+    return name(lib, lib.fa_fwd(R(q), R(k), R(v), R(mask), R(sq), R(sk), causal, scale, thr, R(o), R(lse),
+                                None))
 
 
 def good(B=2, Hq=4, Hkv=2, S=64, D=128, dt=fa.FA_BF16):
@@ -60,7 +61,7 @@ def test_exports_every_declared_function(lib):
             "fa_last_error", "fa_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.fa_version() == 100
+    assert lib.fa_version() == 200
 
 
 def test_status_names(lib):
@@ -76,6 +77,10 @@ def test_fa_fwd_validation(lib):
     assert call_fwd(lib, q, k, v, o, lse, scale=float("nan")) == "FA_ERR_VALUE"
     assert call_fwd(lib, q, k, v, o, lse, scale=-1.0) == "FA_ERR_VALUE"
     assert call_fwd(lib, q, k, v, o, lse, scale=0.0) == "FA_ERR_VALUE"
+    # rescale threshold: [0, 10] log2 units
+    assert call_fwd(lib, q, k, v, o, lse, thr=-0.5) == "FA_ERR_VALUE"
+    assert call_fwd(lib, q, k, v, o, lse, thr=10.5) == "FA_ERR_VALUE"
+    assert call_fwd(lib, q, k, v, o, lse, thr=float("nan")) == "FA_ERR_VALUE"
     assert call_fwd(lib, q, T([2, 2, 64, 128], fa.FA_F16), v, o, lse) == "FA_ERR_DTYPE"
     assert call_fwd(lib, q, k, v, o, T([2, 4, 64], fa.FA_BF16)) == "FA_ERR_DTYPE"
     assert call_fwd(lib, q, T([2, 3, 64, 128]), T([2, 3, 64, 128]), o, lse) == "FA_ERR_SHAPE"
@@ -108,8 +113,9 @@ def test_blocksparse_validation(lib):
     q, k, v, o, lse = good(S=256)
     bi = T([2, 16], fa.FA_I32)
 
-    def bs(bi=bi, bq=128, bk=128, seq=None, q=q):
-        return name(lib, lib.fa_fwd_blocksparse(R(q), R(k), R(v), R(bi), bq, bk, R(seq), 0.1, R(o), R(lse), None))
+    def bs(bi=bi, bq=128, bk=128, seq=None, q=q, thr=8.0):
+        return name(lib, lib.fa_fwd_blocksparse(R(q), R(k), R(v), R(bi), bq, bk, R(seq), 0.1, thr, R(o),
+                                                R(lse), None))
 
     assert bs(bq=64) == "FA_ERR_UNSUPPORTED"
     assert bs(bi=None) == "FA_ERR_NULL"
@@ -118,8 +124,10 @@ def test_blocksparse_validation(lib):
     assert bs(bi=T([2, 16], fa.FA_F32)) == "FA_ERR_DTYPE"
     assert bs(bi=T([3, 2, 2, 16], fa.FA_I32)) == "FA_ERR_SHAPE"
     assert bs(seq=T([2], fa.FA_U8)) == "FA_ERR_DTYPE"
+    assert bs(thr=-1.0) == "FA_ERR_VALUE"
     q0, k0, v0, o0, l0 = good(B=0, S=256)
-    assert name(lib, lib.fa_fwd_blocksparse(R(q0), R(k0), R(v0), R(bi), 128, 128, None, 0.1, R(o0), R(l0), None)) == "FA_OK"
+    assert name(lib, lib.fa_fwd_blocksparse(R(q0), R(k0), R(v0), R(bi), 128, 128, None, 0.1, 0.0, R(o0),
+                                            R(l0), None)) == "FA_OK"
 
 
 def test_topk_validation(lib):

@@ -14,9 +14,9 @@ from fa_testutil import absv, check, f32, gpu, sample_rows
 pytestmark = pytest.mark.gpu
 
 
-def run_dense(case, q, k, v, scale, causal=False, mask=None, sq=None, sk=None):
+def run_dense(case, q, k, v, scale, causal=False, mask=None, sq=None, sk=None, thr=8.0):
     o, lse = fa.fa_fwd(*gpu(q, k, v), scale=scale, causal=causal, mask=gpu(mask),
-                       seqlens_q=gpu(sq), seqlens_k=gpu(sk))
+                       seqlens_q=gpu(sq), seqlens_k=gpu(sk), rescale_threshold=thr)
     torch.cuda.synchronize()
     kw = dict(scale=f32(scale), causal=causal, mask=mask, seqlens_q=sq, seqlens_k=sk)
     o_ref, lse_ref = oracle.attn_dense(q, k, v, **kw)
@@ -24,20 +24,34 @@ def run_dense(case, q, k, v, scale, causal=False, mask=None, sq=None, sk=None):
     return check(case, o, lse, o_ref, lse_ref, q.dtype, o_abs)
 
 
+@pytest.mark.parametrize("thr", [0.0, 8.0])
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_dense_ragged(dtype, D, causal):
-    # 300 rows/keys: several 64-key tiles, a ragged tail, a partial query block
+def test_dense_ragged(dtype, D, causal, thr):
+    # 300 rows/keys: several 64-key tiles, a ragged tail, a partial query block;
+    # thr 0 = exact running max, 8 = lazy rescale
     _, q, k, v = synth.dense_inputs(100 + D + causal, 2, 4, 4, 300, 300, D, D, dtype)
-    run_dense("dense_%s_D%d_causal%d" % (dtype, D, causal), q, k, v, 1 / math.sqrt(D), causal)
+    run_dense("dense_%s_D%d_causal%d_thr%g" % (dtype, D, causal, thr), q, k, v, 1 / math.sqrt(D), causal,
+              thr=thr)
 
 
+@pytest.mark.parametrize("thr", [0.0, 8.0])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_gqa_causal_mask(dtype):
+def test_gqa_causal_mask(dtype, thr):
     g, q, k, v = synth.dense_inputs(7, 2, 8, 2, 333, 333, 128, 128, dtype)
     mask = synth.bernoulli_mask(g, 333, 333, 0.05)
-    run_dense("gqa_mask_%s" % dtype, q, k, v, 1 / math.sqrt(128), True, mask)
+    run_dense("gqa_mask_%s_thr%g" % (dtype, thr), q, k, v, 1 / math.sqrt(128), True, mask, thr=thr)
+
+
+def test_growing_scores_rescale_paths():
+    # Scores that keep growing along the keys force a rescale on every tile
+    # with the exact max and on some tiles with the lazy one; both must match.
+    g, q, k, v = synth.dense_inputs(21, 1, 2, 2, 256, 640, 128, 128, "bf16")
+    ramp = torch.linspace(0.2, 3.0, 640).view(1, 1, 640, 1)
+    k = (k.float() * ramp).to(k.dtype)
+    for thr in (0.0, 2.0, 8.0):
+        run_dense("ramp_thr%g" % thr, q, k, v, 1 / math.sqrt(128), False, thr=thr)
 
 
 def test_mask_4d_broadcasts_and_empty_rows():
