@@ -228,19 +228,13 @@ __device__ __forceinline__ void acc_written(f32x16 (&a)[N]) {
     asm volatile("s_nop 4" : "+a"(a[0]), "+a"(a[1]));
 }
 
-// One loop step j of a wave (64-key tiles; a wave owns QT blocks of 32 query
-// rows and reads every K/V operand once for all of them):
-//   softmax(j): mask, row max, reference max update, p = exp2(s c - m), row
-//               sum, p rounded into the P operand;
-//   S(j+1):     S^T = K_{j+1} Q^T into the other score buffer;
-//   PV(j-1):    O^T += V_{j-1}^T P_{j-1}^T.
-// softmax(j) and PV(j-1) are independent: their instructions are interleaved
-// (per V operand, QT P V MFMAs and a slice of the softmax VALU work), then
-// S(j+1) refills the score registers. Operands are read AHEAD ahead.
-// Every step runs the same code (no diamonds around the MFMAs): a step past
-// this wave's last tile does an inactive softmax (P = 0, m and l unchanged),
-// the P V of step 0 multiplies P = 0 with a zeroed V slot, and the S of the
-// last step reads a slot whose result goes unused.
+// Per 64-key tile j a wave (QT blocks of 32 query rows; every K/V operand it
+// reads serves all of them) has a VALU phase V(j) and an MFMA phase M(j):
+//   V(j): mask, row max, reference max update, p = exp2(s c - m), row sum,
+//         p rounded into the P operand (and the rare rescale of O);
+//   M(j): S(j+1) = K_{j+1} Q^T and O^T += V_j^T P_j^T, interleaved.
+// The waves form two groups one phase apart (see the loop below), so on each
+// SIMD one wave's V phase overlaps the other's M phase.
 //
 // Running max with a rescale threshold t (log2 units): a row's reference max
 // moves only when the tile's max exceeds it by more than t; then O and l are
@@ -248,12 +242,8 @@ __device__ __forceinline__ void acc_written(f32x16 (&a)[N]) {
 // growth rescales, the largest p of the row is exactly 1); t > 0 is the lazy
 // rescale, with p <= 2^t.
 //
-// K and V tiles live in three-deep LDS rings (tile t in slot t % 3). Step j
-// copies K_{j+3} into the slot of K_j (last read by S(j) in step j-1) and
-// V_{j+1} into the slot of V_{j-2} (last read by PV(j-2) in step j-1). A
-// step ends by waiting for the copies of the step before and a workgroup
-// barrier, so a tile copied in step j is visible from step j+2 on, when it is
-// first read.
+// K and V tiles live in three-deep LDS rings (tile t in slot t % 3), filled
+// by LDS-DMA copies issued three (K) and two (V) tiles ahead of use.
 template <class T, int D, int NW, int QT, int HP, bool CAUSAL, bool MASK, bool SPARSE>
 __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   constexpr int WPH = NW / HP;
@@ -325,7 +315,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   for (int b = 0; b < QT; ++b) acc_written(oacc[b]);  // O^T lives in AGPRs from here on
   float m_ref[QT], l_run[QT];
   f32x16 sc[QT][2];      // [block][kt]: scores of the tile the next softmax works on
-  u32x4 pp[2][QT][4];    // [parity][block][k-step]: P operand of a tile
+  u32x4 pp[1][QT][4];    // P operand of the tile between its V and M phases
 #pragma unroll
   for (int b = 0; b < QT; ++b) {
     m_ref[b] = -INFINITY;
@@ -335,9 +325,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[b][kt][i] = 0.f;
 #pragma unroll
-    for (int par = 0; par < 2; ++par)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) pp[par][b][ks] = u32x4{0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < 4; ++ks) pp[0][b][ks] = u32x4{0u, 0u, 0u, 0u};
   }
 
   auto tile_start = [&](int it) __attribute__((always_inline)) { return SPARSE ? s_kstart[it] : it * BN; };
@@ -475,55 +463,51 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     }
   };
 
-  // S = K Q^T of the tile in kt_buf into sn, K operands read AHEAD ahead.
-  auto scores = [&](f32x16 (&sn)[QT][2], const uint16_t* kt_buf) __attribute__((always_inline)) {
+  // M phase: S = K Q^T of the tile in kt_buf into sn and O^T += V^T P^T
+  // with the tile in vt_buf, interleaved operand by operand (independent
+  // accumulators), operands read AHEAD ahead.
+  auto mphase = [&](f32x16 (&sn)[QT][2], const u32x4 (&pop)[QT][4], const uint16_t* kt_buf,
+                    const uint16_t* vt_buf, bool do_pv) __attribute__((always_inline)) {
     const lds_u16* kb = lds_ptr(lds_addr_of(kt_buf));
-    u32x4 kq[RING];
+    const lds_u16* vb[DT];
 #pragma unroll
-    for (int r = 0; r < AHEAD; ++r) kq[r] = kread(kb, r);
+    for (int dt = 0; dt < DT; ++dt) vb[dt] = lds_ptr(lds_addr_of(vt_buf) + 2 * voff[dt]);
+    u32x4 kq[RING], vq[RING];
+#pragma unroll
+    for (int r = 0; r < AHEAD; ++r) {
+      kq[r] = kread(kb, r);
+      if (do_pv) vq[r] = vread(vb, r);
+    }
 #pragma unroll
     for (int r = 0; r < NS; ++r) {
-      if (r + AHEAD < NS) kq[(r + AHEAD) % RING] = kread(kb, r + AHEAD);
+      if (r + AHEAD < NS) {
+        kq[(r + AHEAD) % RING] = kread(kb, r + AHEAD);
+        if (do_pv) vq[(r + AHEAD) % RING] = vread(vb, r + AHEAD);
+      }
 #pragma unroll
       for (int b = 0; b < QT; ++b) {
-        // key half r & 1, k-step r >> 1
+        // S: key half r & 1, k-step r >> 1
         if (r < 2)
           Mma<T>::v0b(sn[b][r & 1], kq[r % RING], qop[b][r >> 1]);
         else
           Mma<T>::vb(sn[b][r & 1], kq[r % RING], qop[b][r >> 1]);
+        // P V: d tile r % DT, key step r / DT
+        if (do_pv) Mma<T>::a(oacc[b][r % DT], vq[r % RING], pop[b][r / DT]);
       }
     }
-    // Results complete before the compiler may touch the registers again.
+    // S results complete before the compiler may touch the registers again.
 #pragma unroll
     for (int b = 0; b < QT; ++b) mfma_wait_v(sn[b]);
   };
 
-  // softmax(j) on sv into pop, interleaved V operand by V operand with
-  // PV(j-1) (pprev, V tile in vt_buf), whose MFMAs accumulate in AGPRs and so
-  // leave the VALU free.
-  auto softmax_pv = [&](f32x16 (&sv)[QT][2], u32x4 (&pop)[QT][4], const u32x4 (&pprev)[QT][4],
-                        const uint16_t* vt_buf, bool act, bool o_live) __attribute__((always_inline)) {
-    const lds_u16* vb[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vb[dt] = lds_ptr(lds_addr_of(vt_buf) + 2 * voff[dt]);
-    u32x4 vq[RING];
-#pragma unroll
-    for (int r = 0; r < AHEAD; ++r) vq[r] = vread(vb, r);
+  // V phase: softmax(j) of the scores in sv into pop (VALU only), and the
+  // rescale of O and l when a reference max moved (O is only ever touched by
+  // MFMAs otherwise).
+  auto vphase = [&](f32x16 (&sv)[QT][2], u32x4 (&pop)[QT][4], bool act, bool o_live)
+                    __attribute__((always_inline)) {
     upd_any = false;
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < NP; ++r) {
-      if (r + AHEAD < NP) vq[(r + AHEAD) % RING] = vread(vb, r + AHEAD);
-      // d tile r % DT, key step r / DT
-#pragma unroll
-      for (int b = 0; b < QT; ++b) Mma<T>::a(oacc[b][r % DT], vq[r % RING], pprev[b][r / DT]);
-#pragma unroll
-      for (int s = (NSLICE * r) / NP; s < (NSLICE * (r + 1)) / NP; ++s) slice(sv, pop, s, act);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Rescale of O and l when a reference max moved (O is only ever touched
-    // by MFMAs otherwise). An inactive step's row sum is dropped, not
-    // multiplied by zero: its scores may be anything.
+    for (int sl = 0; sl < NSLICE; ++sl) slice(sv, pop, sl, act);
     if (o_live && __builtin_amdgcn_ballot_w64(upd_any) != 0) {
 #pragma unroll
       for (int b = 0; b < QT; ++b) {
@@ -539,19 +523,40 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     for (int b = 0; b < QT; ++b) l_run[b] = act ? __builtin_fmaf(l_run[b], alpha[b], rs0[b] + rs1[b]) : l_run[b];
   };
 
-  // Prologue. V slot 2 is read by the PV(-1) of step 0 (with P = 0), so it
-  // must hold finite values: zero it. Then K_0, K_1, K_2 and V_0 in flight.
-  {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    uint16_t* v2 = s_vring + 2 * TILE;
-    for (int i = tid * 8; i < TILE; i += NW * 64 * 8) *(u32x4*)&v2[i] = z;
-  }
-  __syncthreads();
+  // Global phase 2m+2 (m >= 0): copy K_{m+3} into K_m's slot (last read by
+  // group 1's S in phase 2m+1) and V_{m+2} into V_{m-1}'s slot (last read by
+  // group 1's P V in phase 2m+1).
+  auto copies = [&](int m) __attribute__((always_inline)) {
+    bool any = false;
+    if (m + 3 < n_iter) {
+      kcopy.issue(tile_start(m + 3), wk.Lk, s_kring + (m % 3) * TILE);
+      any = true;
+    }
+    if (m + 2 < n_iter) {
+      vcopy.issue(tile_start(m + 2), wk.Lk, s_vring + ((m + 2) % 3) * TILE);
+      any = true;
+    }
+    return any;
+  };
+  // End of a phase: this wave's copies of the phase before are complete (those
+  // of this phase may still fly), then the workgroup barrier.
+  auto end_phase = [&](bool copied_now) __attribute__((always_inline)) {
+    if (copied_now)
+      wait_vmem_below<NCOPY>();
+    else
+      wait_vmem();
+    barrier_keep_copies();
+  };
+
+  // Prologue: K_0, K_1, K_2, V_0, V_1 in flight.
   if (n_iter > 0) {
     kcopy.issue(tile_start(0), wk.Lk, s_kring);
     vcopy.issue(tile_start(0), wk.Lk, s_vring);
   }
-  if (n_iter > 1) kcopy.issue(tile_start(1), wk.Lk, s_kring + TILE);
+  if (n_iter > 1) {
+    kcopy.issue(tile_start(1), wk.Lk, s_kring + TILE);
+    vcopy.issue(tile_start(1), wk.Lk, s_vring + TILE);
+  }
   if (n_iter > 2) kcopy.issue(tile_start(2), wk.Lk, s_kring + 2 * TILE);
   // Make the compiler wait for the Q loads here, once: it does not see the
   // copies above, and otherwise would wait for its Q loads (vmcnt(0), which
@@ -562,45 +567,39 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     for (int ds = 0; ds < DS; ++ds) asm volatile("s_nop 4" : "+a"(qop[b][ds]));
   wait_vmem();
   __syncthreads();
-  // S(0).
-  scores(sc, s_kring);
-  // Nobody may overwrite K_0's slot (step 0 copies K_3 there) before every
-  // wave has read it.
-  barrier_keep_copies();
 
-  // One loop step; PAR = j & 1 selects the buffers.
-  auto step = [&](auto par_tag, int j) __attribute__((always_inline)) {
-    constexpr int PAR = decltype(par_tag)::value;
-    bool copied = false;
-    if (j + 3 < n_iter) {
-      kcopy.issue(tile_start(j + 3), wk.Lk, s_kring + (j % 3) * TILE);
-      copied = true;
-    }
-    if (j + 1 < n_iter) {
-      vcopy.issue(tile_start(j + 1), wk.Lk, s_vring + ((j + 1) % 3) * TILE);
-      copied = true;
-    }
+  // Two wave groups one phase apart: group 0 runs M(-1) V(0) M(0) V(1) ...,
+  // group 1 the same one phase later; every phase ends with a workgroup
+  // barrier. Waves w and w + NW/2 share a SIMD, so there one wave's softmax
+  // issues while the other's MFMAs run. M(j) computes S(j+1) and O += P(j)
+  // V(j); V(j) turns S(j) into P(j). Every wave runs the same stream: a
+  // softmax past this wave's tiles is inactive (P = 0, m and l unchanged),
+  // and the S of the last M phase is computed from a slot whose result goes
+  // unused.
+  const int grp = (int)(threadIdx.x >> 6) / (NW / 2);
+  if (grp == 1) end_phase(false);
+  mphase(sc, pp[0], s_kring, s_vring, false);  // M(-1): S(0)
+  end_phase(false);
+  for (int j = 0; j < n_iter; ++j) {
     const bool act = j < n_act;
+    // V(j): global phase 2j+1 (group 0) or 2j+2 (group 1).
     if (act) {
 #pragma unroll
       for (int b = 0; b < QT; ++b) mask_tile(sc[b], b, j);
     }
-    softmax_pv(sc, pp[PAR], pp[PAR ^ 1], s_vring + ((j + 2) % 3) * TILE, act, j > 0);
-    // S(j+1) reuses the score registers (the softmax above consumed them).
-    // In the last step there is no tile j+1 and the result goes unused; the
-    // slot read is in bounds either way.
-    scores(sc, s_kring + ((j + 1) % 3) * TILE);
-    if (copied)
-      wait_vmem_below<NCOPY>();
-    else
-      wait_vmem();
-    barrier_keep_copies();
-  };
-  for (int j = 0; j <= n_iter; j += 2) {
-    step(std::integral_constant<int, 0>(), j);
-    if (j + 1 > n_iter) break;
-    step(std::integral_constant<int, 1>(), j + 1);
+    // After the mask loads: the compiler's wait for them would also drain the
+    // copies, which it does not see.
+    bool cp = false;
+    if (grp == 1) cp = copies(j);
+    vphase(sc, pp[0], act, j > 0);
+    end_phase(cp);
+    // M(j): global phase 2j+2 (group 0) or 2j+3 (group 1).
+    cp = false;
+    if (grp == 0) cp = copies(j);
+    mphase(sc, pp[0], s_kring + ((j + 1) % 3) * TILE, s_vring + (j % 3) * TILE, true);
+    end_phase(cp);
   }
+  if (grp == 0) end_phase(false);
 
   // Epilogue.
   uint16_t* og = (uint16_t*)p.o + wk.b * p.o_sb + wk.hq * p.o_sh;
