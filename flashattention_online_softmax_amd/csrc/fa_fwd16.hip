@@ -53,22 +53,24 @@ namespace {
 // Issued through inline assembly so that the compiler does not hold later
 // LDS reads of other buffers behind it; the kernel itself waits for these
 // copies (s_waitcnt vmcnt) before the barrier that publishes their data.
-__device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
-      :
-      : "s"(lds_addr), "v"(voff), "s"(gbase)
-      : "memory", "m0");
-}
-
 // A pointer whose value is the same in every lane, moved to scalar registers.
 __device__ __forceinline__ const char* uniform_ptr(const void* p) {
   const uint64_t v = (uint64_t)(uintptr_t)p;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// gbase and lds_addr are the same in every lane of the wave (they are moved
+// to scalar registers here, a no-op when they already are).
+__device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(uniform_ptr(gbase))
+      : "memory", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
@@ -466,18 +468,26 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   // M phase: S = K Q^T of the tile in kt_buf into sn and O^T += V^T P^T
   // with the tile in vt_buf, interleaved operand by operand (independent
   // accumulators), operands read AHEAD ahead.
+  // Operands 0 .. AHEAD-1 of an M phase, read ahead of it (at the end of the
+  // wave's V phase, so the M phase starts without waiting on LDS).
+  u32x4 kq[RING], vq[RING];
+  auto mprefetch = [&](const uint16_t* kt_buf, const uint16_t* vt_buf, bool do_pv) __attribute__((always_inline)) {
+    const lds_u16* kb = lds_ptr(lds_addr_of(kt_buf));
+    const lds_u16* vb[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vb[dt] = lds_ptr(lds_addr_of(vt_buf) + 2 * voff[dt]);
+#pragma unroll
+    for (int r = 0; r < AHEAD; ++r) {
+      kq[r] = kread(kb, r);
+      if (do_pv) vq[r] = vread(vb, r);
+    }
+  };
   auto mphase = [&](f32x16 (&sn)[QT][2], const u32x4 (&pop)[QT][4], const uint16_t* kt_buf,
                     const uint16_t* vt_buf, bool do_pv) __attribute__((always_inline)) {
     const lds_u16* kb = lds_ptr(lds_addr_of(kt_buf));
     const lds_u16* vb[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vb[dt] = lds_ptr(lds_addr_of(vt_buf) + 2 * voff[dt]);
-    u32x4 kq[RING], vq[RING];
-#pragma unroll
-    for (int r = 0; r < AHEAD; ++r) {
-      kq[r] = kread(kb, r);
-      if (do_pv) vq[r] = vread(vb, r);
-    }
 #pragma unroll
     for (int r = 0; r < NS; ++r) {
       if (r + AHEAD < NS) {
@@ -523,9 +533,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     for (int b = 0; b < QT; ++b) l_run[b] = act ? __builtin_fmaf(l_run[b], alpha[b], rs0[b] + rs1[b]) : l_run[b];
   };
 
-  // Global phase 2m+2 (m >= 0): copy K_{m+3} into K_m's slot (last read by
-  // group 1's S in phase 2m+1) and V_{m+2} into V_{m-1}'s slot (last read by
-  // group 1's P V in phase 2m+1).
+  // Copies of K_{m+3} (into K_m's slot) and V_{m+2} (into V_{m-1}'s slot).
   auto copies = [&](int m) __attribute__((always_inline)) {
     bool any = false;
     if (m + 3 < n_iter) {
@@ -576,28 +584,35 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   // softmax past this wave's tiles is inactive (P = 0, m and l unchanged),
   // and the S of the last M phase is computed from a slot whose result goes
   // unused.
-  const int grp = (int)(threadIdx.x >> 6) / (NW / 2);
+  //
+  // Copies: every wave issues its share of the copies of K_{j+3} (into K_j's
+  // slot) and V_{j+2} (into V_{j-1}'s slot) right after the MFMAs of its
+  // M(j), while they drain. Those slots were last read in M(j-1), which both
+  // groups have finished (group 0's M(j) is global phase 2j+2, group 1's
+  // M(j-1) is 2j+1). A wave waits for its copies at the end of its next
+  // phase; the first reader of K_{j+3} / V_{j+2} is M(j+2), two phases later.
+  const int grp = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) / (NW / 2));
   if (grp == 1) end_phase(false);
+  mprefetch(s_kring, s_vring, false);
   mphase(sc, pp[0], s_kring, s_vring, false);  // M(-1): S(0)
   end_phase(false);
   for (int j = 0; j < n_iter; ++j) {
     const bool act = j < n_act;
+    const uint16_t* kt_buf = s_kring + ((j + 1) % 3) * TILE;  // K_{j+1}
+    const uint16_t* vt_buf = s_vring + (j % 3) * TILE;        // V_j
     // V(j): global phase 2j+1 (group 0) or 2j+2 (group 1).
     if (act) {
 #pragma unroll
       for (int b = 0; b < QT; ++b) mask_tile(sc[b], b, j);
     }
-    // After the mask loads: the compiler's wait for them would also drain the
-    // copies, which it does not see.
-    bool cp = false;
-    if (grp == 1) cp = copies(j);
     vphase(sc, pp[0], act, j > 0);
-    end_phase(cp);
+    // K_{j+1} and V_j have been in LDS since phase 2j (their copies were
+    // waited for two phases after they were issued in M(j-2)).
+    mprefetch(kt_buf, vt_buf, true);
+    end_phase(false);
     // M(j): global phase 2j+2 (group 0) or 2j+3 (group 1).
-    cp = false;
-    if (grp == 0) cp = copies(j);
-    mphase(sc, pp[0], s_kring + ((j + 1) % 3) * TILE, s_vring + (j % 3) * TILE, true);
-    end_phase(cp);
+    mphase(sc, pp[0], kt_buf, vt_buf, true);
+    end_phase(copies(j));
   }
   if (grp == 0) end_phase(false);
 
