@@ -2,14 +2,15 @@
 
 Two kinds of device code go into it:
   * fa_abi / fa_dense / fa_topk: ordinary HIP sources compiled by hipcc.
-  * fa_fwd16: the 16-bit forward kernels, compiled on their own into a gfx950
-    code object that libfa.so embeds and loads at run time. They keep their
-    O accumulators in AGPRs (so that VALU work overlaps the MFMAs) and need
-    about 170 VGPRs next to them; with both register files in use the
-    compiler would split the 256 registers of a wave evenly (128 + 128).
-    The build therefore stops after the device IR, sets each kernel's
-    "amdgpu-agpr-alloc" (the number of AGPRs to reserve: the O accumulators),
-    generates code with llc and links the code object with lld.
+  * fa_fwd16 and fa_topk16: the 16-bit forward kernels, compiled on their own
+    into one gfx950 code object that libfa.so embeds and loads at run time.
+    They keep their O accumulators (and for fa_fwd16 the Q operands) in AGPRs
+    so that VALU work overlaps the MFMAs, and need most of the VGPRs next to
+    them; with both register files in use the compiler would split a wave's
+    registers evenly between the two files. The build therefore stops after
+    the device IR, links the two modules, sets each kernel's
+    "amdgpu-agpr-alloc" (the number of AGPRs to reserve), generates code with
+    llc and links the code object with lld.
 """
 import concurrent.futures
 import os
@@ -29,10 +30,17 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-I", os.path.join(HERE, "..", "include")]
 
 
+CODE_OBJECT_SOURCES = ["fa_fwd16.hip", "fa_topk16.hip"]
+
+
 def _agprs(kernel: str) -> int:
-    """AGPRs reserved for an fa_fwd16 kernel: for each 32-row block of the wave
-    its O^T accumulators (D / 2 per lane) and its Q^T operands (D / 4 per lane);
-    name fields d<D> and q<blocks>."""
+    """AGPRs reserved for a code-object kernel.
+
+    fa_fwd16: for each 32-row block of the wave its O^T accumulators (D / 2 per
+    lane) and its Q^T operands (D / 4 per lane); name fields d<D>, q<blocks>.
+    fa_topk16: the O^T accumulators of 32 heads x 512 (256 per lane)."""
+    if kernel.startswith("fa_topk16_"):
+        return 256
     d = int(re.search(r"_d(\d+)_", kernel).group(1))
     q = int(re.search(r"_q(\d+)_", kernel).group(1))
     return (d // 2 + d // 4) * q
@@ -52,7 +60,7 @@ def _compile(src: str) -> str:
 
 
 def _set_agpr_alloc(ir: str) -> str:
-    """Gives every fa_fwd16 kernel its own attribute group with amdgpu-agpr-alloc set."""
+    """Gives every code-object kernel its own attribute group with amdgpu-agpr-alloc set."""
     groups = dict(re.findall(r"^attributes #(\d+) = \{(.*)\}$", ir, re.M))
     next_id = max(int(g) for g in groups) + 1
     new_groups = []
@@ -66,38 +74,47 @@ def _set_agpr_alloc(ir: str) -> str:
         next_id += 1
         return out
 
-    ir, n = re.subn(r"^(define [^@]*amdgpu_kernel void @)(fa_fwd16_\w+)(\(.*\) [^#]*#)(\d+)",
+    ir, n = re.subn(r"^(define [^@]*amdgpu_kernel void @)(fa_(?:fwd|topk)16_\w+)(\(.*\) [^#]*#)(\d+)",
                     patch_define, ir, flags=re.M)
     if n == 0:
-        raise RuntimeError("no fa_fwd16 kernels found in the device IR")
+        raise RuntimeError("no code-object kernels found in the device IR")
     return ir + "\n" + "\n".join(new_groups) + "\n"
 
 
-def _build_fwd16_code_object() -> str:
-    """fa_fwd16.hip -> gfx950 code object -> C array include for fa_module.hip."""
-    bc = os.path.join(BUILD_DIR, "fa_fwd16.bc")
-    ll = os.path.join(BUILD_DIR, "fa_fwd16.ll")
-    obj = os.path.join(BUILD_DIR, "fa_fwd16.gfx950.o")
-    hsaco = os.path.join(BUILD_DIR, "fa_fwd16.hsaco")
+def _device_ir(src: str) -> str:
+    bc = os.path.join(BUILD_DIR, src.replace(".hip", ".bc"))
     _run([HIPCC, *FLAGS, "--cuda-device-only", "-emit-llvm", "-c",
-          os.path.join(CSRC, "fa_fwd16.hip"), "-o", bc], "hipcc fa_fwd16 (device IR)")
+          os.path.join(CSRC, src), "-o", bc], "hipcc %s (device IR)" % src)
+    return bc
+
+
+def _build_code_object() -> str:
+    """fa_fwd16.hip + fa_topk16.hip -> gfx950 code object -> C array include
+    for fa_module.hip."""
+    bc = os.path.join(BUILD_DIR, "fa_kernels.bc")
+    ll = os.path.join(BUILD_DIR, "fa_kernels.ll")
+    obj = os.path.join(BUILD_DIR, "fa_kernels.gfx950.o")
+    hsaco = os.path.join(BUILD_DIR, "fa_kernels.hsaco")
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(CODE_OBJECT_SOURCES)) as ex:
+        bcs = list(ex.map(_device_ir, CODE_OBJECT_SOURCES))
+    _run([os.path.join(LLVM_BIN, "llvm-link"), *bcs, "-o", bc], "llvm-link")
     _run([os.path.join(LLVM_BIN, "llvm-dis"), bc, "-o", ll], "llvm-dis")
     with open(ll) as f:
         ir = _set_agpr_alloc(f.read())
     with open(ll, "w") as f:
         f.write(ir)
     _run([os.path.join(LLVM_BIN, "llc"), "-O3", "-mtriple=amdgcn-amd-amdhsa", "-mcpu=gfx950",
-          "-filetype=obj", ll, "-o", obj], "llc fa_fwd16")
-    _run([os.path.join(LLVM_BIN, "ld.lld"), "-shared", obj, "-o", hsaco], "ld.lld fa_fwd16")
+          "-filetype=obj", ll, "-o", obj], "llc code object")
+    _run([os.path.join(LLVM_BIN, "ld.lld"), "-shared", obj, "-o", hsaco], "ld.lld code object")
     with open(hsaco, "rb") as f:
         blob = f.read()
-    inc = os.path.join(BUILD_DIR, "fa_fwd16_hsaco.inc")
+    inc = os.path.join(BUILD_DIR, "fa_kernels_hsaco.inc")
     lines = []
     for i in range(0, len(blob), 24):
         lines.append(",".join(str(b) for b in blob[i:i + 24]) + ",")
     with open(inc + ".tmp", "w") as f:
-        f.write("// generated by build.py from csrc/fa_fwd16.hip; do not edit\n")
-        f.write("static const unsigned char kFwd16CodeObject[%d] __attribute__((aligned(4096))) = {\n" % len(blob))
+        f.write("// generated by build.py from csrc/%s; do not edit\n" % " + csrc/".join(CODE_OBJECT_SOURCES))
+        f.write("static const unsigned char kCodeObject[%d] __attribute__((aligned(4096))) = {\n" % len(blob))
         f.write("\n".join(lines))
         f.write("\n};\n")
     os.replace(inc + ".tmp", inc)
@@ -108,9 +125,9 @@ def build(verbose: bool = False) -> str:
     """Compiles every HIP source for gfx950 and links libfa.so next to this file."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        fwd16 = ex.submit(_build_fwd16_code_object)
+        kernels = ex.submit(_build_code_object)
         others = [ex.submit(_compile, s) for s in SOURCES if s != "fa_module.hip"]
-        fwd16.result()
+        kernels.result()
         objs = [f.result() for f in others] + [_compile("fa_module.hip")]
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], "link")

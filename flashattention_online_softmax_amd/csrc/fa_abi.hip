@@ -300,6 +300,11 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
   if (Hq % 32 != 0) return fail(FA_ERR_UNSUPPORTED, "Hq (%lld) must be a multiple of 32", (long long)Hq);
   if (W > 4096) return fail(FA_ERR_UNSUPPORTED, "W (%lld) > 4096", (long long)W);
   if (!fits_i32(T * Hq) || !fits_i32(S) || !fits_i32(W)) return fail(FA_ERR_UNSUPPORTED, "problem too large");
+  // Bytes spanned by k and v (the gathers address them with 32-bit offsets).
+  const int64_t k_bytes = S > 0 ? (S - 1) * k->stride[0] * 2 + Dqk * 2 : 0;
+  const int64_t v_bytes = S > 0 ? (S - 1) * v->stride[0] * 2 + Dv * 2 : 0;
+  if (k_bytes > 0xFFFFFFFFLL || v_bytes > 0xFFFFFFFFLL)
+    return fail(FA_ERR_UNSUPPORTED, "k and v must each span less than 4 GiB");
   if (T * Hq == 0) return FA_OK;
   if (W > 0 && !idx->data) return fail(FA_ERR_NULL, "idx.data is NULL");
   fa::TopkParams p;
@@ -315,6 +320,7 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
   p.o_st = o->stride[0]; p.o_sh = o->stride[1];
   p.idx_st = idx->stride[0];
   p.T = (int32_t)T; p.Hq = (int32_t)Hq; p.S = (int32_t)S; p.W = (int32_t)W;
+  p.k_bytes = (uint32_t)k_bytes; p.v_bytes = (uint32_t)v_bytes;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   return hip_status(fa::launch_topk(to_dt(q->dtype), p, (hipStream_t)stream));

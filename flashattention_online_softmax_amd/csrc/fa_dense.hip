@@ -217,7 +217,7 @@ hipError_t launch16_named(const char* tn, int D, bool causal, bool mask, bool sp
   snprintf(name, sizeof(name), "fa_fwd16_%s_d%d_w%d_q%d_h%d_c%dm%ds%d", tn, D, NW, QT, HP,
            causal ? 1 : 0, mask ? 1 : 0, sparse ? 1 : 0);
   hipFunction_t fn = nullptr;
-  hipError_t e = fwd16_function(name, &fn);
+  hipError_t e = code_object_function(name, &fn);
   if (e != hipSuccess) return e;
   void* args[] = {&p};
   return hipModuleLaunchKernel(fn, grid.x, grid.y, grid.z, NW * 64, 1, 1, 0, st, args, nullptr);

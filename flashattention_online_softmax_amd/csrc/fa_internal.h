@@ -49,14 +49,15 @@ struct TopkParams {
   int64_t o_st, o_sh;
   int64_t idx_st;
   int32_t T, Hq, S, W;
+  uint32_t k_bytes, v_bytes;  // bytes spanned by k and v
   int32_t n_htiles;  // head tiles per token
   float scale;
   float scale_log2;
 };
 
-// Kernel `name` of the 16-bit forward code object on the current device
-// (loaded on first use).
-hipError_t fwd16_function(const char* name, hipFunction_t* fn);
+// Kernel `name` of the run-time loaded code object (the 16-bit dense,
+// block-sparse and top-k kernels) on the current device (loaded on first use).
+hipError_t code_object_function(const char* name, hipFunction_t* fn);
 
 // Launchers: enqueue on `stream`, return the HIP status of the launch.
 hipError_t launch_dense(Dt dt, int D, bool causal, bool has_mask, bool sparse,

@@ -1,6 +1,6 @@
-// Run-time loading of the 16-bit forward code object (built from
-// fa_fwd16.hip by build.py and embedded here as a byte array) and lookup of
-// its kernels by name, once per device.
+// Run-time loading of the code object that holds the 16-bit forward kernels
+// (built from fa_fwd16.hip and fa_topk16.hip by build.py and embedded here as
+// a byte array) and lookup of its kernels by name, once per device.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -9,7 +9,7 @@
 #include <vector>
 
 #include "fa_internal.h"
-#include "fa_fwd16_hsaco.inc"
+#include "fa_kernels_hsaco.inc"
 
 namespace fa {
 namespace {
@@ -24,7 +24,7 @@ std::vector<DeviceModule> g_modules;
 
 }  // namespace
 
-hipError_t fwd16_function(const char* name, hipFunction_t* fn) {
+hipError_t code_object_function(const char* name, hipFunction_t* fn) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -32,7 +32,7 @@ hipError_t fwd16_function(const char* name, hipFunction_t* fn) {
   if ((int)g_modules.size() <= dev) g_modules.resize(dev + 1);
   DeviceModule& dm = g_modules[dev];
   if (!dm.module) {
-    e = hipModuleLoadData(&dm.module, kFwd16CodeObject);
+    e = hipModuleLoadData(&dm.module, kCodeObject);
     if (e != hipSuccess) {
       dm.module = nullptr;
       return e;

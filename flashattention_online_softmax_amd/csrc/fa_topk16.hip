@@ -1,0 +1,489 @@
+// Top-k gathered sparse MLA forward for gfx950 (one KV head shared by every
+// query head), fp16 / bf16, Dqk = 576 (512 latent + 64 rope), Dv = 512.
+//
+// Method: per token t, attention of every query head over the keys named in
+// idx[t, :] (the sparse-MLA forward of the flash-attention SM100 page,
+// background section), with that page's exact running max (threshold 0: any
+// growth of a row max rescales O and l, so the largest p of a row is exactly
+// 1.0 before it is rounded for P.V). The online-softmax recurrence is the one
+// of the "FlashAttention correctness verification" page (tiled computation,
+// loop invariant).
+//
+// This file is compiled into the run-time loaded code object (see build.py):
+// a wave keeps its O^T accumulators in all 256 AGPRs next to about 230
+// VGPRs, a split the code object gets through amdgpu-agpr-alloc.
+//
+// Decomposition (MI355X): one workgroup of 4 waves (one per SIMD) per token
+// and 128 query heads; wave w owns heads 32 w .. 32 w + 31 as two 16-head
+// tiles. The MFMAs are v_mfma_f32_16x16x32 (every accumulator is a 4-register
+// tile, so the O rescale can be spread over the MFMA stream one tile at a
+// time; every K or V operand read from LDS feeds both head tiles). Q^T
+// (576 x 32) stays in VGPRs as the B operand of S^T = K_g Q^T; O^T (512 x 32
+// fp32) fills the AGPRs. The valid entries of idx[t, :] are compacted into LDS
+// (list order kept, negative slots dropped); 32 consecutive list entries form
+// a tile whose key rows (1152 bytes each) are gathered from HBM/L2 straight
+// into LDS by global_load_lds_dwordx4 (no register staging; an index at or
+// past S reads the last row). When V is the first 512 columns of K (the MLA latent) the
+// tiles live in a 4-deep ring and P.V reads V^T out of the gathered K rows
+// with ds_read_b64_tr_b16; otherwise K and V tiles have 2-deep rings of their
+// own. Only the last tile of a token can be partial: its padding rows repeat
+// a valid key and their scores are masked to -inf.
+//
+// Lane l of a wave (G = l / 16, n = l % 16) owns heads 16 ht + n of the wave
+// (ht = 0, 1) and, of each 32-key tile, keys 4 G .. 4 G + 3 and
+// 16 + 4 G .. 16 + 4 G + 3: the S^T accumulator layout of the 16x16x32 MFMA,
+// which is also the key order of its B operand when P^T is packed in-lane.
+// The row max and row sum are in-lane reductions plus two lane swaps.
+//
+// Per tile j a wave runs two MFMA phases:
+//   1. S^T(j+1) = K_{j+1} Q^T (72 MFMAs, VGPR accumulators) while its VALU
+//      does the softmax of tile j and then rescales O^T tiles 0 .. 39 (by 1
+//      for rows whose max did not grow: the rescale runs every step);
+//   2. O^T += V_j^T P_j^T (64 MFMAs, AGPR accumulators) while its VALU
+//      rescales O^T tiles 40 .. 63 (each before its MFMA) and computes the
+//      gather offset of the next tile copy;
+// then it waits for its share of tile j+2's copies, passes the workgroup
+// barrier and starts the copy of tile j+4 into the slot tile j leaves.
+#include <stdint.h>
+
+#include "fa_asm.h"
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int DQK = 576, DV = 512;
+constexpr int TB = 32;                           // gathered keys per tile
+constexpr int NWAVE = 4;
+constexpr int CHK = DQK / 8;                     // 16-byte chunks per K row (72)
+constexpr int CHV = DV / 8;                      // ... per V row (64)
+constexpr int KCOPY = CHK / 8;                   // copy instructions per wave per K tile (9)
+constexpr int KSTEP = DQK / 32;                  // MFMA k-steps of S^T (18)
+constexpr int NKOP = 2 * KSTEP;                  // K operands per tile (2 key halves x 18)
+constexpr int NDT = DV / 16;                     // 16-row d tiles of O^T (32)
+constexpr uint32_t KTILE = TB * DQK * 2;         // bytes of a K tile
+constexpr uint32_t VTILE = TB * DV * 2;          // bytes of a V tile
+constexpr int LIST = 4096;                       // longest index row
+constexpr int KAHEAD = 3, KRING = KAHEAD + 1;    // K operands read ahead / their ring
+constexpr int VAHEAD = 3, VRING = VAHEAD + 1;    // V operands read ahead / their ring
+constexpr int EXP_GAPS = 8;                      // phase-1 MFMAs carrying the exponentials (a pair each)
+constexpr int RS_TILES = 2 * NDT;                // O^T accumulator tiles (64)
+constexpr int RS_P1 = 40;                        // tiles rescaled in phase 1
+constexpr int RS_GAPS_P2 = 40;                   // phase-2 MFMAs carrying the other tiles
+constexpr int PREP_AT = 48;                      // phase-2 MFMA after which the next gather offset is read
+
+static_assert(TB == 8 * NWAVE, "each wave copies 8 rows of a tile");
+static_assert(EXP_GAPS == 8, "8 score pairs per lane (2 head tiles x 2 key halves x 2)");
+// Phase-2 MFMA q reads tile q; the rescale of tile u >= RS_P1 is done in
+// phase-2 gap (u - RS_P1) * RS_GAPS_P2 / (RS_TILES - RS_P1) or earlier.
+static_assert(RS_GAPS_P2 <= RS_P1 + 1, "each O^T tile is rescaled before its phase-2 MFMA");
+
+// A ring slot holds a tile as 4 regions of 8 rows (RK bytes for K rows,
+// RV for V rows); region byte 1024 g + 128 r + 16 e is position e of the
+// 8-chunk group g of row r. Position e of row r in region w holds logical
+// chunk e ^ rsw(r, w) of its group: over the 16 rows 0..15 (or 16..31) of a
+// tile the pair (r % 2, rsw) takes 16 distinct values, so the 16 lanes of an
+// LDS read phase (16 rows, one chunk each) hit distinct banks.
+constexpr uint32_t RK = 8 * DQK * 2;  // 9216
+constexpr uint32_t RV = 8 * DV * 2;   // 8192
+__device__ __forceinline__ int rsw(int r, int w) { return (r >> 1) | ((w & 1) << 2); }
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x32 with the accumulator file chosen here: lane l holds
+// A[m = l % 16][k = 8 (l / 16) + e], B[k = 8 (l / 16) + e][n = l % 16] and
+// D[m = 4 (l / 16) + i][n = l % 16].
+template <class T>
+struct Mma16;
+template <>
+struct Mma16<BF16> {
+  static __device__ __forceinline__ void v0(f32x4& d, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void v(f32x4& d, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void a(f32x4& d, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  }
+};
+template <>
+struct Mma16<F16> {
+  static __device__ __forceinline__ void v0(f32x4& d, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void v(f32x4& d, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void a(f32x4& d, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  }
+};
+
+// Maximum / sum over the 4 lanes l % 16 + 16 G (G = 0..3) that hold one head:
+// v_permlane16_swap pairs l with l ^ 16, v_permlane32_swap l with l ^ 32 (with
+// both operands x, element 0 / 1 of the result hold own / partner values).
+__device__ __forceinline__ float quad_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return half_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return half_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+// Waits until at most n (0, KCOPY or 2 KCOPY) copies of this wave are in
+// flight; n is wave-uniform.
+__device__ __forceinline__ void wait_copies_below(int n) {
+  if (n >= 2 * KCOPY)
+    wait_vmem_below<2 * KCOPY>();
+  else if (n >= KCOPY)
+    wait_vmem_below<KCOPY>();
+  else
+    wait_vmem();
+}
+
+// Wait states between VALU writes of an accumulator tile and the MFMA that
+// reads it next; the writes are placed before this point.
+__device__ __forceinline__ void acc_written4(f32x4& a) { asm volatile("s_nop 4" : "+a"(a)); }
+
+template <class T, bool VALIAS>
+__device__ __forceinline__ void topk16_body(const TopkParams& p) {
+  using Mm = Mma16<T>;
+  constexpr int KR = VALIAS ? 4 : 2;  // K tile ring depth
+  constexpr uint32_t V_BASE = KR * KTILE;
+  constexpr uint32_t L_BASE = V_BASE + (VALIAS ? 0u : 2u * VTILE);
+  __shared__ __attribute__((aligned(16))) uint8_t s_mem[L_BASE + LIST * 4];
+  int* const s_list = (int*)(s_mem + L_BASE);
+  int* const s_wcount = (int*)s_mem;  // scan scratch; the ring is not in use yet
+  const uint32_t lds0 = lds_addr_of(s_mem);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = lane >> 4, n = lane & 15;
+  // Tokens in decreasing order: under a causal index pattern the late tokens
+  // have the longest lists and start first.
+  const int tb = (int)blockIdx.x / p.n_htiles;
+  const int t = p.T - 1 - tb;
+  const int head0 = ((int)blockIdx.x - tb * p.n_htiles) * 128 + w * 32;
+  const bool active = head0 < p.Hq;  // Hq is a multiple of 32
+
+  // Q^T operands (B operand of S^T): qop[ht][ks] = Q[t, head 16 ht + n,
+  // 32 ks + 8 G .. +7]. A wave past Hq computes on heads 0..31 and stores
+  // nothing.
+  u32x4 qop[2][KSTEP];
+  {
+    const uint16_t* qb =
+        (const uint16_t*)p.q + (int64_t)t * p.q_st + (int64_t)((active ? head0 : 0) + n) * p.q_sh + 8 * G;
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int ks = 0; ks < KSTEP; ++ks) qop[ht][ks] = *(const u32x4*)(qb + 16 * ht * p.q_sh + 32 * ks);
+  }
+
+  // Compact the valid indices of row t into s_list (list order kept):
+  // thread tid owns the slots [tid*spt, tid*spt + spt).
+  const int32_t* irow = p.idx + (int64_t)t * p.idx_st;
+  const int spt = (p.W + 255) / 256;
+  int cnt = 0;
+  for (int e = 0; e < spt; ++e) {
+    const int s = tid * spt + e;
+    if (s < p.W && irow[s] >= 0) ++cnt;
+  }
+  int incl = cnt;  // inclusive scan over the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) s_wcount[w] = incl;
+  __syncthreads();
+  int off = incl - cnt;
+  for (int ww = 0; ww < w; ++ww) off += s_wcount[ww];
+  const int n_valid = __builtin_amdgcn_readfirstlane(s_wcount[0] + s_wcount[1] + s_wcount[2] + s_wcount[3]);
+  for (int e = 0; e < spt; ++e) {
+    const int s = tid * spt + e;
+    if (s < p.W) {
+      const int x = irow[s];
+      if (x >= 0) s_list[off++] = x;
+    }
+  }
+  __syncthreads();
+  const int n_tiles = (n_valid + TB - 1) / TB;
+
+  // Gathers. Wave w copies rows 8 w .. 8 w + 7 of a tile into its region of
+  // the ring slot; lane l handles row 8 w + l / 8. Copy instruction g (one
+  // per 8-chunk group of a row) fills region bytes 1024 g + 16 l, which hold
+  // the row's logical chunk 8 g + (l % 8 ^ rsw(l / 8, w)).
+  const uint32_t krow = (uint32_t)p.k_ss * 2u;
+  const uint32_t vrow = (uint32_t)p.v_ss * 2u;
+  const uint32_t s_rows = (uint32_t)p.S;
+  const int crow = lane >> 3;
+  const uint32_t cchunk = (uint32_t)(((lane & 7) ^ rsw(crow, w)) << 4);
+  // Byte offset of a key row (an index past the last row reads the last row).
+  auto gather_base = [&](int tile, uint32_t row_bytes) __attribute__((always_inline)) {
+    const uint32_t key = (uint32_t)s_list[min(tile * TB + 8 * w + crow, n_valid - 1)];
+    return min(key, s_rows - 1) * row_bytes + cchunk;
+  };
+  uint32_t kbase;  // gather offset (group 0) of the next K copy
+  auto prep_k = [&](int tile) __attribute__((always_inline)) { kbase = gather_base(tile, krow); };
+  auto issue_k = [&](int tile) __attribute__((always_inline)) {
+    const uint32_t l0 = lds0 + (uint32_t)(tile % KR) * KTILE + (uint32_t)w * RK;
+#pragma unroll
+    for (int g = 0; g < KCOPY; ++g) lds_copy16(p.k, kbase + 128u * g, l0 + 1024u * g);
+  };
+  auto issue_v = [&](int tile) __attribute__((always_inline)) {
+    const uint32_t vb = gather_base(tile, vrow);
+    const uint32_t l0 = lds0 + V_BASE + (uint32_t)(tile & 1) * VTILE + (uint32_t)w * RV;
+#pragma unroll
+    for (int g = 0; g < CHV / 8; ++g) lds_copy16(p.v, vb + 128u * g, l0 + 1024u * g);
+  };
+
+  // K operand r = 2 ks + kt (A operand of S^T, key half kt, k-step ks): row
+  // 16 kt + n (region 2 kt + n / 8, row n % 8), logical chunk 4 ks + G (group
+  // ks / 2, position (4 (ks % 2) + G) ^ rsw), at byte
+  // koff[ks % 2] + 2 RK kt + 1024 (ks / 2) of the slot.
+  uint32_t koff[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    koff[par] = (uint32_t)((n >> 3) * RK + (n & 7) * 128 + (((4 * par + G) ^ rsw(n & 7, n >> 3)) << 4));
+  auto kread = [&](uint32_t tile_addr, int r) __attribute__((always_inline)) -> u32x4 {
+    const int kt = r & 1, ks = r >> 1;
+    const int imm = (kt * 2 * RK + (ks >> 1) * 1024) / 2;
+    return *(const __attribute__((address_space(3))) u32x4*)(lds_ptr(tile_addr + koff[ks & 1]) + imm);
+  };
+  // V^T operand dt (A operand of O^T += V^T P^T: d rows 16 dt + n, keys in
+  // the order of P^T), two ds_read_b64_tr_b16: lane l reads 4 consecutive
+  // elements of row vr (low half) or vr + 16 (high half) at column
+  // 16 dt + vc. Row vr is row vr % 8 of region vr / 8 (= G / 2); column
+  // 16 dt + vc is in logical chunk 2 dt + vc / 8 (group dt / 4). voff[dt % 4]
+  // + 1024 (dt / 4) is the low half's byte offset in the slot, + 2 RB the high
+  // half's.
+  constexpr uint32_t RB = VALIAS ? RK : RV;
+  const int vr = 4 * G + ((lane & 15) >> 2);
+  const int vc = 4 * (lane & 3);
+  uint32_t voff[4];
+#pragma unroll
+  for (int d4 = 0; d4 < 4; ++d4)
+    voff[d4] = (uint32_t)((G >> 1) * RB + (vr & 7) * 128 + (((2 * d4 + (vc >> 3)) ^ rsw(vr & 7, G >> 1)) << 4) +
+                          2 * (vc & 7));
+  auto vread = [&](uint32_t tile_addr, int dt) __attribute__((always_inline)) -> u32x4 {
+    const int imm = ((dt >> 2) * 1024) / 2;
+    const u32x2 lo = lds_read_tr16(lds_ptr(tile_addr + voff[dt & 3]) + imm);
+    const u32x2 hi = lds_read_tr16(lds_ptr(tile_addr + voff[dt & 3]) + imm + RB);
+    const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+    return v;
+  };
+  auto ktile = [&](int tile) __attribute__((always_inline)) { return lds0 + (uint32_t)(tile % KR) * KTILE; };
+  auto vtile = [&](int tile) __attribute__((always_inline)) {
+    return VALIAS ? ktile(tile) : lds0 + V_BASE + (uint32_t)(tile & 1) * VTILE;
+  };
+
+  // O^T accumulator tiles oacc[dt][ht]: d rows 16 dt + 4 G + i, head 16 ht + n.
+  f32x4 oacc[NDT][2];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      oacc[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc_written4(oacc[dt][ht]);  // O^T lives in AGPRs from here on
+    }
+  float m_run[2] = {-INFINITY, -INFINITY};  // running row max (exp2 domain)
+  float l_run[2] = {0.f, 0.f};              // row sum over this lane's keys
+  float alpha[2] = {1.f, 1.f};
+  u32x4 pop[2];                             // P^T operands of the tile between phases
+  u32x4 kq[KRING], vq[VRING];
+  f32x4 s0[2][2], s1[2][2];                 // [kt][ht] score tiles, alternately S(j), S(j+1)
+
+  // S^T MFMA x (0..71) of a tile into acc: K operand r = x / 2, head tile
+  // x % 2; operands read KAHEAD ahead.
+  auto s_mfma = [&](f32x4 (&acc)[2][2], uint32_t ta, int x) __attribute__((always_inline)) {
+    const int r = x >> 1, ht = x & 1, kt = r & 1, ks = r >> 1;
+    if (ht == 0 && r + KAHEAD < NKOP) kq[(r + KAHEAD) % KRING] = kread(ta, r + KAHEAD);
+    if (ks == 0)
+      Mm::v0(acc[kt][ht], kq[r % KRING], qop[ht][0]);
+    else
+      Mm::v(acc[kt][ht], kq[r % KRING], qop[ht][ks]);
+  };
+  auto s_chain = [&](f32x4 (&acc)[2][2], uint32_t ta) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < KAHEAD; ++r) kq[r] = kread(ta, r);
+#pragma unroll
+    for (int x = 0; x < 2 * NKOP; ++x) s_mfma(acc, ta, x);
+  };
+
+  // Rescale of O^T tile u = 2 dt + ht by alpha[ht]. The empty asm statements
+  // on the tile keep its reads, multiplies and writes at this point of the
+  // MFMA stream; the next MFMA on the tile comes at least 15 MFMAs later, far
+  // past the wait states a VALU write needs before an MFMA reads it.
+  auto rescale_tile = [&](int u) __attribute__((always_inline)) {
+    const int dt = u >> 1, ht = u & 1;
+    asm volatile("" : "+a"(oacc[dt][ht]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oacc[dt][ht][i] *= alpha[ht];
+    asm volatile("" : "+a"(oacc[dt][ht]));
+  };
+
+  // End of step j: this wave's copies of tile j+2 have landed, barrier, then
+  // the copies into the slots step j left.
+  auto end_step = [&](int j) __attribute__((always_inline)) {
+    if (VALIAS) {
+      wait_copies_below(j + 3 < n_tiles ? KCOPY : 0);
+      barrier_keep_copies();
+      if (j + 4 < n_tiles) issue_k(j + 4);
+    } else {
+      wait_vmem();
+      barrier_keep_copies();
+      if (j + 3 < n_tiles) issue_k(j + 3);
+      if (j + 2 < n_tiles) issue_v(j + 2);
+    }
+  };
+  auto next_k_copy = [&](int j) __attribute__((always_inline)) { return VALIAS ? j + 4 : j + 3; };
+
+  // Step j: softmax of tile j (scores sb), S^T of tile j+1 into sa, O^T +=
+  // V_j^T P_j^T. On the last step the S^T of the (absent) next tile reads a
+  // stale ring slot and is discarded.
+  auto step = [&](int j, f32x4 (&sb)[2][2], f32x4 (&sa)[2][2]) __attribute__((always_inline)) {
+    const uint32_t ta = ktile(j + 1);
+    const uint32_t tv = vtile(j);
+#pragma unroll
+    for (int r = 0; r < KAHEAD; ++r) kq[r] = kread(ta, r);
+    // The scores were complete one MFMA phase ago; order the reads here.
+    asm volatile("s_nop 0" : "+v"(sb[0][0]), "+v"(sb[0][1]), "+v"(sb[1][0]), "+v"(sb[1][1]));
+    // Only the last tile can be partial: keys past n_valid are masked.
+    const int nk = n_valid - j * TB;
+    if (nk < TB) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * kt + 4 * G + i >= nk) sb[kt][ht][i] = -INFINITY;
+    }
+    // Row max of each head (in-lane, then the 4 lanes of the head) and the
+    // running-max update: exact, so any growth moves m.
+    float m_new[2];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      float mq = max3(sb[0][ht][0], sb[0][ht][1], sb[0][ht][2]);
+      mq = max3(mq, sb[0][ht][3], sb[1][ht][0]);
+      mq = max3(mq, sb[1][ht][1], sb[1][ht][2]);
+      mq = fmaxf(mq, sb[1][ht][3]);
+      const float mx = quad_max(mq) * p.scale_log2;
+      const bool upd = mx > m_run[ht];
+      m_new[ht] = upd ? mx : m_run[ht];  // finite: every tile has a valid key
+      alpha[ht] = upd ? fast_exp2(m_run[ht] - m_new[ht]) : 1.f;
+      m_run[ht] = m_new[ht];
+    }
+    float rs[2] = {0.f, 0.f};
+    // Phase 1: S^T(j+1); MFMAs 0 .. EXP_GAPS - 1 carry the exponentials
+    // (one pair of scores each), the following ones the rescale of O^T tiles
+    // 0 .. RS_P1 - 1.
+#pragma unroll
+    for (int x = 0; x < 2 * NKOP; ++x) {
+      s_mfma(sa, ta, x);
+      if (x + VAHEAD >= 2 * NKOP) vq[x + VAHEAD - 2 * NKOP] = vread(tv, x + VAHEAD - 2 * NKOP);
+      if (x < EXP_GAPS) {
+        // head tile x % 2, scores e, e + 1 of it (e = 0, 2, 4, 6 over kt, i)
+        const int ht = x & 1, e = 2 * (x >> 1);
+        const int kt = e >> 2, i = e & 3;
+        const float x0 = fast_exp2(__builtin_fmaf(sb[kt][ht][i], p.scale_log2, -m_new[ht]));
+        const float x1 = fast_exp2(__builtin_fmaf(sb[kt][ht][i + 1], p.scale_log2, -m_new[ht]));
+        pop[ht][e >> 1] = T::pack2(x0, x1);
+        rs[ht] += x0 + x1;
+        asm volatile("" ::"v"(pop[ht][e >> 1]), "v"(rs[ht]));
+      } else {
+        constexpr int G1 = 2 * NKOP - EXP_GAPS;
+        const int g = x - EXP_GAPS;
+#pragma unroll
+        for (int u = (g * RS_P1 + G1 - 1) / G1; u < ((g + 1) * RS_P1 + G1 - 1) / G1; ++u) rescale_tile(u);
+      }
+    }
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) l_run[ht] = __builtin_fmaf(l_run[ht], alpha[ht], rs[ht]);
+    // Phase 2: O^T += V^T P^T, MFMA q: d tile q / 2, head tile q % 2.
+#pragma unroll
+    for (int q = 0; q < 2 * NDT; ++q) {
+      const int dt = q >> 1, ht = q & 1;
+      if (ht == 0 && dt + VAHEAD < NDT) vq[(dt + VAHEAD) % VRING] = vread(tv, dt + VAHEAD);
+      Mm::a(oacc[dt][ht], vq[dt % VRING], pop[ht]);
+      if (q < RS_GAPS_P2) {
+        constexpr int N2 = RS_TILES - RS_P1;
+#pragma unroll
+        for (int u = RS_P1 + (q * N2 + RS_GAPS_P2 - 1) / RS_GAPS_P2;
+             u < RS_P1 + ((q + 1) * N2 + RS_GAPS_P2 - 1) / RS_GAPS_P2; ++u)
+          rescale_tile(u);
+      }
+      if (q == PREP_AT) prep_k(next_k_copy(j));
+    }
+    end_step(j);
+  };
+
+  // Prologue: the first tiles in flight, S^T of tile 0.
+  if (n_tiles > 0) {
+    if (VALIAS) {
+      for (int i = 0; i < 3 && i < n_tiles; ++i) {
+        prep_k(i);
+        issue_k(i);
+      }
+      wait_copies_below((min(n_tiles, 3) - 1) * KCOPY);
+    } else {
+      prep_k(0);
+      issue_k(0);
+      if (n_tiles > 1) {
+        prep_k(1);
+        issue_k(1);
+      }
+      issue_v(0);
+      wait_vmem();
+    }
+    barrier_keep_copies();
+    s_chain(s0, ktile(0));
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0[0][0]), "+v"(s0[0][1]), "+v"(s0[1][0]), "+v"(s0[1][1]));
+    prep_k(next_k_copy(-1));
+    end_step(-1);
+  }
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(j, s0, s1);
+    if (j + 1 < n_tiles) step(j + 1, s1, s0);
+  }
+
+  // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l); no valid key -> 0 / -inf.
+#pragma unroll
+  for (int dt = 0; dt < NDT; dt += 2)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(oacc[dt][0]), "+a"(oacc[dt][1]), "+a"(oacc[dt + 1][0]), "+a"(oacc[dt + 1][1]));
+  if (active) {
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const float lt = quad_sum(l_run[ht]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const int head = head0 + 16 * ht + n;
+      uint16_t* orow = (uint16_t*)p.o + (int64_t)t * p.o_st + (int64_t)head * p.o_sh + 4 * G;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        u32x2 v;
+        v[0] = T::pack2(oacc[dt][ht][0] * inv, oacc[dt][ht][1] * inv);
+        v[1] = T::pack2(oacc[dt][ht][2] * inv, oacc[dt][ht][3] * inv);
+        *(u32x2*)(orow + 16 * dt) = v;
+      }
+      if (G == 0) p.lse[(int64_t)t * p.Hq + head] = lt > 0.f ? (m_run[ht] + log2f(lt)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace fa
+
+// Kernel entry points (names are looked up by the library at run time):
+// fa_topk16_<dtype>_v<1: V is the first 512 columns of K, 0: V of its own>.
+#define FA_TOPK16_KERNEL(TN, T, VA)                                                                   \
+  extern "C" __global__ void __launch_bounds__(256, 1) fa_topk16_##TN##_v##VA(const fa::TopkParams p) { \
+    fa::topk16_body<fa::T, VA != 0>(p);                                                                 \
+  }
+FA_TOPK16_KERNEL(bf16, BF16, 1)
+FA_TOPK16_KERNEL(bf16, BF16, 0)
+FA_TOPK16_KERNEL(f16, F16, 1)
+FA_TOPK16_KERNEL(f16, F16, 0)

@@ -154,11 +154,15 @@ fa_status fa_fwd_blocksparse(const fa_tensor* q, const fa_tensor* k, const fa_te
  *  v   [S, Dv] same dtype; may alias k (v.data == k.data with the same row
  *      stride, i.e. V = the first Dv columns of K, the MLA latent)
  *  idx int32 [T, W], last dim contiguous; idx[t, s] in [0, S) names a key,
- *      negative = unused slot (anywhere in the row)
+ *      negative = unused slot (anywhere in the row). An index >= S is not
+ *      detected; it reads key row S - 1 (never memory outside k or v).
  *  o   [T, Hq, Dv] in q's dtype (strided)
  *  lse fp32 [T, Hq], contiguous
  *
- * Supported: Dqk == 576, Dv == 512, Hq a multiple of 32, W <= 4096.
+ * Supported: Dqk == 576, Dv == 512, Hq a multiple of 32, W <= 4096, and k
+ * and v each spanning less than 4 GiB ((S - 1) * row stride + row length,
+ * in bytes: the gathers use 32-bit byte offsets). Rows with no valid index
+ * give O = 0 and LSE = -inf.
  */
 fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
                              const fa_tensor* idx, float scale, const fa_tensor* o,
