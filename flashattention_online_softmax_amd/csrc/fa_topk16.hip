@@ -15,19 +15,19 @@
 //
 // Decomposition (MI355X): one workgroup of 4 waves (one per SIMD) per token
 // and 128 query heads; wave w owns heads 32 w .. 32 w + 31 as two 16-head
-// tiles. The MFMAs are v_mfma_f32_16x16x32 (every accumulator is a 4-register
-// tile, so the O rescale can be spread over the MFMA stream one tile at a
-// time; every K or V operand read from LDS feeds both head tiles). Q^T
-// (576 x 32) stays in VGPRs as the B operand of S^T = K_g Q^T; O^T (512 x 32
-// fp32) fills the AGPRs. The valid entries of idx[t, :] are compacted into LDS
-// (list order kept, negative slots dropped); 32 consecutive list entries form
-// a tile whose key rows (1152 bytes each) are gathered from HBM/L2 straight
-// into LDS by global_load_lds_dwordx4 (no register staging; an index at or
-// past S reads the last row). When V is the first 512 columns of K (the MLA latent) the
+// tiles. The MFMAs are v_mfma_f32_16x16x32; every K or V operand read from
+// LDS feeds both head tiles. Q^T (576 x 32) stays in VGPRs as the B operand
+// of S^T = K_g Q^T; O^T (512 x 32 fp32) fills the AGPRs. The valid entries
+// of idx[t, :] are compacted into LDS (list order kept, negative slots
+// dropped); 32 consecutive list entries form a tile whose key rows (1152
+// bytes each) are gathered from HBM/L2 straight into LDS by
+// global_load_lds_dwordx4 (no register staging; an index at or past S reads
+// the last row). When V is the first 512 columns of K (the MLA latent) the
 // tiles live in a 4-deep ring and P.V reads V^T out of the gathered K rows
 // with ds_read_b64_tr_b16; otherwise K and V tiles have 2-deep rings of their
-// own. Only the last tile of a token can be partial: its padding rows repeat
-// a valid key and their scores are masked to -inf.
+// own. Only the last list tile can be partial: its padding rows repeat a
+// valid key and their scores are masked to -inf. Tiles are visited first,
+// last, then the rest in list order (see visit()).
 //
 // Lane l of a wave (G = l / 16, n = l % 16) owns heads 16 ht + n of the wave
 // (ht = 0, 1) and, of each 32-key tile, keys 4 G .. 4 G + 3 and
@@ -35,13 +35,13 @@
 // which is also the key order of its B operand when P^T is packed in-lane.
 // The row max and row sum are in-lane reductions plus two lane swaps.
 //
-// Per tile j a wave runs two MFMA phases:
+// Per visited tile j a wave runs two MFMA phases:
 //   1. S^T(j+1) = K_{j+1} Q^T (72 MFMAs, VGPR accumulators) while its VALU
-//      does the softmax of tile j and then rescales O^T tiles 0 .. 39 (by 1
-//      for rows whose max did not grow: the rescale runs every step);
+//      does the softmax of tile j and rescales O^T (in pieces of 4 tiles
+//      between the MFMAs; a 16-head tile whose row maxima all stayed is not
+//      touched);
 //   2. O^T += V_j^T P_j^T (64 MFMAs, AGPR accumulators) while its VALU
-//      rescales O^T tiles 40 .. 63 (each before its MFMA) and computes the
-//      gather offset of the next tile copy;
+//      computes the gather offset of the next tile copy;
 // then it waits for its share of tile j+2's copies, passes the workgroup
 // barrier and starts the copy of tile j+4 into the slot tile j leaves.
 #include <stdint.h>
@@ -68,26 +68,28 @@ constexpr int LIST = 4096;                       // longest index row
 constexpr int KAHEAD = 3, KRING = KAHEAD + 1;    // K operands read ahead / their ring
 constexpr int VAHEAD = 3, VRING = VAHEAD + 1;    // V operands read ahead / their ring
 constexpr int EXP_GAPS = 8;                      // phase-1 MFMAs carrying the exponentials (a pair each)
-constexpr int RS_TILES = 2 * NDT;                // O^T accumulator tiles (64)
-constexpr int RS_P1 = 40;                        // tiles rescaled in phase 1
-constexpr int RS_GAPS_P2 = 40;                   // phase-2 MFMAs carrying the other tiles
+constexpr int RS_TILES = 4;                      // O^T tiles per rescale piece
 constexpr int PREP_AT = 48;                      // phase-2 MFMA after which the next gather offset is read
 
 static_assert(TB == 8 * NWAVE, "each wave copies 8 rows of a tile");
 static_assert(EXP_GAPS == 8, "8 score pairs per lane (2 head tiles x 2 key halves x 2)");
-// Phase-2 MFMA q reads tile q; the rescale of tile u >= RS_P1 is done in
-// phase-2 gap (u - RS_P1) * RS_GAPS_P2 / (RS_TILES - RS_P1) or earlier.
-static_assert(RS_GAPS_P2 <= RS_P1 + 1, "each O^T tile is rescaled before its phase-2 MFMA");
+static_assert(EXP_GAPS + 2 * NDT / RS_TILES * 4 == 2 * NKOP, "rescale pieces fill phase 1");
 
 // A ring slot holds a tile as 4 regions of 8 rows (RK bytes for K rows,
 // RV for V rows); region byte 1024 g + 128 r + 16 e is position e of the
-// 8-chunk group g of row r. Position e of row r in region w holds logical
-// chunk e ^ rsw(r, w) of its group: over the 16 rows 0..15 (or 16..31) of a
-// tile the pair (r % 2, rsw) takes 16 distinct values, so the 16 lanes of an
-// LDS read phase (16 rows, one chunk each) hit distinct banks.
+// 8-chunk group g of row r (rows r and r + 2 share LDS banks, odd rows sit on
+// the other half of the banks). Position e of row r in region w holds
+// logical chunk e ^ rsw(r, w) of its group, rsw(r, w) = (r & 6) | (w & 1):
+//  * K operand reads (16 lanes = rows 0..15 or 16..31 of a tile, the same
+//    logical chunk): for each row parity, (r / 2, w % 2) -> rsw is one-to-one
+//    onto 0..7, so the 16 chunks fall on distinct banks;
+//  * V^T operand reads (16 lanes = 4 consecutive rows 4a .. 4a + 3 of one
+//    region, a chunk pair 2d, 2d + 1 each): rows 4a and 4a + 2 differ in bit
+//    1 of rsw, so they read different chunk pairs, and so do rows 4a and
+//    4a + 4 (bit 2) in the neighbouring lane group.
 constexpr uint32_t RK = 8 * DQK * 2;  // 9216
 constexpr uint32_t RV = 8 * DV * 2;   // 8192
-__device__ __forceinline__ int rsw(int r, int w) { return (r >> 1) | ((w & 1) << 2); }
+__device__ __forceinline__ int rsw(int r, int w) { return (r & 6) | (w & 1); }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -211,6 +213,13 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
   }
   __syncthreads();
   const int n_tiles = (n_valid + TB - 1) / TB;
+  // Retire the Q loads here, visibly to the compiler, before any copy is in
+  // flight: its wait for them would otherwise stay inside the loop and, as
+  // the copies count on the same counter, also wait for every copy.
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+    for (int ks = 0; ks < KSTEP; ++ks) asm volatile("" ::"v"(qop[ht][ks]));
 
   // Gathers. Wave w copies rows 8 w .. 8 w + 7 of a tile into its region of
   // the ring slot; lane l handles row 8 w + l / 8. Copy instruction g (one
@@ -222,20 +231,31 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
   const int crow = lane >> 3;
   const uint32_t cchunk = (uint32_t)(((lane & 7) ^ rsw(crow, w)) << 4);
   // Byte offset of a key row (an index past the last row reads the last row).
-  auto gather_base = [&](int tile, uint32_t row_bytes) __attribute__((always_inline)) {
-    const uint32_t key = (uint32_t)s_list[min(tile * TB + 8 * w + crow, n_valid - 1)];
+  // Visit order of the list tiles: the first, the last, then the others in
+  // list order. Index lists tend to hold their strongest key at one end (an
+  // indexer ranks keys best first; a causal list in key order ends with the
+  // token's own key), and meeting each row's maximum early makes later
+  // growth, each of which costs an exact rescale of O, rare. The running max
+  // stays exact in any order; only the rounding order of the sums changes.
+  auto visit = [&](int step) __attribute__((always_inline)) {
+    return step == 0 ? 0 : step == 1 ? n_tiles - 1 : step - 1;
+  };
+  // Gather offset of this lane's key row of the tile visited at `step` (steps
+  // past the last one read a valid row and are never used).
+  auto gather_base = [&](int step, uint32_t row_bytes) __attribute__((always_inline)) {
+    const uint32_t key = (uint32_t)s_list[min(visit(step) * TB + 8 * w + crow, n_valid - 1)];
     return min(key, s_rows - 1) * row_bytes + cchunk;
   };
   uint32_t kbase;  // gather offset (group 0) of the next K copy
-  auto prep_k = [&](int tile) __attribute__((always_inline)) { kbase = gather_base(tile, krow); };
-  auto issue_k = [&](int tile) __attribute__((always_inline)) {
-    const uint32_t l0 = lds0 + (uint32_t)(tile % KR) * KTILE + (uint32_t)w * RK;
+  auto prep_k = [&](int step) __attribute__((always_inline)) { kbase = gather_base(step, krow); };
+  auto issue_k = [&](int step) __attribute__((always_inline)) {
+    const uint32_t l0 = lds0 + (uint32_t)(step % KR) * KTILE + (uint32_t)w * RK;
 #pragma unroll
     for (int g = 0; g < KCOPY; ++g) lds_copy16(p.k, kbase + 128u * g, l0 + 1024u * g);
   };
-  auto issue_v = [&](int tile) __attribute__((always_inline)) {
-    const uint32_t vb = gather_base(tile, vrow);
-    const uint32_t l0 = lds0 + V_BASE + (uint32_t)(tile & 1) * VTILE + (uint32_t)w * RV;
+  auto issue_v = [&](int step) __attribute__((always_inline)) {
+    const uint32_t vb = gather_base(step, vrow);
+    const uint32_t l0 = lds0 + V_BASE + (uint32_t)(step & 1) * VTILE + (uint32_t)w * RV;
 #pragma unroll
     for (int g = 0; g < CHV / 8; ++g) lds_copy16(p.v, vb + 128u * g, l0 + 1024u * g);
   };
@@ -275,9 +295,9 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
     const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
     return v;
   };
-  auto ktile = [&](int tile) __attribute__((always_inline)) { return lds0 + (uint32_t)(tile % KR) * KTILE; };
-  auto vtile = [&](int tile) __attribute__((always_inline)) {
-    return VALIAS ? ktile(tile) : lds0 + V_BASE + (uint32_t)(tile & 1) * VTILE;
+  auto ktile = [&](int step) __attribute__((always_inline)) { return lds0 + (uint32_t)(step % KR) * KTILE; };
+  auto vtile = [&](int step) __attribute__((always_inline)) {
+    return VALIAS ? ktile(step) : lds0 + V_BASE + (uint32_t)(step & 1) * VTILE;
   };
 
   // O^T accumulator tiles oacc[dt][ht]: d rows 16 dt + 4 G + i, head 16 ht + n.
@@ -313,16 +333,22 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
     for (int x = 0; x < 2 * NKOP; ++x) s_mfma(acc, ta, x);
   };
 
-  // Rescale of O^T tile u = 2 dt + ht by alpha[ht]. The empty asm statements
-  // on the tile keep its reads, multiplies and writes at this point of the
-  // MFMA stream; the next MFMA on the tile comes at least 15 MFMAs later, far
-  // past the wait states a VALU write needs before an MFMA reads it.
-  auto rescale_tile = [&](int u) __attribute__((always_inline)) {
-    const int dt = u >> 1, ht = u & 1;
-    asm volatile("" : "+a"(oacc[dt][ht]));
+  // Rescale piece (ht, dt0): O^T tiles dt0 .. dt0 + RS_TILES - 1 of head tile
+  // ht, each lane by its head's alpha. Skipped unless one of the tile's 16
+  // heads' max grew (rescale_ht[ht]): with the exact running max the rescale
+  // happens whenever a row max grows, and only then. The next MFMA reading
+  // these tiles is in phase 2, many instructions later, past the wait states
+  // a VALU write needs before an MFMA reads it.
+  bool rescale_ht[2] = {false, false};
+  auto rescale_piece = [&](int ht, int dt0) __attribute__((always_inline)) {
+    if (rescale_ht[ht]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) oacc[dt][ht][i] *= alpha[ht];
-    asm volatile("" : "+a"(oacc[dt][ht]));
+      for (int dt = dt0; dt < dt0 + RS_TILES; ++dt) {
+        asm volatile("" : "+a"(oacc[dt][ht]));
+        oacc[dt][ht] *= alpha[ht];
+        asm volatile("" : "+a"(oacc[dt][ht]));
+      }
+    }
   };
 
   // End of step j: this wave's copies of tile j+2 have landed, barrier, then
@@ -351,8 +377,8 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
     for (int r = 0; r < KAHEAD; ++r) kq[r] = kread(ta, r);
     // The scores were complete one MFMA phase ago; order the reads here.
     asm volatile("s_nop 0" : "+v"(sb[0][0]), "+v"(sb[0][1]), "+v"(sb[1][0]), "+v"(sb[1][1]));
-    // Only the last tile can be partial: keys past n_valid are masked.
-    const int nk = n_valid - j * TB;
+    // Only the last list tile can be partial: keys past n_valid are masked.
+    const int nk = n_valid - visit(j) * TB;
     if (nk < TB) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -376,31 +402,62 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
       m_new[ht] = upd ? mx : m_run[ht];  // finite: every tile has a valid key
       alpha[ht] = upd ? fast_exp2(m_run[ht] - m_new[ht]) : 1.f;
       m_run[ht] = m_new[ht];
+      rescale_ht[ht] = j > 0 && __builtin_amdgcn_ballot_w64(upd) != 0;  // O is zero at j = 0
     }
     float rs[2] = {0.f, 0.f};
     // Phase 1: S^T(j+1); MFMAs 0 .. EXP_GAPS - 1 carry the exponentials
-    // (one pair of scores each), the following ones the rescale of O^T tiles
-    // 0 .. RS_P1 - 1.
+    // (one pair of scores each); rescale piece k (head tile k % 2, d tiles
+    // RS_TILES (k / 2) ..) goes before MFMAs EXP_GAPS + 4 k .. + 3.
+    auto seg = [&](int x0, int x1) __attribute__((always_inline)) {
 #pragma unroll
-    for (int x = 0; x < 2 * NKOP; ++x) {
-      s_mfma(sa, ta, x);
-      if (x + VAHEAD >= 2 * NKOP) vq[x + VAHEAD - 2 * NKOP] = vread(tv, x + VAHEAD - 2 * NKOP);
-      if (x < EXP_GAPS) {
-        // head tile x % 2, scores e, e + 1 of it (e = 0, 2, 4, 6 over kt, i)
-        const int ht = x & 1, e = 2 * (x >> 1);
-        const int kt = e >> 2, i = e & 3;
-        const float x0 = fast_exp2(__builtin_fmaf(sb[kt][ht][i], p.scale_log2, -m_new[ht]));
-        const float x1 = fast_exp2(__builtin_fmaf(sb[kt][ht][i + 1], p.scale_log2, -m_new[ht]));
-        pop[ht][e >> 1] = T::pack2(x0, x1);
-        rs[ht] += x0 + x1;
-        asm volatile("" ::"v"(pop[ht][e >> 1]), "v"(rs[ht]));
-      } else {
-        constexpr int G1 = 2 * NKOP - EXP_GAPS;
-        const int g = x - EXP_GAPS;
-#pragma unroll
-        for (int u = (g * RS_P1 + G1 - 1) / G1; u < ((g + 1) * RS_P1 + G1 - 1) / G1; ++u) rescale_tile(u);
+      for (int x = x0; x < x1; ++x) {
+        s_mfma(sa, ta, x);
+        if (x + VAHEAD >= 2 * NKOP) vq[x + VAHEAD - 2 * NKOP] = vread(tv, x + VAHEAD - 2 * NKOP);
+        if (x < EXP_GAPS) {
+          // head tile x % 2, scores e, e + 1 of it (e = 0, 2, 4, 6 over kt, i)
+          const int ht = x & 1, e = 2 * (x >> 1);
+          const int kt = e >> 2, i = e & 3;
+          const float x0 = fast_exp2(__builtin_fmaf(sb[kt][ht][i], p.scale_log2, -m_new[ht]));
+          const float x1 = fast_exp2(__builtin_fmaf(sb[kt][ht][i + 1], p.scale_log2, -m_new[ht]));
+          pop[ht][e >> 1] = T::pack2(x0, x1);
+          rs[ht] += x0 + x1;
+          asm volatile("" ::"v"(pop[ht][e >> 1]), "v"(rs[ht]));
+        }
       }
-    }
+    };
+    seg(0, EXP_GAPS);
+    rescale_piece(0, 0);
+    seg(EXP_GAPS + 0, EXP_GAPS + 4);
+    rescale_piece(1, 0);
+    seg(EXP_GAPS + 4, EXP_GAPS + 8);
+    rescale_piece(0, 4);
+    seg(EXP_GAPS + 8, EXP_GAPS + 12);
+    rescale_piece(1, 4);
+    seg(EXP_GAPS + 12, EXP_GAPS + 16);
+    rescale_piece(0, 8);
+    seg(EXP_GAPS + 16, EXP_GAPS + 20);
+    rescale_piece(1, 8);
+    seg(EXP_GAPS + 20, EXP_GAPS + 24);
+    rescale_piece(0, 12);
+    seg(EXP_GAPS + 24, EXP_GAPS + 28);
+    rescale_piece(1, 12);
+    seg(EXP_GAPS + 28, EXP_GAPS + 32);
+    rescale_piece(0, 16);
+    seg(EXP_GAPS + 32, EXP_GAPS + 36);
+    rescale_piece(1, 16);
+    seg(EXP_GAPS + 36, EXP_GAPS + 40);
+    rescale_piece(0, 20);
+    seg(EXP_GAPS + 40, EXP_GAPS + 44);
+    rescale_piece(1, 20);
+    seg(EXP_GAPS + 44, EXP_GAPS + 48);
+    rescale_piece(0, 24);
+    seg(EXP_GAPS + 48, EXP_GAPS + 52);
+    rescale_piece(1, 24);
+    seg(EXP_GAPS + 52, EXP_GAPS + 56);
+    rescale_piece(0, 28);
+    seg(EXP_GAPS + 56, EXP_GAPS + 60);
+    rescale_piece(1, 28);
+    seg(EXP_GAPS + 60, EXP_GAPS + 64);
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) l_run[ht] = __builtin_fmaf(l_run[ht], alpha[ht], rs[ht]);
     // Phase 2: O^T += V^T P^T, MFMA q: d tile q / 2, head tile q % 2.
@@ -409,13 +466,6 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
       const int dt = q >> 1, ht = q & 1;
       if (ht == 0 && dt + VAHEAD < NDT) vq[(dt + VAHEAD) % VRING] = vread(tv, dt + VAHEAD);
       Mm::a(oacc[dt][ht], vq[dt % VRING], pop[ht]);
-      if (q < RS_GAPS_P2) {
-        constexpr int N2 = RS_TILES - RS_P1;
-#pragma unroll
-        for (int u = RS_P1 + (q * N2 + RS_GAPS_P2 - 1) / RS_GAPS_P2;
-             u < RS_P1 + ((q + 1) * N2 + RS_GAPS_P2 - 1) / RS_GAPS_P2; ++u)
-          rescale_tile(u);
-      }
       if (q == PREP_AT) prep_k(next_k_copy(j));
     }
     end_step(j);
