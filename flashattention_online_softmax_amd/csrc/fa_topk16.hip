@@ -37,9 +37,8 @@
 //
 // Per visited tile j a wave runs two MFMA phases:
 //   1. S^T(j+1) = K_{j+1} Q^T (72 MFMAs, VGPR accumulators) while its VALU
-//      does the softmax of tile j and rescales O^T (in pieces of 4 tiles
-//      between the MFMAs; a 16-head tile whose row maxima all stayed is not
-//      touched);
+//      does the softmax of tile j; when a row max grew, the O^T tiles of its
+//      16-head tile are rescaled;
 //   2. O^T += V_j^T P_j^T (64 MFMAs, AGPR accumulators) while its VALU
 //      computes the gather offset of the next tile copy;
 // then it waits for its share of tile j+2's copies, passes the workgroup
@@ -65,15 +64,13 @@ constexpr int NDT = DV / 16;                     // 16-row d tiles of O^T (32)
 constexpr uint32_t KTILE = TB * DQK * 2;         // bytes of a K tile
 constexpr uint32_t VTILE = TB * DV * 2;          // bytes of a V tile
 constexpr int LIST = 4096;                       // longest index row
-constexpr int KAHEAD = 3, KRING = KAHEAD + 1;    // K operands read ahead / their ring
-constexpr int VAHEAD = 3, VRING = VAHEAD + 1;    // V operands read ahead / their ring
+constexpr int NOPS = NKOP + DV / 16;             // LDS operands per step: 36 K, then 32 V
+constexpr int AHEAD = 6, RING = 8;               // operands read ahead / their ring
 constexpr int EXP_GAPS = 8;                      // phase-1 MFMAs carrying the exponentials (a pair each)
-constexpr int RS_TILES = 4;                      // O^T tiles per rescale piece
 constexpr int PREP_AT = 48;                      // phase-2 MFMA after which the next gather offset is read
 
 static_assert(TB == 8 * NWAVE, "each wave copies 8 rows of a tile");
 static_assert(EXP_GAPS == 8, "8 score pairs per lane (2 head tiles x 2 key halves x 2)");
-static_assert(EXP_GAPS + 2 * NDT / RS_TILES * 4 == 2 * NKOP, "rescale pieces fill phase 1");
 
 // A ring slot holds a tile as 4 regions of 8 rows (RK bytes for K rows,
 // RV for V rows); region byte 1024 g + 128 r + 16 e is position e of the
@@ -313,37 +310,52 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
   float l_run[2] = {0.f, 0.f};              // row sum over this lane's keys
   float alpha[2] = {1.f, 1.f};
   u32x4 pop[2];                             // P^T operands of the tile between phases
-  u32x4 kq[KRING], vq[VRING];
   f32x4 s0[2][2], s1[2][2];                 // [kt][ht] score tiles, alternately S(j), S(j+1)
 
-  // S^T MFMA x (0..71) of a tile into acc: K operand r = x / 2, head tile
-  // x % 2; operands read KAHEAD ahead.
-  auto s_mfma = [&](f32x4 (&acc)[2][2], uint32_t ta, int x) __attribute__((always_inline)) {
-    const int r = x >> 1, ht = x & 1, kt = r & 1, ks = r >> 1;
-    if (ht == 0 && r + KAHEAD < NKOP) kq[(r + KAHEAD) % KRING] = kread(ta, r + KAHEAD);
-    if (ks == 0)
-      Mm::v0(acc[kt][ht], kq[r % KRING], qop[ht][0]);
-    else
-      Mm::v(acc[kt][ht], kq[r % KRING], qop[ht][ks]);
-  };
-  auto s_chain = [&](f32x4 (&acc)[2][2], uint32_t ta) __attribute__((always_inline)) {
-#pragma unroll
-    for (int r = 0; r < KAHEAD; ++r) kq[r] = kread(ta, r);
-#pragma unroll
-    for (int x = 0; x < 2 * NKOP; ++x) s_mfma(acc, ta, x);
+  // The LDS operands of a step, u = 0 .. NOPS-1 (K operands of phase 1, then
+  // V operands of phase 2), stream through one ring read AHEAD operands
+  // ahead; operand u of a step of parity par sits in slot (u + NOPS par) % RING
+  // (steps alternate parity, so every slot index is a compile-time constant).
+  u32x4 op[RING];
+  auto slot = [&](int par, int u) __attribute__((always_inline)) { return (u + NOPS * par) % RING; };
+  auto read_op = [&](int par, int u, uint32_t ta, uint32_t tv) __attribute__((always_inline)) {
+    if (u < NKOP)
+      op[slot(par, u)] = kread(ta, u);
+    else if (u < NOPS)
+      op[slot(par, u)] = vread(tv, u - NKOP);
   };
 
-  // Rescale piece (ht, dt0): O^T tiles dt0 .. dt0 + RS_TILES - 1 of head tile
-  // ht, each lane by its head's alpha. Skipped unless one of the tile's 16
-  // heads' max grew (rescale_ht[ht]): with the exact running max the rescale
-  // happens whenever a row max grows, and only then. The next MFMA reading
-  // these tiles is in phase 2, many instructions later, past the wait states
-  // a VALU write needs before an MFMA reads it.
+  // S^T MFMA x (0..71) of a tile into acc: K operand u = x / 2, head tile
+  // x % 2. With v_ops, the read-ahead runs on into the V operands of tv.
+  auto s_mfma = [&](f32x4 (&acc)[2][2], int par, uint32_t ta, uint32_t tv, bool v_ops, int x)
+                    __attribute__((always_inline)) {
+    const int u = x >> 1, ht = x & 1, kt = u & 1, ks = u >> 1;
+    if (ht == 0 && (u + AHEAD < NKOP || v_ops)) read_op(par, u + AHEAD, ta, tv);
+    if (ks == 0)
+      Mm::v0(acc[kt][ht], op[slot(par, u)], qop[ht][0]);
+    else
+      Mm::v(acc[kt][ht], op[slot(par, u)], qop[ht][ks]);
+  };
+  // S^T of the first tile (the prologue, parity of step -1).
+  auto s_chain = [&](f32x4 (&acc)[2][2], uint32_t ta) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < AHEAD; ++u) read_op(1, u, ta, 0);
+#pragma unroll
+    for (int x = 0; x < 2 * NKOP; ++x) s_mfma(acc, 1, ta, 0, false, x);
+  };
+
+  // Rescale of the O^T tiles of head tile ht, each lane by its head's alpha,
+  // when one of the tile's 16 row maxima grew (rescale_ht[ht]): with the
+  // exact running max every growth rescales, and nothing else does. The empty
+  // asm statements keep one tile's reads, multiplies and writes together
+  // (unfenced, the compiler would hold all products in VGPRs at once). The
+  // next MFMA reading these tiles is in phase 2, many instructions later, past
+  // the wait states a VALU write needs before an MFMA reads it.
   bool rescale_ht[2] = {false, false};
-  auto rescale_piece = [&](int ht, int dt0) __attribute__((always_inline)) {
+  auto rescale_tiles = [&](int ht) __attribute__((always_inline)) {
     if (rescale_ht[ht]) {
 #pragma unroll
-      for (int dt = dt0; dt < dt0 + RS_TILES; ++dt) {
+      for (int dt = 0; dt < NDT; ++dt) {
         asm volatile("" : "+a"(oacc[dt][ht]));
         oacc[dt][ht] *= alpha[ht];
         asm volatile("" : "+a"(oacc[dt][ht]));
@@ -370,11 +382,11 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
   // Step j: softmax of tile j (scores sb), S^T of tile j+1 into sa, O^T +=
   // V_j^T P_j^T. On the last step the S^T of the (absent) next tile reads a
   // stale ring slot and is discarded.
-  auto step = [&](int j, f32x4 (&sb)[2][2], f32x4 (&sa)[2][2]) __attribute__((always_inline)) {
+  auto step = [&](int j, f32x4 (&sb)[2][2], f32x4 (&sa)[2][2], int par) __attribute__((always_inline)) {
     const uint32_t ta = ktile(j + 1);
     const uint32_t tv = vtile(j);
 #pragma unroll
-    for (int r = 0; r < KAHEAD; ++r) kq[r] = kread(ta, r);
+    for (int u = 0; u < AHEAD; ++u) read_op(par, u, ta, tv);
     // The scores were complete one MFMA phase ago; order the reads here.
     asm volatile("s_nop 0" : "+v"(sb[0][0]), "+v"(sb[0][1]), "+v"(sb[1][0]), "+v"(sb[1][1]));
     // Only the last list tile can be partial: keys past n_valid are masked.
@@ -406,13 +418,11 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
     }
     float rs[2] = {0.f, 0.f};
     // Phase 1: S^T(j+1); MFMAs 0 .. EXP_GAPS - 1 carry the exponentials
-    // (one pair of scores each); rescale piece k (head tile k % 2, d tiles
-    // RS_TILES (k / 2) ..) goes before MFMAs EXP_GAPS + 4 k .. + 3.
+    // (one pair of scores each), then the rescale of O^T if a max grew.
     auto seg = [&](int x0, int x1) __attribute__((always_inline)) {
 #pragma unroll
       for (int x = x0; x < x1; ++x) {
-        s_mfma(sa, ta, x);
-        if (x + VAHEAD >= 2 * NKOP) vq[x + VAHEAD - 2 * NKOP] = vread(tv, x + VAHEAD - 2 * NKOP);
+        s_mfma(sa, par, ta, tv, true, x);
         if (x < EXP_GAPS) {
           // head tile x % 2, scores e, e + 1 of it (e = 0, 2, 4, 6 over kt, i)
           const int ht = x & 1, e = 2 * (x >> 1);
@@ -426,46 +436,22 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
       }
     };
     seg(0, EXP_GAPS);
-    rescale_piece(0, 0);
-    seg(EXP_GAPS + 0, EXP_GAPS + 4);
-    rescale_piece(1, 0);
-    seg(EXP_GAPS + 4, EXP_GAPS + 8);
-    rescale_piece(0, 4);
-    seg(EXP_GAPS + 8, EXP_GAPS + 12);
-    rescale_piece(1, 4);
-    seg(EXP_GAPS + 12, EXP_GAPS + 16);
-    rescale_piece(0, 8);
-    seg(EXP_GAPS + 16, EXP_GAPS + 20);
-    rescale_piece(1, 8);
-    seg(EXP_GAPS + 20, EXP_GAPS + 24);
-    rescale_piece(0, 12);
-    seg(EXP_GAPS + 24, EXP_GAPS + 28);
-    rescale_piece(1, 12);
-    seg(EXP_GAPS + 28, EXP_GAPS + 32);
-    rescale_piece(0, 16);
-    seg(EXP_GAPS + 32, EXP_GAPS + 36);
-    rescale_piece(1, 16);
-    seg(EXP_GAPS + 36, EXP_GAPS + 40);
-    rescale_piece(0, 20);
-    seg(EXP_GAPS + 40, EXP_GAPS + 44);
-    rescale_piece(1, 20);
-    seg(EXP_GAPS + 44, EXP_GAPS + 48);
-    rescale_piece(0, 24);
-    seg(EXP_GAPS + 48, EXP_GAPS + 52);
-    rescale_piece(1, 24);
-    seg(EXP_GAPS + 52, EXP_GAPS + 56);
-    rescale_piece(0, 28);
-    seg(EXP_GAPS + 56, EXP_GAPS + 60);
-    rescale_piece(1, 28);
-    seg(EXP_GAPS + 60, EXP_GAPS + 64);
+    // Rare once the row maxima are met (see visit()): one branch, laid out of
+    // line, keeps the common path free of taken jumps.
+    if (__builtin_expect(rescale_ht[0] || rescale_ht[1], 0)) {
+      rescale_tiles(0);
+      rescale_tiles(1);
+    }
+    seg(EXP_GAPS, 2 * NKOP);
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) l_run[ht] = __builtin_fmaf(l_run[ht], alpha[ht], rs[ht]);
-    // Phase 2: O^T += V^T P^T, MFMA q: d tile q / 2, head tile q % 2.
+    // Phase 2: O^T += V^T P^T, MFMA q: d tile q / 2 (operand NKOP + q / 2),
+    // head tile q % 2.
 #pragma unroll
     for (int q = 0; q < 2 * NDT; ++q) {
-      const int dt = q >> 1, ht = q & 1;
-      if (ht == 0 && dt + VAHEAD < NDT) vq[(dt + VAHEAD) % VRING] = vread(tv, dt + VAHEAD);
-      Mm::a(oacc[dt][ht], vq[dt % VRING], pop[ht]);
+      const int dt = q >> 1, ht = q & 1, u = NKOP + dt;
+      if (ht == 0) read_op(par, u + AHEAD, ta, tv);
+      Mm::a(oacc[dt][ht], op[slot(par, u)], pop[ht]);
       if (q == PREP_AT) prep_k(next_k_copy(j));
     }
     end_step(j);
@@ -496,8 +482,8 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
     end_step(-1);
   }
   for (int j = 0; j < n_tiles; j += 2) {
-    step(j, s0, s1);
-    if (j + 1 < n_tiles) step(j + 1, s1, s0);
+    step(j, s0, s1, 0);
+    if (j + 1 < n_tiles) step(j + 1, s1, s0, 1);
   }
 
   // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l); no valid key -> 0 / -inf.
