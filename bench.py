@@ -269,6 +269,7 @@ def main():
             torch.cuda.empty_cache()
         log("secondary topk_mla_bf16_t4096")
         w5 = synth.workload("topk_mla_bf16_t4096")
+        topk_traffic = measured_traffic("topk_mla_bf16_t4096")
         for order in ("idx_a", "idx_b"):
             fl, nb = topk_work(w5, w5[order])
             c5 = make_call(w5, order)
@@ -276,7 +277,7 @@ def main():
             sec["topk_mla_bf16_t4096_" + ("self_first" if order == "idx_a" else "self_last")] = {
                 "gbs": round(nb / (km * 1e-3) / 1e9, 1), "tflops": round(fl / (km * 1e-3) / 1e12, 2),
                 "kernel_ms": round(km, 4), "frac_hbm_peak": round(nb / (km * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                "algorithmic_bytes": nb}
+                "algorithmic_bytes": nb, "traffic": topk_traffic}
             del c5
         del w5
         torch.cuda.empty_cache()
