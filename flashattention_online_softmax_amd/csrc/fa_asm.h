@@ -144,8 +144,13 @@ struct Mma<F16> {
 // instruction touching it (more than the 8-pass MFMA needs). The registers
 // are operands of the wait so that the compiler places every access to them
 // after it.
-__device__ __forceinline__ void mfma_wait_v(f32x16 (&a)[2]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a[0]), "+v"(a[1]));
+template <int N>
+__device__ __forceinline__ void mfma_wait_v(f32x16 (&a)[N]) {
+  static_assert(N == 1 || N == 2, "score tiles");
+  if constexpr (N == 2)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a[0]), "+v"(a[1]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a[0]));
 }
 template <int N>
 __device__ __forceinline__ void mfma_wait_a(f32x16 (&a)[N]) {

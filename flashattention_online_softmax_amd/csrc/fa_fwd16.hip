@@ -42,66 +42,13 @@
 #include <type_traits>
 
 #include "fa_asm.h"
+#include "fa_copy.h"
 #include "fa_device.h"
 #include "fa_internal.h"
 #include "fa_tiles.h"
 
 namespace fa {
 namespace {
-
-// Copies of 64-key tiles (rows kstart .. kstart+63 of one K or V head) into
-// LDS buffers of 64 rows x D elements stored with the 16-byte chunk swizzle.
-// One copy instruction fills 64 consecutive chunks (1 KB) of LDS, lane i
-// chunk 64n + i, so each lane fetches the logical chunk the swizzle keeps at
-// that position (the XOR is an involution). The per-lane byte offset inside a
-// tile is the same for every tile and is computed once. On the last, partial
-// tile, rows at or past Lk fetch row Lk - 1 instead (finite data whose scores
-// are masked), so nothing past the valid keys is ever read.
-template <int D, int NW, bool IS_V>
-struct TileCopy {
-  static constexpr int CH = D / 8;
-  static constexpr int NINST = BN * CH / 64;
-  static constexpr int PER_WAVE = NINST / NW;
-  static_assert(NINST % NW == 0, "tile copy must divide evenly over the waves");
-  const char* g;       // head base
-  uint32_t row_bytes;  // row stride in bytes (the library keeps it below 2^24)
-  uint32_t off[PER_WAVE];
-
-  __device__ __forceinline__ static int pos(int j) {
-    return (((int)threadIdx.x >> 6) * PER_WAVE + j) * 64 + ((int)threadIdx.x & 63);
-  }
-  __device__ __forceinline__ static int chunk_row(int j) { return pos(j) / CH; }
-  __device__ __forceinline__ static uint32_t chunk_col_bytes(int j) {
-    const int row = pos(j) / CH, ph = pos(j) % CH;
-    return (uint32_t)((ph ^ (IS_V ? vswz<D>(row) : kswz<D>(row))) * 16);
-  }
-
-  // head is the same in every lane of the wave.
-  __device__ __forceinline__ TileCopy(const uint16_t* head, int64_t row_stride)
-      : g(uniform_ptr(head)), row_bytes((uint32_t)row_stride * 2u) {
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) off[j] = (uint32_t)chunk_row(j) * row_bytes + chunk_col_bytes(j);
-  }
-
-  // kstart, Lk and lds are the same in every lane of the wave.
-  __device__ __forceinline__ void issue(int kstart, int Lk, const uint16_t* lds) const {
-    kstart = __builtin_amdgcn_readfirstlane(kstart);
-    const uint32_t l0 = __builtin_amdgcn_readfirstlane(
-        lds_addr_of(lds) + (((int)threadIdx.x >> 6) * PER_WAVE) * 1024);
-    const char* base = g + (int64_t)kstart * row_bytes;
-    if (kstart + BN <= Lk) {
-#pragma unroll
-      for (int j = 0; j < PER_WAVE; ++j) lds_copy16(base, off[j], l0 + j * 1024);
-    } else {
-      const int last = Lk - 1 - kstart;
-#pragma unroll
-      for (int j = 0; j < PER_WAVE; ++j) {
-        const int over = max(chunk_row(j) - last, 0);
-        lds_copy16(base, off[j] - (uint32_t)over * row_bytes, l0 + j * 1024);
-      }
-    }
-  }
-};
 
 // Per 64-key tile j a wave (QT blocks of 32 query rows; every K/V operand it
 // reads serves all of them) has a VALU phase V(j) and an MFMA phase M(j):
@@ -133,8 +80,10 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   constexpr int RING = AHEAD + 1;
   static_assert(!SPARSE || MPH == 128, "block-sparse needs 128 query rows per head");
 
-  __shared__ __attribute__((aligned(16))) uint16_t s_kring[3 * TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vring[3 * TILE];
+  // K ring (3 tiles) then V ring (3 tiles); the epilogue reuses the space.
+  __shared__ __attribute__((aligned(16))) uint16_t s_ring[6 * TILE];
+  uint16_t* const s_kring = s_ring;
+  uint16_t* const s_vring = s_ring + 3 * TILE;
   __shared__ int s_kstart[SPARSE ? 512 : 1];
   __shared__ int s_n;
 
@@ -165,19 +114,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   const uint16_t* kg = (const uint16_t*)p.k + wk.b * p.k_sb + wk.hkv * p.k_sh;
   const uint16_t* vg = (const uint16_t*)p.v + wk.b * p.v_sb + wk.hkv * p.v_sh;
 
-  // Q^T operands (B operand of S^T = K Q^T, kept in AGPRs): block b, lane
-  // holds Q[row0 + 32 b + c][16 ds + 8 h .. +7].
-  u32x4 qop[QT][DS];
-#pragma unroll
-  for (int b = 0; b < QT; ++b) {
-    const int qrow = wk.row0 + 32 * b + c;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (qrow < p.Sq) z = *(const u32x4*)(qg + (int64_t)qrow * p.q_ss + 16 * ds + 8 * h);
-      qop[b][ds] = z;
-    }
-  }
+  u32x4 qop[QT][DS];  // Q^T operands, loaded after the first tile copies
 
   f32x16 oacc[QT][DT];
 #pragma unroll
@@ -439,6 +376,19 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     vcopy.issue(tile_start(1), wk.Lk, s_vring + TILE);
   }
   if (n_iter > 2) kcopy.issue(tile_start(2), wk.Lk, s_kring + 2 * TILE);
+  // Q^T operands (B operand of S^T = K Q^T, kept in AGPRs): block b, lane
+  // holds Q[row0 + 32 b + c][16 ds + 8 h .. +7]. Loaded after the copies are
+  // issued so that both latencies overlap.
+#pragma unroll
+  for (int b = 0; b < QT; ++b) {
+    const int qrow = wk.row0 + 32 * b + c;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (qrow < p.Sq) z = *(const u32x4*)(qg + (int64_t)qrow * p.q_ss + 16 * ds + 8 * h);
+      qop[b][ds] = z;
+    }
+  }
   // Make the compiler wait for the Q loads here, once: it does not see the
   // copies above, and otherwise would wait for its Q loads (vmcnt(0), which
   // drains copies in flight) at their first use inside the loop.
@@ -489,29 +439,47 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   }
   if (grp == 0) end_phase(false);
 
-  // Epilogue.
+  // Epilogue: O = acc / l rounded to the output dtype, staged through LDS
+  // (free now: every wave is past its last ring read and copy) so that each
+  // store instruction writes whole rows, 16 bytes per lane; LSE = ln2 (m +
+  // log2 l) in fp32. Rows with no key give O = 0 and LSE = -inf.
+  constexpr int OPAD = D + 8;  // padded LDS row: a 16-byte bank shift per row
+  static_assert(NW * QT * 32 * OPAD <= 6 * TILE, "O staging fits in the rings");
+  uint16_t* const s_o = s_ring + ((int)threadIdx.x >> 6) * (QT * 32 * OPAD);
   uint16_t* og = (uint16_t*)p.o + wk.b * p.o_sb + wk.hq * p.o_sh;
 #pragma unroll
   for (int b = 0; b < QT; ++b) {
     mfma_wait_a(oacc[b]);
     const int qrow = wk.row0 + 32 * b + c;
     const float lt = half_sum(l_run[b]);
-    if (qrow < p.Sq) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      uint16_t* orow = og + (int64_t)qrow * p.o_ss;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* orow = s_o + (32 * b + c) * OPAD;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2 v;
-          v[0] = T::pack2(oacc[b][dt][4 * g] * inv, oacc[b][dt][4 * g + 1] * inv);
-          v[1] = T::pack2(oacc[b][dt][4 * g + 2] * inv, oacc[b][dt][4 * g + 3] * inv);
-          *(u32x2*)(orow + 32 * dt + 8 * g + 4 * h) = v;
-        }
-      if (h == 0)
-        p.lse[((int64_t)wk.b * p.Hq + wk.hq) * p.Sq + qrow] =
-            lt > 0.f ? (m_ref[b] + log2f(lt)) * kLn2 : -INFINITY;
-    }
+      for (int g = 0; g < 4; ++g) {
+        u32x2 v;
+        v[0] = T::pack2(oacc[b][dt][4 * g] * inv, oacc[b][dt][4 * g + 1] * inv);
+        v[1] = T::pack2(oacc[b][dt][4 * g + 2] * inv, oacc[b][dt][4 * g + 3] * inv);
+        *(u32x2*)(orow + 32 * dt + 8 * g + 4 * h) = v;
+      }
+    if (h == 0 && qrow < p.Sq)
+      p.lse[((int64_t)wk.b * p.Hq + wk.hq) * p.Sq + qrow] =
+          lt > 0.f ? (m_ref[b] + log2f(lt)) * kLn2 : -INFINITY;
+  }
+  // The wave reads back what its own lanes wrote (LDS operations of a wave
+  // complete in order).
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;     // rows per store instruction
+#pragma unroll
+  for (int k = 0; k < QT * 32 / RPI; ++k) {
+    const int r = k * RPI + lane / CPR, ch = lane % CPR;
+    const int qrow = wk.row0 + r;
+    const u32x4 v = *(const u32x4*)(s_o + r * OPAD + 8 * ch);
+    if (qrow < p.Sq) *(u32x4*)(og + (int64_t)qrow * p.o_ss + 8 * ch) = v;
   }
 }
 
