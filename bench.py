@@ -264,7 +264,8 @@ def main():
             c2 = make_call(w2)
             _, km = time_calls(c2, max(5, args.steps // 2), 2, 0.3)
             sec[name] = {"tflops": round(fl / (km * 1e-3) / 1e12, 2), "kernel_ms": round(km, 4),
-                         "frac_mfma_peak": round(fl / (km * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                         "frac_mfma_peak": round(fl / (km * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "traffic": measured_traffic(name)}
             del c2, w2
             torch.cuda.empty_cache()
         log("secondary topk_mla_bf16_t4096")
