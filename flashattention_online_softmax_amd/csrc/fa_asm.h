@@ -146,8 +146,10 @@ struct Mma<F16> {
 // after it.
 template <int N>
 __device__ __forceinline__ void mfma_wait_v(f32x16 (&a)[N]) {
-  static_assert(N == 1 || N == 2, "score tiles");
-  if constexpr (N == 2)
+  static_assert(N == 1 || N == 2 || N == 4, "tiles");
+  if constexpr (N == 4)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+  else if constexpr (N == 2)
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a[0]), "+v"(a[1]));
   else
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a[0]));
@@ -159,6 +161,16 @@ __device__ __forceinline__ void mfma_wait_a(f32x16 (&a)[N]) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]));
   else
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a[0]), "+a"(a[1]));
+}
+// Wait states between VALU writes of VGPR accumulators and the next MFMA
+// reading them; the writes are placed before it.
+template <int N>
+__device__ __forceinline__ void vacc_written(f32x16 (&a)[N]) {
+  static_assert(N == 2 || N == 4, "d tiles");
+  if constexpr (N == 4)
+    asm volatile("s_nop 4" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+  else
+    asm volatile("s_nop 4" : "+v"(a[0]), "+v"(a[1]));
 }
 // Wait states between VALU writes of accumulator registers and the next
 // MFMA reading them; the writes are placed before it.

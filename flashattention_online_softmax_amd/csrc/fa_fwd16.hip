@@ -10,8 +10,9 @@
 // sparse-MLA page, threshold-branch section, for t > 0).
 //
 // This file is compiled on its own into a gfx950 code object (see build.py:
-// the kernels need most of the register file as VGPRs next to 64 AGPRs, a
-// split the code object gets through its amdgpu-agpr-alloc attribute) and is
+// the kernels keep the Q^T operands in 32 AGPRs and need the rest of a
+// wave's 256 registers as VGPRs, a split the code object gets through its
+// amdgpu-agpr-alloc attribute) and is
 // loaded by the library at run time. Kernels are extern "C" with names of the
 // form fa_fwd16_<dtype>_d<D>_w<waves>_h<heads>_c<causal>m<mask>s<sparse>.
 //
@@ -26,15 +27,17 @@
 //     register staging) into three-deep rings, with an XOR swizzle of the
 //     16-byte chunks so that the MFMA operand reads hit distinct LDS banks.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16 (K from LDS as the A operand, Q^T
-//     resident in VGPRs as the B operand). Each lane owns one query column
+//     resident in AGPRs as the B operand). Each lane owns one query column
 //     and 16 keys of it, so the row max and row sum are in-lane reductions
 //     plus one v_permlane32_swap between the wave halves.
 //   * p = exp2(s * scale*log2e - m) (one FMA + one v_exp_f32 per score), m
 //     being the reference max already in the exp2 domain; l accumulates the
 //     fp32 p; p is rounded to 16 bits into the B operand of the next MFMA.
-//   * O^T += V^T P^T on MFMA with the accumulators in AGPRs: V^T is read from
+//   * O^T += V^T P^T on MFMA with the accumulators in VGPRs: V^T is read from
 //     the row-major V tile with ds_read_b64_tr_b16, in the key order in which
-//     the S^T accumulator holds P. A rescale is a per-lane multiply.
+//     the S^T accumulator holds P. A rescale is one v_mul_f32 per
+//     accumulator (in AGPRs it would be a read, a multiply and a write each,
+//     which made the exact running max three times as expensive).
 // Epilogue: O = acc / l rounded to the output dtype, LSE = ln2 * (m + log2 l)
 // in fp32; rows with no key give O = 0 and LSE = -inf.
 #include <stdint.h>
@@ -124,7 +127,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[b][dt][i] = 0.f;
 #pragma unroll
-  for (int b = 0; b < QT; ++b) acc_written(oacc[b]);  // O^T lives in AGPRs from here on
+  for (int b = 0; b < QT; ++b) vacc_written(oacc[b]);
   float m_ref[QT], l_run[QT];
   f32x16 sc[QT][2];      // [block][kt]: scores of the tile the next softmax works on
   u32x4 pp[1][QT][4];    // P operand of the tile between its V and M phases
@@ -312,7 +315,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
         else
           Mma<T>::vb(sn[b][r & 1], kq[r % RING], qop[b][r >> 1]);
         // P V: d tile r % DT, key step r / DT
-        if (do_pv) Mma<T>::a(oacc[b][r % DT], vq[r % RING], pop[b][r / DT]);
+        if (do_pv) Mma<T>::v(oacc[b][r % DT], vq[r % RING], pop[b][r / DT]);
       }
     }
     // S results complete before the compiler may touch the registers again.
@@ -331,12 +334,12 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     if (o_live && __builtin_amdgcn_ballot_w64(upd_any) != 0) {
 #pragma unroll
       for (int b = 0; b < QT; ++b) {
-        mfma_wait_a(oacc[b]);
+        mfma_wait_v(oacc[b]);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[b][dt][i] *= alpha[b];
-        acc_written(oacc[b]);
+        vacc_written(oacc[b]);
       }
     }
 #pragma unroll
@@ -449,7 +452,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   uint16_t* og = (uint16_t*)p.o + wk.b * p.o_sb + wk.hq * p.o_sh;
 #pragma unroll
   for (int b = 0; b < QT; ++b) {
-    mfma_wait_a(oacc[b]);
+    mfma_wait_v(oacc[b]);
     const int qrow = wk.row0 + 32 * b + c;
     const float lt = half_sum(l_run[b]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
