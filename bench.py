@@ -248,7 +248,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), cast to bf16)",
         "config": {"workload": args.workload, "B": B, "H": H, "S": S, "D": D,
-                   "causal": bool(w["causal"]), "flops_per_step": flops},
+                   "causal": bool(w["causal"]), "flops_per_step": flops,
+                   "rescale_threshold_log2": 8.0},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kern_ms, 4)},
