@@ -146,9 +146,11 @@ struct Mma<F16> {
 // after it.
 template <int N>
 __device__ __forceinline__ void mfma_wait_v(f32x16 (&a)[N]) {
-  static_assert(N == 1 || N == 2 || N == 4, "tiles");
+  static_assert(N >= 1 && N <= 4, "tiles");
   if constexpr (N == 4)
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+  else if constexpr (N == 3)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]));
   else if constexpr (N == 2)
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a[0]), "+v"(a[1]));
   else

@@ -22,7 +22,7 @@
 // rows. With 8 waves two share each SIMD. Workgroups are numbered so that the
 // longest causal row blocks start first and every KV head maps to one XCD.
 //
-// Per 64-key tile and wave:
+// Per key tile (96 keys for dense D = 128, else 64) and wave:
 //   * K and V tiles are copied HBM -> LDS by global_load_lds_dwordx4 (no
 //     register staging) into three-deep rings, with an XOR swizzle of the
 //     16-byte chunks so that the MFMA operand reads hit distinct LDS banks.
@@ -53,8 +53,11 @@
 namespace fa {
 namespace {
 
-// Per 64-key tile j a wave (QT blocks of 32 query rows; every K/V operand it
-// reads serves all of them) has a VALU phase V(j) and an MFMA phase M(j):
+// Per key tile j (BNT = 32 NKT keys: 96 for the dense D = 128 kernels, 64
+// for D = 64 and for the block-sparse ones, whose 128-key blocks split into
+// two tiles) a wave (QT
+// blocks of 32 query rows; every K/V operand it reads serves all of them)
+// has a VALU phase V(j) and an MFMA phase M(j):
 //   V(j): mask, row max, reference max update, p = exp2(s c - m), row sum,
 //         p rounded into the P operand (and the rare rescale of O);
 //   M(j): S(j+1) = K_{j+1} Q^T and O^T += V_j^T P_j^T, interleaved.
@@ -73,12 +76,15 @@ template <class T, int D, int NW, int QT, int HP, bool CAUSAL, bool MASK, bool S
 __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   constexpr int WPH = NW / HP;
   constexpr int MPH = WPH * QT * 32;
-  constexpr int DS = D / 16;  // MFMA k-steps over D for S^T
-  constexpr int DT = D / 32;  // 32-wide d tiles of O^T
-  constexpr int NS = 2 * DS;  // K operands per tile (2 key halves x DS)
-  constexpr int NP = 4 * DT;  // V operands per tile (4 key steps x DT)
+  constexpr int NKT = (SPARSE || D == 64) ? 2 : 3;  // 32-key halves per tile
+  constexpr int BNT = 32 * NKT;        // keys per tile
+  constexpr int DS = D / 16;           // MFMA k-steps over D for S^T
+  constexpr int DT = D / 32;           // 32-wide d tiles of O^T
+  constexpr int NKS = 2 * NKT;         // 16-key steps per tile
+  constexpr int NS = NKT * DS;         // K operands per tile (key halves x DS)
+  constexpr int NP = NKS * DT;         // V operands per tile (key steps x DT)
   static_assert(NS == NP, "K and V operand counts agree (D / 8 each)");
-  constexpr int TILE = BN * D;
+  constexpr int TILE = BNT * D;
   constexpr int AHEAD = 3;    // operand pairs read ahead
   constexpr int RING = AHEAD + 1;
   static_assert(!SPARSE || MPH == 128, "block-sparse needs 128 query rows per head");
@@ -101,7 +107,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   if (SPARSE)
     n_iter = build_sparse_tiles(p, wk, wk.wg_row0 / 128, s_kstart, &s_n);
   else
-    n_iter = dense_tiles<CAUSAL>(wk, MPH, BN);
+    n_iter = dense_tiles<CAUSAL>(wk, MPH, BNT);
   // Tiles this wave works on: none if its rows are past Lq; under the causal
   // mask only the tiles that start at or before its last visible key.
   int n_act = n_iter;
@@ -109,7 +115,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     n_act = 0;
   } else if (CAUSAL && !SPARSE) {
     const int last_key = min(wk.row0 + QT * 32 - 1, wk.Lq - 1) + diag;
-    n_act = last_key < 0 ? 0 : min(n_iter, last_key / BN + 1);
+    n_act = last_key < 0 ? 0 : min(n_iter, last_key / BNT + 1);
   }
   n_act = __builtin_amdgcn_readfirstlane(n_act);
 
@@ -129,29 +135,29 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
 #pragma unroll
   for (int b = 0; b < QT; ++b) vacc_written(oacc[b]);
   float m_ref[QT], l_run[QT];
-  f32x16 sc[QT][2];      // [block][kt]: scores of the tile the next softmax works on
-  u32x4 pp[1][QT][4];    // P operand of the tile between its V and M phases
+  f32x16 sc[QT][NKT];    // [block][kt]: scores of the tile the next softmax works on
+  u32x4 pp[1][QT][NKS];  // P operand of the tile between its V and M phases
 #pragma unroll
   for (int b = 0; b < QT; ++b) {
     m_ref[b] = -INFINITY;
     l_run[b] = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[b][kt][i] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) pp[0][b][ks] = u32x4{0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < NKS; ++ks) pp[0][b][ks] = u32x4{0u, 0u, 0u, 0u};
   }
 
-  auto tile_start = [&](int it) __attribute__((always_inline)) { return SPARSE ? s_kstart[it] : it * BN; };
+  auto tile_start = [&](int it) __attribute__((always_inline)) { return SPARSE ? s_kstart[it] : it * BNT; };
 
-  const TileCopy<D, NW, false> kcopy(kg, p.k_ss);
-  const TileCopy<D, NW, true> vcopy(vg, p.v_ss);
-  constexpr int NCOPY = TileCopy<D, NW, false>::PER_WAVE + TileCopy<D, NW, true>::PER_WAVE;
+  const TileCopy<D, NW, false, BNT> kcopy(kg, p.k_ss);
+  const TileCopy<D, NW, true, BNT> vcopy(vg, p.v_ss);
+  constexpr int NCOPY = TileCopy<D, NW, false, BNT>::PER_WAVE + TileCopy<D, NW, true, BNT>::PER_WAVE;
 
   // Per-lane element offsets of the MFMA operands inside a tile.
-  // K operand r (A operand of S^T): key half kt = r & 1 (rows 32 kt + c),
-  // logical chunk 2 (r >> 1) + h.
+  // K operand r (A operand of S^T): key half kt = r % NKT (rows 32 kt + c),
+  // logical chunk 2 (r / NKT) + h.
   int koff[DS];
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds) koff[ds] = c * D + (((2 * ds + h) ^ kswz<D>(c)) << 3);
@@ -166,7 +172,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     voff[dt] = vrow * D + (((col >> 3) ^ vswz<D>(vrow)) << 3) + (col & 7);
   }
   auto kread = [&](const lds_u16* kb, int r) __attribute__((always_inline)) -> u32x4 {
-    return *(const __attribute__((address_space(3))) u32x4*)(kb + (r & 1) * 32 * D + koff[r >> 1]);
+    return *(const __attribute__((address_space(3))) u32x4*)(kb + (r % NKT) * 32 * D + koff[r / NKT]);
   };
   auto vread = [&](const lds_u16* const (&vb)[DT], int r) __attribute__((always_inline)) -> u32x4 {
     const int dt = r % DT, ks = r / DT;
@@ -179,21 +185,21 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
 
   // Masking of tile j's scores of block b (causal diagonal, ragged edges,
   // boolean mask).
-  auto mask_tile = [&](f32x16 (&sv)[2], int b, int j) __attribute__((always_inline)) {
+  auto mask_tile = [&](f32x16 (&sv)[NKT], int b, int j) __attribute__((always_inline)) {
     const int kstart = tile_start(j);
     const int brow0 = wk.row0 + 32 * b;
     const int qrow = brow0 + c;
-    const bool edge = (kstart + BN > wk.Lk) || (brow0 + 32 > wk.Lq) ||
-                      (CAUSAL && kstart + BN - 1 > brow0 + diag);
+    const bool edge = (kstart + BNT > wk.Lk) || (brow0 + 32 > wk.Lq) ||
+                      (CAUSAL && kstart + BNT - 1 > brow0 + diag);
     if (!MASK && !edge) return;
-    uint32_t mbits[2][4];
+    uint32_t mbits[NKT][4];
     if (MASK) {
       const uint8_t* mrow = p.mask + wk.b * p.m_sb + wk.hq * p.m_sh + (int64_t)qrow * p.m_ss;
       // 4 consecutive mask bytes per (kt, g).
-      const bool vec = p.mask_vec4 && (kstart + BN <= p.Skv);
+      const bool vec = p.mask_vec4 && (kstart + BNT <= p.Skv);
       const bool rv = qrow < p.Sq;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int key0 = kstart + kt * 32 + 8 * g + 4 * h;
@@ -211,7 +217,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
         }
     }
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kstart + kt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
@@ -225,8 +231,9 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   // Softmax state of the step being processed, per block.
   float mq[QT], mc[QT], alpha[QT], rs0[QT], rs1[QT];
   bool upd_any = false;
-  // Quarter part (0..3) of block b's row max (three-input maxima).
-  auto row_max_4 = [&](const f32x16 (&sv)[2], int b, int part) __attribute__((always_inline)) {
+  // Part (0 .. 2 NKT - 1, 8 scores each) of block b's row max (three-input
+  // maxima).
+  auto row_max_4 = [&](const f32x16 (&sv)[NKT], int b, int part) __attribute__((always_inline)) {
     const int kt = part >> 1, i0 = (part & 1) * 8;
     const float t = max3(sv[kt][i0], sv[kt][i0 + 1], sv[kt][i0 + 2]);
     const float u = max3(t, sv[kt][i0 + 3], sv[kt][i0 + 4]);
@@ -250,7 +257,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     rs1[b] = 0.f;
   };
   // Exponentials of block b's scores e, e+1 (e even) into its P operand.
-  auto exp_pair = [&](const f32x16 (&sv)[2], u32x4 (&pop)[4], int b, int e) __attribute__((always_inline)) {
+  auto exp_pair = [&](const f32x16 (&sv)[NKT], u32x4 (&pop)[NKS], int b, int e) __attribute__((always_inline)) {
     const int kt = e >> 4, ii = e & 15;
     const float x0 = fast_exp2(__builtin_fmaf(sv[kt][ii], p.scale_log2, -mc[b]));
     const float x1 = fast_exp2(__builtin_fmaf(sv[kt][ii + 1], p.scale_log2, -mc[b]));
@@ -263,16 +270,17 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     // below the MFMAs they are meant to overlap.
     asm volatile("" ::"v"(pop[e >> 3][(e & 7) >> 1]), "v"(rs0[b]), "v"(rs1[b]));
   };
-  // Softmax slice s of a step (0 .. 21 QT - 1): block maxima, updates, then
-  // exponential pairs alternating between blocks.
-  constexpr int NSLICE = 21 * QT;
-  auto slice = [&](f32x16 (&sv)[QT][2], u32x4 (&pop)[QT][4], int s, bool act) __attribute__((always_inline)) {
-    if (s < 4 * QT) {
-      row_max_4(sv[s / 4], s / 4, s % 4);
-    } else if (s < 5 * QT) {
-      max_update(s - 4 * QT, act);
+  // Softmax slice s of a step (0 .. (10 NKT + 1) QT - 1): block maxima,
+  // updates, then exponential pairs alternating between blocks.
+  constexpr int NMAX = 2 * NKT;  // row-max parts per block
+  constexpr int NSLICE = (5 * NMAX + 1) * QT;
+  auto slice = [&](f32x16 (&sv)[QT][NKT], u32x4 (&pop)[QT][NKS], int s, bool act) __attribute__((always_inline)) {
+    if (s < NMAX * QT) {
+      row_max_4(sv[s / NMAX], s / NMAX, s % NMAX);
+    } else if (s < (NMAX + 1) * QT) {
+      max_update(s - NMAX * QT, act);
     } else {
-      const int t = s - 5 * QT;  // 0 .. 16 QT - 1
+      const int t = s - (NMAX + 1) * QT;  // 0 .. 8 NKT QT - 1
       const int b = t % QT, e = 2 * (t / QT);
       exp_pair(sv[b], pop[b], b, e);
     }
@@ -295,7 +303,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
       if (do_pv) vq[r] = vread(vb, r);
     }
   };
-  auto mphase = [&](f32x16 (&sn)[QT][2], const u32x4 (&pop)[QT][4], const uint16_t* kt_buf,
+  auto mphase = [&](f32x16 (&sn)[QT][NKT], const u32x4 (&pop)[QT][NKS], const uint16_t* kt_buf,
                     const uint16_t* vt_buf, bool do_pv) __attribute__((always_inline)) {
     const lds_u16* kb = lds_ptr(lds_addr_of(kt_buf));
     const lds_u16* vb[DT];
@@ -309,11 +317,11 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
       }
 #pragma unroll
       for (int b = 0; b < QT; ++b) {
-        // S: key half r & 1, k-step r >> 1
-        if (r < 2)
-          Mma<T>::v0b(sn[b][r & 1], kq[r % RING], qop[b][r >> 1]);
+        // S: key half r % NKT, k-step r / NKT
+        if (r < NKT)
+          Mma<T>::v0b(sn[b][r % NKT], kq[r % RING], qop[b][r / NKT]);
         else
-          Mma<T>::vb(sn[b][r & 1], kq[r % RING], qop[b][r >> 1]);
+          Mma<T>::vb(sn[b][r % NKT], kq[r % RING], qop[b][r / NKT]);
         // P V: d tile r % DT, key step r / DT
         if (do_pv) Mma<T>::v(oacc[b][r % DT], vq[r % RING], pop[b][r / DT]);
       }
@@ -326,7 +334,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   // V phase: softmax(j) of the scores in sv into pop (VALU only), and the
   // rescale of O and l when a reference max moved (O is only ever touched by
   // MFMAs otherwise).
-  auto vphase = [&](f32x16 (&sv)[QT][2], u32x4 (&pop)[QT][4], bool act, bool o_live)
+  auto vphase = [&](f32x16 (&sv)[QT][NKT], u32x4 (&pop)[QT][NKS], bool act, bool o_live)
                     __attribute__((always_inline)) {
     upd_any = false;
 #pragma unroll

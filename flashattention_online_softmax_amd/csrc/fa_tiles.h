@@ -1,6 +1,6 @@
 // Work decomposition and tile bookkeeping shared by the attention forward
 // kernels: workgroup-to-(batch, head, query block) mapping, the number of
-// 64-key tiles a query block visits (dense / causal / block-sparse), and the
+// key tiles a query block visits (dense / causal / block-sparse), and the
 // LDS chunk swizzles of K and V tiles.
 #pragma once
 
@@ -11,7 +11,7 @@
 
 namespace fa {
 
-constexpr int BN = 64;  // keys per tile (16-bit path)
+constexpr int BN = 64;  // keys per block-sparse tile (half a 128-key block)
 
 // 16-byte chunk swizzles (chunk index XOR f(row)) of the K and V tiles.
 // K is read 16 bytes per lane by 32 lanes at 32 consecutive rows of one chunk
@@ -97,7 +97,7 @@ __device__ __forceinline__ int build_sparse_tiles(const FwdParams& p, const Work
   return *s_n;
 }
 
-// Number of 64-key tiles of a dense (optionally causal) workgroup.
+// Number of bn-key tiles of a dense (optionally causal) workgroup.
 template <bool CAUSAL>
 __device__ __forceinline__ int dense_tiles(const Work& wk, int mph, int bn) {
   if (wk.wg_row0 >= wk.Lq) return 0;
