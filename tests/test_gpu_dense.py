@@ -36,6 +36,18 @@ def test_dense_ragged(dtype, D, causal, thr):
               thr=thr)
 
 
+@pytest.mark.parametrize("skv", [95, 96, 97, 191, 192, 193])
+@pytest.mark.parametrize("causal", [False, True])
+def test_tile_boundaries_d128(skv, causal):
+    # Key counts around the 96-key tiles of the D = 128 kernels (one key short
+    # of, exactly at and one past a tile edge), queries over two workgroups.
+    dtype = "f16" if skv % 2 else "bf16"
+    _, q, k, v = synth.dense_inputs(300 + skv + causal, 1, 2, 2, 300, skv, 128, 128, dtype)
+    run_dense("tiles_skv%d_causal%d" % (skv, causal), q, k, v, 1 / math.sqrt(128), causal, thr=0.0)
+    _, q, k, v = synth.dense_inputs(400 + skv + causal, 1, 2, 2, skv, skv, 128, 128, dtype)
+    run_dense("tiles_sq_skv%d_causal%d" % (skv, causal), q, k, v, 1 / math.sqrt(128), causal, thr=8.0)
+
+
 @pytest.mark.parametrize("thr", [0.0, 8.0])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_gqa_causal_mask(dtype, thr):
