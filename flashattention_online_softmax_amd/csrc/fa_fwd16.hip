@@ -53,9 +53,9 @@
 namespace fa {
 namespace {
 
-// Per key tile j (BNT = 32 NKT keys: 96 for the dense D = 128 kernels, 64
-// for D = 64 and for the block-sparse ones, whose 128-key blocks split into
-// two tiles) a wave (QT
+// Per key tile j (BNT = 32 NKT keys: 96 for the dense D = 128 kernels
+// without a boolean mask, 64 for the masked ones, for D = 64 and for the
+// block-sparse ones, whose 128-key blocks split into two tiles) a wave (QT
 // blocks of 32 query rows; every K/V operand it reads serves all of them)
 // has a VALU phase V(j) and an MFMA phase M(j):
 //   V(j): mask, row max, reference max update, p = exp2(s c - m), row sum,
@@ -76,7 +76,9 @@ template <class T, int D, int NW, int QT, int HP, bool CAUSAL, bool MASK, bool S
 __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   constexpr int WPH = NW / HP;
   constexpr int MPH = WPH * QT * 32;
-  constexpr int NKT = (SPARSE || D == 64) ? 2 : 3;  // 32-key halves per tile
+  // 32-key halves per tile: 3 for dense D = 128 without a boolean mask; the
+  // masked kernels spend those registers on the prefetched mask words.
+  constexpr int NKT = (SPARSE || MASK || D == 64) ? 2 : 3;
   constexpr int BNT = 32 * NKT;        // keys per tile
   constexpr int DS = D / 16;           // MFMA k-steps over D for S^T
   constexpr int DT = D / 32;           // 32-wide d tiles of O^T
@@ -185,6 +187,55 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
 
   // Masking of tile j's scores of block b (causal diagonal, ragged edges,
   // boolean mask).
+  // Boolean-mask words of the tile the next V phase masks, per block: 4 mask
+  // bytes (keys 8 g + 4 h .. +3 of key half kt of the lane's row). They are
+  // loaded at the start of the M phase before that V phase, so the global
+  // load latency hides behind its MFMAs, and are pinned in registers before
+  // the phase's tile copies go out (a later wait for them would also drain
+  // the copies).
+  uint32_t mwords[QT][MASK ? NKT : 1][4];
+  auto mask_load = [&](int j) __attribute__((always_inline)) {
+    if constexpr (MASK) {
+      const int kstart = tile_start(j);
+      const bool vec = p.mask_vec4 && (kstart + BNT <= p.Skv);
+#pragma unroll
+      for (int b = 0; b < QT; ++b) {
+        const int qrow = wk.row0 + 32 * b + c;
+        const uint8_t* mrow = p.mask + wk.b * p.m_sb + wk.hq * p.m_sh + (int64_t)qrow * p.m_ss;
+        const bool rv = qrow < p.Sq;
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int key0 = kstart + kt * 32 + 8 * g + 4 * h;
+            uint32_t bits = 0x01010101u;
+            if (rv) {
+              if (vec) {
+                bits = *(const uint32_t*)(mrow + key0);
+              } else {
+                bits = 0;
+                for (int e = 0; e < 4; ++e)
+                  bits |= (uint32_t)((key0 + e < p.Skv) ? mrow[key0 + e] : 1) << (8 * e);
+              }
+            }
+            mwords[b][kt][g] = bits;
+          }
+      }
+    }
+  };
+  auto mask_pin = [&]() __attribute__((always_inline)) {
+    if constexpr (MASK) {
+#pragma unroll
+      for (int b = 0; b < QT; ++b)
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) asm volatile("" ::"v"(mwords[b][kt][g]));
+    }
+  };
+
+  // Masking of tile j's scores of block b (causal diagonal, ragged edges,
+  // boolean mask from mwords).
   auto mask_tile = [&](f32x16 (&sv)[NKT], int b, int j) __attribute__((always_inline)) {
     const int kstart = tile_start(j);
     const int brow0 = wk.row0 + 32 * b;
@@ -192,30 +243,6 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     const bool edge = (kstart + BNT > wk.Lk) || (brow0 + 32 > wk.Lq) ||
                       (CAUSAL && kstart + BNT - 1 > brow0 + diag);
     if (!MASK && !edge) return;
-    uint32_t mbits[NKT][4];
-    if (MASK) {
-      const uint8_t* mrow = p.mask + wk.b * p.m_sb + wk.hq * p.m_sh + (int64_t)qrow * p.m_ss;
-      // 4 consecutive mask bytes per (kt, g).
-      const bool vec = p.mask_vec4 && (kstart + BNT <= p.Skv);
-      const bool rv = qrow < p.Sq;
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int key0 = kstart + kt * 32 + 8 * g + 4 * h;
-          uint32_t bits = 0x01010101u;
-          if (rv) {
-            if (vec) {
-              bits = *(const uint32_t*)(mrow + key0);
-            } else {
-              bits = 0;
-              for (int e = 0; e < 4; ++e)
-                bits |= (uint32_t)((key0 + e < p.Skv) ? mrow[key0 + e] : 1) << (8 * e);
-            }
-          }
-          mbits[kt][g] = bits;
-        }
-    }
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
@@ -223,7 +250,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
         const int key = kstart + kt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
         bool ok = key < wk.Lk && qrow < wk.Lq;
         if (CAUSAL) ok = ok && key <= qrow + diag;
-        if (MASK) ok = ok && ((mbits[kt][i >> 2] >> (8 * (i & 3))) & 0xffu) == 0u;
+        if constexpr (MASK) ok = ok && ((mwords[b][kt][i >> 2] >> (8 * (i & 3))) & 0xffu) == 0u;
         if (!ok) sv[kt][i] = -INFINITY;
       }
   };
@@ -427,8 +454,10 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   // phase; the first reader of K_{j+3} / V_{j+2} is M(j+2), two phases later.
   const int grp = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) / (NW / 2));
   if (grp == 1) end_phase(false);
+  if (n_act > 0) mask_load(0);
   mprefetch(s_kring, s_vring, false);
   mphase(sc, pp[0], s_kring, s_vring, false);  // M(-1): S(0)
+  mask_pin();
   end_phase(false);
   for (int j = 0; j < n_iter; ++j) {
     const bool act = j < n_act;
@@ -445,7 +474,9 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     mprefetch(kt_buf, vt_buf, true);
     end_phase(false);
     // M(j): global phase 2j+2 (group 0) or 2j+3 (group 1).
+    if (j + 1 < n_act) mask_load(j + 1);
     mphase(sc, pp[0], kt_buf, vt_buf, true);
+    mask_pin();
     end_phase(copies(j));
   }
   if (grp == 0) end_phase(false);

@@ -76,13 +76,19 @@ def test_mask_4d_broadcasts_and_empty_rows():
     assert rep["rows"] == 2 * 3 * 130
 
 
-def test_zero_mask_is_bitwise_no_mask():
+def test_zero_mask_matches_no_mask():
+    # An all-zero boolean mask excludes nothing. The masked and unmasked
+    # D = 128 kernels tile the keys differently (64 and 96 keys), so the two
+    # results agree to rounding, and each matches the oracle.
     _, q, k, v = synth.dense_inputs(9, 1, 2, 2, 190, 190, 128, 128, "bf16")
+    zero = torch.zeros((190, 190), dtype=torch.uint8)
+    run_dense("zero_mask", q, k, v, 0.1, True, zero)
     qq, kk, vv = gpu(q, k, v)
     a, la = fa.fa_fwd(qq, kk, vv, scale=0.1, causal=True)
-    b, lb = fa.fa_fwd(qq, kk, vv, scale=0.1, causal=True,
-                      mask=torch.zeros((190, 190), dtype=torch.uint8, device="cuda"))
-    assert torch.equal(a, b) and torch.equal(la, lb)
+    b, lb = fa.fa_fwd(qq, kk, vv, scale=0.1, causal=True, mask=zero.cuda())
+    torch.cuda.synchronize()
+    assert (a.float() - b.float()).abs().max().item() <= 2 ** -7 * max(1.0, a.float().abs().max().item())
+    assert (la - lb).abs().max().item() <= 1e-5
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
