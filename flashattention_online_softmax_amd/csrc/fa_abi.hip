@@ -222,6 +222,8 @@ fa_status fa_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
     p.mask = (const uint8_t*)mask->data;
     p.mask_vec4 = (((uintptr_t)mask->data) % 4 == 0) && (p.m_sb % 4 == 0) && (p.m_sh % 4 == 0) &&
                   (p.m_ss % 4 == 0);
+    p.mask_vec16 = (((uintptr_t)mask->data) % 16 == 0) && (p.m_sb % 16 == 0) && (p.m_sh % 16 == 0) &&
+                   (p.m_ss % 16 == 0);
   }
   p.seqlens_q = seqlens_q ? (const int32_t*)seqlens_q->data : nullptr;
   p.seqlens_k = seqlens_k ? (const int32_t*)seqlens_k->data : nullptr;

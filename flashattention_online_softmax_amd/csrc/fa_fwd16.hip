@@ -197,6 +197,34 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   auto mask_load = [&](int j) __attribute__((always_inline)) {
     if constexpr (MASK) {
       const int kstart = tile_start(j);
+      if (NKT == 2 && p.mask_vec16 && kstart + BNT <= p.Skv) {
+        // Coalesced: the two lanes of a row load its 64 mask bytes, 32 each
+        // (lane half h: bytes 32 h .. 32 h + 31, own words 0..7 = row words
+        // 8 h .. 8 h + 7), then trade words across the wave halves. Word
+        // 8 kt + 2 g + h is what mwords[kt][g] needs: swapping the upper half
+        // of own word 2 g with the lower half of own word 2 g + 1 gives the
+        // kt = 0 word in the first result and the kt = 1 word in the second,
+        // on both halves.
+#pragma unroll
+        for (int b = 0; b < QT; ++b) {
+          const int qrow = wk.row0 + 32 * b + c;
+          u32x4 lo = {0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u}, hi = lo;
+          if (qrow < p.Sq) {
+            const u32x4* src = (const u32x4*)(p.mask + wk.b * p.m_sb + wk.hq * p.m_sh + (int64_t)qrow * p.m_ss +
+                                              kstart + 32 * h);
+            lo = src[0];
+            hi = src[1];
+          }
+          const uint32_t own[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const auto r = __builtin_amdgcn_permlane32_swap(own[2 * g], own[2 * g + 1], false, false);
+            mwords[b][0][g] = r[0];
+            mwords[b][NKT - 1][g] = r[1];
+          }
+        }
+        return;
+      }
       const bool vec = p.mask_vec4 && (kstart + BNT <= p.Skv);
 #pragma unroll
       for (int b = 0; b < QT; ++b) {
@@ -242,7 +270,18 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     const int qrow = brow0 + c;
     const bool edge = (kstart + BNT > wk.Lk) || (brow0 + 32 > wk.Lq) ||
                       (CAUSAL && kstart + BNT - 1 > brow0 + diag);
-    if (!MASK && !edge) return;
+    if constexpr (MASK) {
+      if (!edge) {  // inside every range: the mask bytes alone decide
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (((mwords[b][kt][i >> 2] >> (8 * (i & 3))) & 0xffu) != 0u) sv[kt][i] = -INFINITY;
+        return;
+      }
+    } else if (!edge) {
+      return;
+    }
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll

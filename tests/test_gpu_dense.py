@@ -56,6 +56,18 @@ def test_gqa_causal_mask(dtype, thr):
     run_dense("gqa_mask_%s_thr%g" % (dtype, thr), q, k, v, 1 / math.sqrt(128), True, mask, thr=thr)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_mask_aligned_rows(causal):
+    # Mask rows 16-byte aligned (Skv = 336): full 64-key tiles take the
+    # coalesced 16-byte mask loads, the partial last tile the byte loads.
+    g, q, k, v = synth.dense_inputs(17 + causal, 2, 4, 2, 300, 336, 128, 128, "f16")
+    mask = synth.bernoulli_mask(g, 300, 336, 0.3)
+    run_dense("mask_aligned_causal%d" % causal, q, k, v, 1 / math.sqrt(128), causal, mask, thr=0.0)
+    m4 = torch.from_numpy((g.random((2, 1, 300, 336)) < 0.2).astype(np.uint8))
+    m4[1, 0, 7] = 1  # a fully masked row
+    run_dense("mask4d_aligned_causal%d" % causal, q, k, v, 1 / math.sqrt(128), causal, m4, thr=8.0)
+
+
 def test_growing_scores_rescale_paths():
     # Scores that keep growing along the keys force a rescale on every tile
     # with the exact max and on some tiles with the lazy one; both must match.
