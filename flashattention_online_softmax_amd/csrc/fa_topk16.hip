@@ -167,6 +167,28 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
   const int head0 = ((int)blockIdx.x - tb * p.n_htiles) * 128 + w * 32;
   const bool active = head0 < p.Hq;  // Hq is a multiple of 32
 
+  // The index row first, into registers (thread tid owns the slots
+  // [tid*spt, tid*spt + spt), spt <= 16): the compaction below then waits
+  // for it alone, while the Q loads issued after it are still in flight.
+  const int32_t* irow = p.idx + (int64_t)t * p.idx_st;
+  const int spt = (p.W + 255) / 256;
+  int iv[16];
+  if (spt == 8 && p.W == 2048 && (((uintptr_t)irow) & 15) == 0) {
+    const int4 a = *(const int4*)(irow + tid * 8);
+    const int4 b = *(const int4*)(irow + tid * 8 + 4);
+    iv[0] = a.x; iv[1] = a.y; iv[2] = a.z; iv[3] = a.w;
+    iv[4] = b.x; iv[5] = b.y; iv[6] = b.z; iv[7] = b.w;
+#pragma unroll
+    for (int e = 8; e < 16; ++e) iv[e] = -1;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int s = tid * spt + e;
+      iv[e] = (e < spt && s < p.W) ? irow[s] : -1;
+    }
+  }
+  asm volatile("" ::: "memory");  // keep the Q loads behind the index loads
+
   // Q^T operands (B operand of S^T): qop[ht][ks] = Q[t, head 16 ht + n,
   // 32 ks + 8 G .. +7]. A wave past Hq computes on heads 0..31 and stores
   // nothing.
@@ -180,15 +202,10 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
       for (int ks = 0; ks < KSTEP; ++ks) qop[ht][ks] = *(const u32x4*)(qb + 16 * ht * p.q_sh + 32 * ks);
   }
 
-  // Compact the valid indices of row t into s_list (list order kept):
-  // thread tid owns the slots [tid*spt, tid*spt + spt).
-  const int32_t* irow = p.idx + (int64_t)t * p.idx_st;
-  const int spt = (p.W + 255) / 256;
+  // Compact the valid indices of row t into s_list (list order kept).
   int cnt = 0;
-  for (int e = 0; e < spt; ++e) {
-    const int s = tid * spt + e;
-    if (s < p.W && irow[s] >= 0) ++cnt;
-  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) cnt += iv[e] >= 0 ? 1 : 0;
   int incl = cnt;  // inclusive scan over the wave
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -200,13 +217,9 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
   int off = incl - cnt;
   for (int ww = 0; ww < w; ++ww) off += s_wcount[ww];
   const int n_valid = __builtin_amdgcn_readfirstlane(s_wcount[0] + s_wcount[1] + s_wcount[2] + s_wcount[3]);
-  for (int e = 0; e < spt; ++e) {
-    const int s = tid * spt + e;
-    if (s < p.W) {
-      const int x = irow[s];
-      if (x >= 0) s_list[off++] = x;
-    }
-  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if (iv[e] >= 0) s_list[off++] = iv[e];
   __syncthreads();
   const int n_tiles = (n_valid + TB - 1) / TB;
   // Retire the Q loads here, visibly to the compiler, before any copy is in
@@ -486,25 +499,44 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
   }
 
   // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l); no valid key -> 0 / -inf.
+  // O goes through the ring (free once every copy has landed and every wave
+  // has passed its last step): wave w writes its 32 heads x 512 as 32 rows
+  // of 1 KB with the 16-byte chunks of row r XOR-swizzled by r (conflict-free
+  // on both sides), then stores one whole head row per instruction.
 #pragma unroll
   for (int dt = 0; dt < NDT; dt += 2)
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+a"(oacc[dt][0]), "+a"(oacc[dt][1]), "+a"(oacc[dt + 1][0]), "+a"(oacc[dt + 1][1]));
+  wait_vmem();
+  __syncthreads();
+  static_assert(NWAVE * 32 * DV * 2 <= L_BASE, "O staging fits in the ring");
+  char* const stage = (char*)s_mem + w * (32 * DV * 2);
+  auto st_at = [&](int r, int ch) __attribute__((always_inline)) { return stage + r * (DV * 2) + ((ch ^ (r & 63)) << 4); };
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const float lt = quad_sum(l_run[ht]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int r = 16 * ht + n;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      u32x2 v;
+      v[0] = T::pack2(oacc[dt][ht][0] * inv, oacc[dt][ht][1] * inv);
+      v[1] = T::pack2(oacc[dt][ht][2] * inv, oacc[dt][ht][3] * inv);
+      // columns 16 dt + 4 G .. +3: chunk 2 dt + G / 2, bytes 8 (G % 2) in it
+      *(u32x2*)(st_at(r, 2 * dt + (G >> 1)) + 8 * (G & 1)) = v;
+    }
+    if (active && G == 0)
+      p.lse[(int64_t)t * p.Hq + head0 + r] = lt > 0.f ? (m_run[ht] + log2f(lt)) * kLn2 : -INFINITY;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if (active) {
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const float lt = quad_sum(l_run[ht]);
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const int head = head0 + 16 * ht + n;
-      uint16_t* orow = (uint16_t*)p.o + (int64_t)t * p.o_st + (int64_t)head * p.o_sh + 4 * G;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        u32x2 v;
-        v[0] = T::pack2(oacc[dt][ht][0] * inv, oacc[dt][ht][1] * inv);
-        v[1] = T::pack2(oacc[dt][ht][2] * inv, oacc[dt][ht][3] * inv);
-        *(u32x2*)(orow + 16 * dt) = v;
-      }
-      if (G == 0) p.lse[(int64_t)t * p.Hq + head] = lt > 0.f ? (m_run[ht] + log2f(lt)) * kLn2 : -INFINITY;
+    uint16_t* const ob = (uint16_t*)p.o + (int64_t)t * p.o_st + (int64_t)head0 * p.o_sh;
+#pragma unroll 8
+    for (int r = 0; r < 32; ++r) {
+      const u32x4 v = *(const u32x4*)st_at(r, lane);
+      *(u32x4*)(ob + (int64_t)r * p.o_sh + 8 * lane) = v;
     }
   }
 }
