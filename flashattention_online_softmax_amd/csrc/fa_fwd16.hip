@@ -282,16 +282,30 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     } else if (!edge) {
       return;
     }
+    // The lane's last visible key (-1: none): keys of its row run up to
+    // Lk - 1, and under the causal mask up to qrow + diag; rows past Lq see
+    // none. lim_lo is the smallest of these over the block's 32 rows (the
+    // first row's under the causal mask), the same in every lane.
+    int lim = qrow < wk.Lq ? wk.Lk - 1 : -1;
+    if (CAUSAL) lim = min(lim, qrow + diag);
+    int lim_lo = brow0 + 32 <= wk.Lq ? wk.Lk - 1 : -1;
+    if (CAUSAL) lim_lo = min(lim_lo, brow0 + diag);
+    lim_lo = __builtin_amdgcn_readfirstlane(lim_lo);
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
+    for (int kt = 0; kt < NKT; ++kt) {
+      const int k0 = kstart + kt * 32;
+      // Key half kt entirely visible in every row: only the mask bytes apply.
+      if (!MASK && k0 + 31 <= lim_lo) continue;
+      // Element i holds key k0 + 4 h + 8 (i / 4) + i % 4: visible iff
+      // 8 (i / 4) + i % 4 <= r.
+      const int r = k0 + 31 <= lim_lo ? 31 : lim - k0 - 4 * h;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = kstart + kt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        bool ok = key < wk.Lk && qrow < wk.Lq;
-        if (CAUSAL) ok = ok && key <= qrow + diag;
+        bool ok = 8 * (i >> 2) + (i & 3) <= r;
         if constexpr (MASK) ok = ok && ((mwords[b][kt][i >> 2] >> (8 * (i & 3))) & 0xffu) == 0u;
         if (!ok) sv[kt][i] = -INFINITY;
       }
+    }
   };
 
   // Softmax state of the step being processed, per block.
