@@ -32,7 +32,13 @@ struct Work {
 
 // Decodes blockIdx.x into (query block, head group, KV head, batch); the
 // last query block comes first (longest causal rows first) and the KV-head
-// index varies fastest, so all query heads of one KV head land on one XCD.
+// index varies fastest, so the query heads of one KV head share an XCD
+// (workgroup i runs on XCD i % 8). Head group g takes the (batch, KV head)
+// pairs rotated by g * B Hkv / n_hgroups: with eight pairs and two head
+// groups each XCD then serves two pairs instead of one, so batches of
+// different lengths (per-batch sequence lengths) no longer leave whole XCDs
+// idle; when B Hkv is a multiple of 8 n_hgroups the rotation keeps every
+// pair on its XCD.
 template <int NW, int QT, int HP>
 __device__ __forceinline__ Work decode_work(const FwdParams& p) {
   constexpr int WPH = NW / HP;
@@ -45,7 +51,7 @@ __device__ __forceinline__ Work decode_work(const FwdParams& p) {
   const int r = id - mb_rank * per_mb;
   const int mb = p.n_mblocks - 1 - mb_rank;
   const int hg = r / BHkv;
-  const int bkv = r - hg * BHkv;
+  const int bkv = (r - hg * BHkv + hg * (BHkv / p.n_hgroups)) % BHkv;
   Work wk;
   wk.b = bkv / p.Hkv;
   wk.hkv = bkv - wk.b * p.Hkv;
