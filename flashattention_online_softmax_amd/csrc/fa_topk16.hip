@@ -66,6 +66,9 @@ constexpr uint32_t VTILE = TB * DV * 2;          // bytes of a V tile
 constexpr int LIST = 4096;                       // longest index row
 constexpr int NOPS = NKOP + DV / 16;             // LDS operands per step: 36 K, then 32 V
 constexpr int AHEAD = 6, RING = 8;               // operands read ahead / their ring
+// Operand u >= NOPS of a step of parity par is operand u - NOPS of the next
+// step (parity par ^ 1) in the same ring slot.
+static_assert((2 * NOPS) % RING == 0, "slot(par, u + NOPS) == slot(par ^ 1, u)");
 constexpr int EXP_GAPS = 8;                      // phase-1 MFMAs carrying the exponentials (a pair each)
 constexpr int PREP_AT = 48;                      // phase-2 MFMA after which the next gather offset is read
 
@@ -375,11 +378,14 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
     }
   };
 
-  // End of step j: this wave's copies of tile j+2 have landed, barrier, then
-  // the copies into the slots step j left.
+  // End of step j: this wave's copies of tile j+3 have landed (with V read
+  // out of the K rows; else those of tiles j+1, j+2), barrier, then the
+  // copies into the slots step j left. Tile j+3 is waited for one step early
+  // so that step j+1 can read the first operands of K_{j+3}, its successor's,
+  // before this barrier (see step()).
   auto end_step = [&](int j) __attribute__((always_inline)) {
     if (VALIAS) {
-      wait_copies_below(j + 3 < n_tiles ? KCOPY : 0);
+      wait_copies_below(0);
       barrier_keep_copies();
       if (j + 4 < n_tiles) issue_k(j + 4);
     } else {
@@ -397,8 +403,13 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
   auto step = [&](int j, f32x4 (&sb)[2][2], f32x4 (&sa)[2][2], int par) __attribute__((always_inline)) {
     const uint32_t ta = ktile(j + 1);
     const uint32_t tv = vtile(j);
+    const uint32_t tn = ktile(j + 2);
+    // The first AHEAD operands of this step were read at the end of the step
+    // before (with V read out of the K rows); else read them now.
+    if (!VALIAS) {
 #pragma unroll
-    for (int u = 0; u < AHEAD; ++u) read_op(par, u, ta, tv);
+      for (int u = 0; u < AHEAD; ++u) read_op(par, u, ta, tv);
+    }
     // The scores were complete one MFMA phase ago; order the reads here.
     asm volatile("s_nop 0" : "+v"(sb[0][0]), "+v"(sb[0][1]), "+v"(sb[1][0]), "+v"(sb[1][1]));
     // Only the last list tile can be partial: keys past n_valid are masked.
@@ -462,7 +473,12 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
 #pragma unroll
     for (int q = 0; q < 2 * NDT; ++q) {
       const int dt = q >> 1, ht = q & 1, u = NKOP + dt;
-      if (ht == 0) read_op(par, u + AHEAD, ta, tv);
+      if (ht == 0) {
+        if (u + AHEAD < NOPS)
+          read_op(par, u + AHEAD, ta, tv);
+        else if (VALIAS)  // the next step's first K operands (K_{j+2}: landed at end_step(j-1))
+          op[slot(par, u + AHEAD)] = kread(tn, u + AHEAD - NOPS);
+      }
       Mm::a(oacc[dt][ht], op[slot(par, u)], pop[ht]);
       if (q == PREP_AT) prep_k(next_k_copy(j));
     }
@@ -492,6 +508,10 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0[0][0]), "+v"(s0[0][1]), "+v"(s0[1][0]), "+v"(s0[1][1]));
     prep_k(next_k_copy(-1));
     end_step(-1);
+    if (VALIAS) {
+#pragma unroll
+      for (int u = 0; u < AHEAD; ++u) read_op(0, u, ktile(1), vtile(0));
+    }
   }
   for (int j = 0; j < n_tiles; j += 2) {
     step(j, s0, s1, 0);
