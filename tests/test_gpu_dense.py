@@ -57,6 +57,16 @@ def test_gqa_causal_mask(dtype, thr):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_gqa_head_groups_unequal_lengths(causal):
+    # Eight (batch, KV head) pairs and two query heads per KV head: the work
+    # decode gives the two head groups different pair orders; the batches
+    # have different lengths.
+    _, q, k, v = synth.dense_inputs(12 + causal, 2, 8, 4, 300, 300, 128, 128, "bf16")
+    sl = torch.tensor([300, 170], dtype=torch.int32)
+    run_dense("gqa_groups_causal%d" % causal, q, k, v, 1 / math.sqrt(128), causal, None, sl, sl)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_mask_aligned_rows(causal):
     # Mask rows 16-byte aligned (Skv = 336): full 64-key tiles take the
     # coalesced 16-byte mask loads, the partial last tile the byte loads.
