@@ -379,10 +379,10 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
   };
 
   // End of step j: this wave's copies of tile j+3 have landed (with V read
-  // out of the K rows; else those of tiles j+1, j+2), barrier, then the
-  // copies into the slots step j left. Tile j+3 is waited for one step early
-  // so that step j+1 can read the first operands of K_{j+3}, its successor's,
-  // before this barrier (see step()).
+  // out of the K rows; else its copies of V_{j+1} and K_{j+2}), barrier, then
+  // the copies into the slots step j left. Tile j+3 is waited for one step
+  // early so that it is visible during step j+1, whose last MFMAs read the
+  // first K operands of step j+2 from it (see step()).
   auto end_step = [&](int j) __attribute__((always_inline)) {
     if (VALIAS) {
       wait_copies_below(0);
