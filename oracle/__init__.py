@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the attention forward pass.
+"""fp64 CPU oracle for the attention forward pass and its gradients.
 
 TEST INFRASTRUCTURE. This package is the independent reference that the GPU
 library is checked against. It shares no code with the GPU path and only the
@@ -40,7 +40,11 @@ def _load():
                                                 P, P, ctypes.c_int]
         lib.oracle_attn_topk.argtypes = [P, P, I64, P, P, I64, I64, I64, I64, I64, P, I64,
                                          ctypes.c_double, P, P, ctypes.c_int]
-        for f in (lib.oracle_attn_dense, lib.oracle_attn_blocksparse, lib.oracle_attn_topk):
+        lib.oracle_attn_dense_bwd.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, I64,
+                                              P, P, P, P, ctypes.c_int, ctypes.c_double, P, P, P,
+                                              ctypes.c_int]
+        for f in (lib.oracle_attn_dense, lib.oracle_attn_blocksparse, lib.oracle_attn_topk,
+                  lib.oracle_attn_dense_bwd):
             f.restype = ctypes.c_int
         lib.oracle_hardware_threads.restype = ctypes.c_int
         _lib = lib
@@ -203,3 +207,23 @@ def attn_topk(q, k, v, idx, *, scale, rows=None, nthreads=0):
     if rows is None:
         return o.reshape(T, Hq, Dv), lse.reshape(T, Hq)
     return o, lse
+
+
+def attn_dense_bwd(q, k, v, dout, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k=None,
+                   nthreads=0):
+    """Gradients (dq, dk, dv) of dense attention with respect to q, k, v given
+    the output gradient dout [B,Hq,Sq,Dv]; same masking arguments as
+    attn_dense. float64 numpy arrays shaped like q, k, v (dk, dv summed over
+    the query heads of each KV head)."""
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Skv, Dv = v.shape
+    qa, ka, va, da = _f64(q), _f64(k), _f64(v), _f64(dout)
+    m, ms = (None, None) if mask is None else _mask_strides(mask, B, Hq, Sq, Skv)
+    sq, sk = _np(seqlens_q, np.int32), _np(seqlens_k, np.int32)
+    dq = np.zeros((B, Hq, Sq, D), dtype=np.float64)
+    dk = np.zeros((B, Hkv, Skv, D), dtype=np.float64)
+    dv = np.zeros((B, Hkv, Skv, Dv), dtype=np.float64)
+    _check(_load().oracle_attn_dense_bwd(_ptr(qa), _ptr(ka), _ptr(va), _ptr(da), B, Hq, Hkv, Sq, Skv,
+                                         D, Dv, _ptr(m), _ptr(ms), _ptr(sq), _ptr(sk), int(bool(causal)),
+                                         float(scale), _ptr(dq), _ptr(dk), _ptr(dv), int(nthreads)))
+    return dq, dk, dv

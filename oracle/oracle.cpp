@@ -1,4 +1,5 @@
-// Reference attention forward in fp64 on the CPU.
+// Reference attention forward (and the gradients of the dense forward) in
+// fp64 on the CPU.
 //
 // TEST INFRASTRUCTURE ONLY. This file is the oracle that the GPU path is
 // checked against. It shares no code with the GPU library: no header, no
@@ -150,6 +151,99 @@ int oracle_attn_dense(const double* q_rows, const int64_t* row_ids, int64_t nrow
     const double* vb = v + (b * Hkv + hkv) * Skv * Dv;
     attend_row(q_rows + r * D, D, Dv, keys, [&](int64_t j) { return kb + j * D; },
                [&](int64_t j) { return vb + j * Dv; }, scale, o + r * Dv, lse + r);
+    return ORACLE_OK;
+  });
+}
+
+// Gradients of dense attention (same key sets as oracle_attn_dense) with
+// respect to q, k and v, given the gradient dO of the output. Written out from
+// the definitions, as on the ops-transformer FlashAttentionScoreGrad pytest
+// page (section 5.2, the backward golden) and the PyPTO BSA README (section 1:
+// dV carries no scale, dQ and dK carry scaleValue; GQA sums dK and dV over the
+// query heads of a KV head):
+//
+//   P_ij  = exp(s_ij - LSE_i) over the row's key set (s = scale q.k)
+//   dV_j  = sum_i P_ij dO_i
+//   dP_ij = dO_i . v_j
+//   dS_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij')
+//   dQ_i  = scale sum_j dS_ij k_j,     dK_j = scale sum_i dS_ij q_i
+//
+// q [B,Hq,Sq,D], dout [B,Hq,Sq,Dv], k [B,Hkv,Skv,D], v [B,Hkv,Skv,Dv],
+// dq like q, dk like k, dv like v: contiguous fp64. Rows with an empty key set
+// contribute nothing. Runs one (b, kv head) per thread, so the dK / dV sums
+// have one writer each.
+int oracle_attn_dense_bwd(const double* q, const double* k, const double* v, const double* dout,
+                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                          int64_t Dv, const uint8_t* mask, const int64_t* ms,
+                          const int32_t* seqlens_q, const int32_t* seqlens_k, int causal,
+                          double scale, double* dq, double* dk, double* dv, int nthreads) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || D <= 0 || Dv <= 0) return ORACLE_ERR_ARG;
+  if (Hq % Hkv != 0) return ORACLE_ERR_ARG;
+  if (B * Hq * Sq > 0 && (!q || !dout || !dq)) return ORACLE_ERR_ARG;
+  if (B * Hkv * Skv > 0 && (!k || !v || !dk || !dv)) return ORACLE_ERR_ARG;
+  if (mask && !ms) return ORACLE_ERR_ARG;
+  const int64_t G = Hq / Hkv;
+  return parallel_rows(B * Hkv, nthreads, [&](int64_t bk) -> int {
+    const int64_t b = bk / Hkv, hkv = bk % Hkv;
+    const double* kb = k + bk * Skv * D;
+    const double* vb = v + bk * Skv * Dv;
+    double* dkb = dk + bk * Skv * D;
+    double* dvb = dv + bk * Skv * Dv;
+    for (int64_t x = 0; x < Skv * D; ++x) dkb[x] = 0.0;
+    for (int64_t x = 0; x < Skv * Dv; ++x) dvb[x] = 0.0;
+    const int64_t Lq = seqlens_q ? seqlens_q[b] : Sq;
+    const int64_t Lk = seqlens_k ? seqlens_k[b] : Skv;
+    std::vector<int64_t> keys;
+    std::vector<double> s, p, dp;
+    for (int64_t hq = hkv * G; hq < (hkv + 1) * G; ++hq) {
+      for (int64_t i = 0; i < Sq; ++i) {
+        const int64_t row = (b * Hq + hq) * Sq + i;
+        const double* qi = q + row * D;
+        const double* doi = dout + row * Dv;
+        double* dqi = dq + row * D;
+        for (int64_t d = 0; d < D; ++d) dqi[d] = 0.0;
+        keys.clear();
+        if (i < Lq) {
+          for (int64_t j = 0; j < std::min(Lk, Skv); ++j) {
+            if (causal && j > i + (Lk - Lq)) continue;
+            if (mask && mask[b * ms[0] + hq * ms[1] + i * ms[2] + j * ms[3]] != 0) continue;
+            keys.push_back(j);
+          }
+        }
+        if (keys.empty()) continue;
+        const size_t n = keys.size();
+        s.assign(n, 0.0);
+        p.assign(n, 0.0);
+        dp.assign(n, 0.0);
+        double m = -std::numeric_limits<double>::infinity();
+        for (size_t t = 0; t < n; ++t) {
+          const double* kj = kb + keys[t] * D;
+          double dot = 0.0;
+          for (int64_t d = 0; d < D; ++d) dot += qi[d] * kj[d];
+          s[t] = scale * dot;
+          m = std::max(m, s[t]);
+        }
+        double l = 0.0;
+        for (size_t t = 0; t < n; ++t) l += std::exp(s[t] - m);
+        double delta = 0.0;  // sum_j P_ij dP_ij
+        for (size_t t = 0; t < n; ++t) {
+          p[t] = std::exp(s[t] - m) / l;
+          const double* vj = vb + keys[t] * Dv;
+          double dot = 0.0;
+          for (int64_t d = 0; d < Dv; ++d) dot += doi[d] * vj[d];
+          dp[t] = dot;
+          delta += p[t] * dot;
+        }
+        for (size_t t = 0; t < n; ++t) {
+          const int64_t j = keys[t];
+          const double ds = p[t] * (dp[t] - delta);
+          const double* kj = kb + j * D;
+          for (int64_t d = 0; d < D; ++d) dqi[d] += scale * ds * kj[d];
+          for (int64_t d = 0; d < D; ++d) dkb[j * D + d] += scale * ds * qi[d];
+          for (int64_t d = 0; d < Dv; ++d) dvb[j * Dv + d] += p[t] * doi[d];
+        }
+      }
+    }
     return ORACLE_OK;
   });
 }

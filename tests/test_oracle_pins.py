@@ -494,3 +494,86 @@ def test_page_self_weight_and_floor_are_reproduced():
     assert np.all((w > 0) & (w < 1))
     floor = metrics.rel_l2(metrics.round_to(o, torch.bfloat16), o)
     assert abs(floor - fl["value"]) < 0.03 * fl["value"]
+
+
+# ---------------------------------------------------------------- backward
+
+def _loss(q, k, v, dout, **kw):
+    """L = sum(O * dout): its gradient with respect to q, k, v is what the
+    backward oracle returns for output gradient dout."""
+    o, _ = oracle.attn_dense(q, k, v, **kw)
+    return float((o.reshape(dout.shape) * dout.numpy()).sum())
+
+
+@pytest.mark.parametrize("causal,use_mask,use_seqlens", [(False, False, False), (True, False, False),
+                                                         (True, True, True)])
+def test_backward_matches_finite_differences(causal, use_mask, use_seqlens):
+    # Central differences of the forward oracle along random directions pin
+    # every term of the backward (a dropped or mis-signed term, a missing GQA
+    # sum or scale shows up as a mismatch of order one).
+    g = torch.Generator().manual_seed(7 + causal + 2 * use_mask)
+    B, Hq, Hkv, Sq, Skv, D = 2, 4, 2, 5, 7, 6
+    q = torch.randn(B, Hq, Sq, D, generator=g, dtype=torch.float64)
+    k = torch.randn(B, Hkv, Skv, D, generator=g, dtype=torch.float64)
+    v = torch.randn(B, Hkv, Skv, D, generator=g, dtype=torch.float64)
+    dout = torch.randn(B, Hq, Sq, D, generator=g, dtype=torch.float64)
+    kw = dict(scale=0.37, causal=causal)
+    if use_mask:
+        kw["mask"] = (torch.rand(Sq, Skv, generator=g) < 0.3).to(torch.uint8)
+    if use_seqlens:
+        kw["seqlens_q"] = torch.tensor([5, 3], dtype=torch.int32)
+        kw["seqlens_k"] = torch.tensor([7, 4], dtype=torch.int32)
+    dq, dk, dv = oracle.attn_dense_bwd(q, k, v, dout, **kw)
+    eps = 1e-5
+    for name, x, gx in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for trial in range(3):
+            u = torch.randn(x.shape, generator=g, dtype=torch.float64)
+            args = {"q": q, "k": k, "v": v}
+            args[name] = x + eps * u
+            lp = _loss(args["q"], args["k"], args["v"], dout, **kw)
+            args[name] = x - eps * u
+            lm = _loss(args["q"], args["k"], args["v"], dout, **kw)
+            fd = (lp - lm) / (2 * eps)
+            an = float((gx * u.numpy()).sum())
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), (name, trial, fd, an)
+
+
+def test_backward_single_key_rows_and_uniform_rows():
+    # A row with one key has P = 1: dS = 0, so it adds nothing to dq / dk and
+    # adds its dout to that key's dv. With q = 0 every score is 0 and P is
+    # uniform over the row's keys: dv_j = sum over rows that see j of dout_i / n_i.
+    B, H, S, D = 1, 1, 4, 3
+    g = torch.Generator().manual_seed(3)
+    k = torch.randn(B, H, S, D, generator=g, dtype=torch.float64)
+    v = torch.randn(B, H, S, D, generator=g, dtype=torch.float64)
+    dout = torch.randn(B, H, S, D, generator=g, dtype=torch.float64)
+    q = torch.zeros(B, H, S, D, dtype=torch.float64)
+    dq, dk, dv = oracle.attn_dense_bwd(q, k, v, dout, scale=0.5, causal=True)
+    expect = np.zeros((S, D))
+    for i in range(S):  # causal row i sees keys 0..i, each with P = 1 / (i + 1)
+        for j in range(i + 1):
+            expect[j] += dout[0, 0, i].numpy() / (i + 1)
+    np.testing.assert_allclose(dv[0, 0], expect, rtol=0, atol=1e-15)
+    # row 0 sees key 0 only: no contribution to dq[0]
+    assert np.all(dq[0, 0, 0] == 0.0)
+    q2 = torch.randn(B, H, S, D, generator=g, dtype=torch.float64)
+    dq2, dk2, dv2 = oracle.attn_dense_bwd(q2[:, :, :1], k[:, :, :1], v[:, :, :1], dout[:, :, :1], scale=0.5)
+    assert np.all(dq2 == 0.0) and np.all(dk2 == 0.0)
+    np.testing.assert_array_equal(dv2[0, 0, 0], dout[0, 0, 0].numpy())
+
+
+def test_backward_gqa_sums_over_query_heads():
+    # GQA with G query heads per KV head equals multi-head attention on KV
+    # heads repeated G times, with dk / dv summed over each group.
+    g = torch.Generator().manual_seed(11)
+    B, Hkv, G, S, D = 1, 2, 3, 6, 4
+    q = torch.randn(B, Hkv * G, S, D, generator=g, dtype=torch.float64)
+    k = torch.randn(B, Hkv, S, D, generator=g, dtype=torch.float64)
+    v = torch.randn(B, Hkv, S, D, generator=g, dtype=torch.float64)
+    dout = torch.randn(B, Hkv * G, S, D, generator=g, dtype=torch.float64)
+    dq, dk, dv = oracle.attn_dense_bwd(q, k, v, dout, scale=0.4, causal=True)
+    kr, vr = k.repeat_interleave(G, dim=1), v.repeat_interleave(G, dim=1)
+    dq2, dk2, dv2 = oracle.attn_dense_bwd(q, kr, vr, dout, scale=0.4, causal=True)
+    np.testing.assert_allclose(dq, dq2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk, dk2.reshape(B, Hkv, G, S, D).sum(2), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, dv2.reshape(B, Hkv, G, S, D).sum(2), rtol=0, atol=1e-12)
