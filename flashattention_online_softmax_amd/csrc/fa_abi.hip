@@ -328,6 +328,66 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
   return hip_status(fa::launch_topk(to_dt(q->dtype), p, (hipStream_t)stream));
 }
 
+fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* o,
+                 const fa_tensor* lse, const fa_tensor* dout, int causal, float scale,
+                 const fa_tensor* delta, const fa_tensor* dq, const fa_tensor* dk,
+                 const fa_tensor* dv, void* stream) {
+  clear_error();
+  fa_status s = check_bnsd(q, k, v, o, lse, scale, 0.f);
+  if (s != FA_OK) return s;
+  if (causal != 0 && causal != 1) return fail(FA_ERR_VALUE, "causal must be 0 or 1");
+  if (q->dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "the backward takes f16 or bf16");
+  if (q->shape[3] != 128) return fail(FA_ERR_UNSUPPORTED, "the backward supports head dim 128 only");
+  if ((s = check_tensor("dout", dout, 4, true)) != FA_OK) return s;
+  if ((s = check_tensor("dq", dq, 4, true)) != FA_OK) return s;
+  if ((s = check_tensor("dk", dk, 4, true)) != FA_OK) return s;
+  if ((s = check_tensor("dv", dv, 4, true)) != FA_OK) return s;
+  if ((s = check_tensor("delta", delta, 3, false)) != FA_OK) return s;
+  if ((s = check_dtype("dout", dout, q->dtype)) != FA_OK) return s;
+  if ((s = check_dtype("dq", dq, q->dtype)) != FA_OK) return s;
+  if ((s = check_dtype("dk", dk, q->dtype)) != FA_OK) return s;
+  if ((s = check_dtype("dv", dv, q->dtype)) != FA_OK) return s;
+  if ((s = check_dtype("delta", delta, FA_F32)) != FA_OK) return s;
+  for (int i = 0; i < 4; ++i) {
+    if (dout->shape[i] != o->shape[i]) return fail(FA_ERR_SHAPE, "dout must be shaped like o");
+    if (dq->shape[i] != q->shape[i]) return fail(FA_ERR_SHAPE, "dq must be shaped like q");
+    if (dk->shape[i] != k->shape[i]) return fail(FA_ERR_SHAPE, "dk must be shaped like k");
+    if (dv->shape[i] != v->shape[i]) return fail(FA_ERR_SHAPE, "dv must be shaped like v");
+  }
+  for (int i = 0; i < 3; ++i)
+    if (delta->shape[i] != lse->shape[i]) return fail(FA_ERR_SHAPE, "delta must be [B, Hq, Sq]");
+  if ((s = check_contiguous("delta", delta)) != FA_OK) return s;
+  fa::BwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q->data;
+  p.k = k->data;
+  p.v = v->data;
+  p.o = o->data;
+  p.dout = dout->data;
+  p.lse = (const float*)lse->data;
+  p.delta = (float*)delta->data;
+  p.dq = dq->data;
+  p.dk = dk->data;
+  p.dv = dv->data;
+  const fa_tensor* ts[8] = {q, k, v, o, dout, dq, dk, dv};
+  int64_t* st[8][3] = {{&p.q_sb, &p.q_sh, &p.q_ss},    {&p.k_sb, &p.k_sh, &p.k_ss},
+                       {&p.v_sb, &p.v_sh, &p.v_ss},    {&p.o_sb, &p.o_sh, &p.o_ss},
+                       {&p.do_sb, &p.do_sh, &p.do_ss}, {&p.dq_sb, &p.dq_sh, &p.dq_ss},
+                       {&p.dk_sb, &p.dk_sh, &p.dk_ss}, {&p.dv_sb, &p.dv_sh, &p.dv_ss}};
+  for (int t = 0; t < 8; ++t)
+    for (int i = 0; i < 3; ++i) *st[t][i] = ts[t]->stride[i];
+  p.B = (int32_t)q->shape[0];
+  p.Hq = (int32_t)q->shape[1];
+  p.Hkv = (int32_t)k->shape[1];
+  p.G = p.Hkv > 0 ? p.Hq / p.Hkv : 1;
+  p.Sq = (int32_t)q->shape[2];
+  p.Skv = (int32_t)k->shape[2];
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  if ((int64_t)p.B * p.Hq * p.Sq == 0 && (int64_t)p.B * p.Hkv * p.Skv == 0) return FA_OK;
+  return hip_status(fa::launch_bwd(to_dt(q->dtype), causal != 0, p, (hipStream_t)stream));
+}
+
 const char* fa_status_str(fa_status s) {
   switch (s) {
     case FA_OK: return "FA_OK";

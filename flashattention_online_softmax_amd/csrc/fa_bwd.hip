@@ -1,0 +1,290 @@
+// Attention backward for 16-bit inputs on gfx950 (D = 128; dense, causal,
+// GQA): dQ, dK, dV from Q, K, V, the forward's O and LSE, and dO.
+//
+// Method: the backward formulas of the ops-transformer FlashAttentionScoreGrad
+// pytest page (section 5.2) with the recomputation strategy of the PyPTO BSA
+// README (section 3: the backward keeps only O and LSE and recomputes
+// P = exp(scale S - LSE)):
+//   P = exp2(scale log2e S - log2e LSE),  dP = dO V^T,  Delta_i = dO_i . O_i,
+//   dS = P (dP - Delta),  dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K,
+// with dK and dV summed over the query heads of a KV head (BSA README,
+// section 1).
+//
+// Three kernels, none of them with atomics:
+//   * delta: Delta_i = dO_i . O_i in fp32, one row per 16 lanes.
+//   * dkdv: a workgroup owns 128 keys of one KV head (4 waves x 32 keys, K and
+//     V of its keys resident as MFMA B operands) and sweeps the query tiles
+//     (32 rows) of every query head of the group: S = Q K^T, dP = dO V^T,
+//     then dV^T += dO^T P and dK^T += Q^T dS on v_mfma_f32_32x32x16, P and dS
+//     rounded to 16 bits as B operands straight from the accumulator layout.
+//   * dq: a workgroup owns 128 query rows of one head (Q and dO resident) and
+//     sweeps the key tiles: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
+// The operands read transposed (dO^T, Q^T, K^T) come from row-major LDS tiles
+// through ds_read_b64_tr_b16, in the key (query) order in which the
+// accumulator holds P and dS, so the contraction pairs the right elements.
+// Each LDS tile is 32 rows x 128, stored twice when it is read both ways:
+// 16-byte chunks XOR-swizzled by row & 15 for the row reads and by
+// 4 (row & 3) for the transposing reads.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int BD = 128;    // head dim
+constexpr int TR = 32;     // rows of an LDS tile
+constexpr int NWB = 4;     // waves per workgroup
+constexpr int BLK = 32 * NWB;  // keys (dkdv) or query rows (dq) per workgroup
+
+__device__ __forceinline__ int rsw(int row, int ch) { return ch ^ (row & 15); }
+__device__ __forceinline__ int tsw(int row, int ch) { return ch ^ ((row & 3) << 2); }
+
+// Cooperative copy of rows r0 .. r0+31 (clamped to n - 1; n >= 1) of a
+// row-major [*, 128] 16-bit matrix into LDS, once per requested swizzle.
+__device__ __forceinline__ void load_tile(uint16_t* dst_r, uint16_t* dst_t, const uint16_t* src,
+                                          int64_t stride, int r0, int n) {
+#pragma unroll
+  for (int u = 0; u < (TR * BD / 8) / (64 * NWB); ++u) {
+    const int id = (int)threadIdx.x + u * 64 * NWB;
+    const int row = id >> 4, ch = id & 15;
+    const int gr = min(r0 + row, n - 1);
+    const u32x4 v = *(const u32x4*)(src + (int64_t)gr * stride + ch * 8);
+    if (dst_r) *(u32x4*)(dst_r + row * BD + rsw(row, ch) * 8) = v;
+    if (dst_t) *(u32x4*)(dst_t + row * BD + tsw(row, ch) * 8) = v;
+  }
+}
+
+// A operand "rows": lane (c, h) holds tile row c, columns 16 ks + 8 h .. +7.
+__device__ __forceinline__ u32x4 row_op(const uint16_t* t, int ks) {
+  const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
+  return *(const u32x4*)(t + c * BD + rsw(c, 2 * ks + h) * 8);
+}
+// A operand "transposed": M index = tile column 32 dt + (lane & 31); the 8 k
+// values of lane half h are tile rows 16 ks + 4 h + 0..3 and 16 ks + 8 + 4 h
+// + 0..3, the order in which a 32x32 accumulator holds its rows.
+__device__ __forceinline__ u32x4 tr_op(const uint16_t* t, int dt, int ks) {
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  const int vrow = 4 * h + ((lane & 15) >> 2);
+  const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const uint16_t* p = t + (16 * ks + vrow) * BD + tsw(vrow, col >> 3) * 8 + (col & 7);
+  const u32x2 lo = lds_read_tr16(p);
+  const u32x2 hi = lds_read_tr16(p + 8 * BD);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+// B operand from global memory: lane (c, h) holds row r of a row-major
+// matrix, columns 16 ks + 8 h .. +7, for the 8 k-steps over the head dim.
+__device__ __forceinline__ void load_bop(u32x4 (&op)[BD / 16], const uint16_t* base, int64_t stride, int r) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int ks = 0; ks < BD / 16; ++ks) op[ks] = *(const u32x4*)(base + (int64_t)r * stride + 16 * ks + 8 * h);
+}
+// Accumulator elements 8 ks .. 8 ks + 7 rounded to 16 bits: the B operand of
+// k-step ks over the accumulator's rows.
+template <class T>
+__device__ __forceinline__ u32x4 pack_b(const f32x16& a, int ks) {
+  return u32x4{T::pack2(a[8 * ks], a[8 * ks + 1]), T::pack2(a[8 * ks + 2], a[8 * ks + 3]),
+               T::pack2(a[8 * ks + 4], a[8 * ks + 5]), T::pack2(a[8 * ks + 6], a[8 * ks + 7])};
+}
+// Stores accumulator tiles acc[dt] (rows = head dim 32 dt + ..., column =
+// lane's row r of the output) times mul as 16-bit values: 4 consecutive
+// elements per store.
+template <class T>
+__device__ __forceinline__ void store_t(uint16_t* base, int64_t stride, int r, const f32x16 (&acc)[BD / 32], float mul) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int dt = 0; dt < BD / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x2 v = {T::pack2(acc[dt][4 * g] * mul, acc[dt][4 * g + 1] * mul),
+                       T::pack2(acc[dt][4 * g + 2] * mul, acc[dt][4 * g + 3] * mul)};
+      *(u32x2*)(base + (int64_t)r * stride + 32 * dt + 8 * g + 4 * h) = v;
+    }
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    const int64_t i = row % p.Sq, bh = row / p.Sq, hq = bh % p.Hq, b = bh / p.Hq;
+    const uint16_t* o = (const uint16_t*)p.o + b * p.o_sb + hq * p.o_sh + i * p.o_ss + 8 * sub;
+    const uint16_t* d = (const uint16_t*)p.dout + b * p.do_sb + hq * p.do_sh + i * p.do_ss + 8 * sub;
+    const u32x4 ov = *(const u32x4*)o, dv = *(const u32x4*)d;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = T::dot2(ov[e], dv[e], acc);
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  if (row < rows && sub == 0) p.delta[row] = acc;
+}
+
+template <class T, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t sQr[TR * BD], sQt[TR * BD], sOr[TR * BD], sOt[TR * BD];
+  __shared__ float sL[TR], sD[TR];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
+  const int bk = blockIdx.y, b = bk / p.Hkv, hkv = bk % p.Hkv;
+  const int k0 = blockIdx.x * BLK;
+  const int key = k0 + 32 * w + c;  // this lane's key (column of S)
+  const int diag = p.Skv - p.Sq;
+  const uint16_t* kg = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh;
+  const uint16_t* vg = (const uint16_t*)p.v + (int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh;
+  u32x4 kop[BD / 16], vop[BD / 16];
+  load_bop(kop, kg, p.k_ss, min(key, p.Skv - 1));
+  load_bop(vop, vg, p.v_ss, min(key, p.Skv - 1));
+  f32x16 dv_t[BD / 32], dk_t[BD / 32];
+#pragma unroll
+  for (int dt = 0; dt < BD / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dv_t[dt][i] = dk_t[dt][i] = 0.f;
+  // Query rows that can see a key of this block: i >= k0 - diag (causal).
+  const int qfirst = CAUSAL ? max(0, k0 - diag) : 0;
+  const int nqt = p.Sq > qfirst ? (p.Sq - qfirst + TR - 1) / TR : 0;
+  for (int hq = hkv * p.G; hq < (hkv + 1) * p.G; ++hq) {
+    const uint16_t* qg = (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh;
+    const uint16_t* dg = (const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hq * p.do_sh;
+    const float* lg = p.lse + ((int64_t)b * p.Hq + hq) * p.Sq;
+    const float* delg = p.delta + ((int64_t)b * p.Hq + hq) * p.Sq;
+    for (int t = 0; t < nqt; ++t) {
+      const int q0 = qfirst + t * TR;
+      __syncthreads();  // the previous tile's reads are done
+      load_tile(sQr, sQt, qg, p.q_ss, q0, p.Sq);
+      load_tile(sOr, sOt, dg, p.do_ss, q0, p.Sq);
+      if (threadIdx.x < TR) {
+        const int i = q0 + threadIdx.x;
+        const float l = i < p.Sq ? lg[i] : -INFINITY;
+        // rows without keys (LSE = -inf) and padding rows get P = 0
+        sL[threadIdx.x] = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
+        sD[threadIdx.x] = i < p.Sq ? delg[i] : 0.f;
+      }
+      __syncthreads();
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < BD / 16; ++ks) {
+        s = T::mfma(row_op(sQr, ks), kop[ks], s);
+        dp = T::mfma(row_op(sOr, ks), vop[ks], dp);
+      }
+      // Element i: query row q0 + r, r = 8 (i / 4) + 4 h + i % 4; key `key`.
+      f32x16 pm, dsm;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+        const int qi = q0 + r;
+        bool ok = key < p.Skv && qi < p.Sq;
+        if (CAUSAL) ok = ok && key <= qi + diag;
+        const float pv = ok ? fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -sL[r])) : 0.f;
+        pm[i] = pv;
+        dsm[i] = pv * (dp[i] - sD[r]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < TR / 16; ++ks) {
+        const u32x4 pb = pack_b<T>(pm, ks), db = pack_b<T>(dsm, ks);
+#pragma unroll
+        for (int dt = 0; dt < BD / 32; ++dt) {
+          dv_t[dt] = T::mfma(tr_op(sOt, dt, ks), pb, dv_t[dt]);
+          dk_t[dt] = T::mfma(tr_op(sQt, dt, ks), db, dk_t[dt]);
+        }
+      }
+    }
+  }
+  if (key < p.Skv) {
+    store_t<T>((uint16_t*)p.dk + (int64_t)b * p.dk_sb + (int64_t)hkv * p.dk_sh, p.dk_ss, key, dk_t, p.scale);
+    store_t<T>((uint16_t*)p.dv + (int64_t)b * p.dv_sb + (int64_t)hkv * p.dv_sh, p.dv_ss, key, dv_t, 1.f);
+  }
+}
+
+template <class T, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t sKr[TR * BD], sKt[TR * BD], sVr[TR * BD];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
+  const int bh = blockIdx.y, b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.G;
+  const int q0 = blockIdx.x * BLK;
+  const int qi = q0 + 32 * w + c;  // this lane's query row (column of S^T)
+  const int diag = p.Skv - p.Sq;
+  const uint16_t* qg = (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh;
+  const uint16_t* dg = (const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hq * p.do_sh;
+  const uint16_t* kg = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh;
+  const uint16_t* vg = (const uint16_t*)p.v + (int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh;
+  u32x4 qop[BD / 16], dop[BD / 16];
+  load_bop(qop, qg, p.q_ss, min(qi, p.Sq - 1));
+  load_bop(dop, dg, p.do_ss, min(qi, p.Sq - 1));
+  float l2 = INFINITY, del = 0.f;  // padding rows and rows without keys: P = 0
+  if (qi < p.Sq) {
+    const float l = p.lse[((int64_t)b * p.Hq + hq) * p.Sq + qi];
+    l2 = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
+    del = p.delta[((int64_t)b * p.Hq + hq) * p.Sq + qi];
+  }
+  f32x16 dq_t[BD / 32];
+#pragma unroll
+  for (int dt = 0; dt < BD / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq_t[dt][i] = 0.f;
+  // Keys any row of this block sees: j <= q0 + BLK - 1 + diag (causal).
+  const int kend = CAUSAL ? max(0, min(p.Skv, q0 + BLK + diag)) : p.Skv;
+  const int nkt = (kend + TR - 1) / TR;
+  for (int t = 0; t < nkt; ++t) {
+    const int j0 = t * TR;
+    __syncthreads();
+    load_tile(sKr, sKt, kg, p.k_ss, j0, p.Skv);
+    load_tile(sVr, nullptr, vg, p.v_ss, j0, p.Skv);
+    __syncthreads();
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < BD / 16; ++ks) {
+      s = T::mfma(row_op(sKr, ks), qop[ks], s);
+      dp = T::mfma(row_op(sVr, ks), dop[ks], dp);
+    }
+    // Element i: key j0 + r, r = 8 (i / 4) + 4 h + i % 4; query row qi.
+    f32x16 dsm;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kj = j0 + 8 * (i >> 2) + 4 * h + (i & 3);
+      bool ok = kj < p.Skv && qi < p.Sq;
+      if (CAUSAL) ok = ok && kj <= qi + diag;
+      const float pv = ok ? fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -l2)) : 0.f;
+      dsm[i] = pv * (dp[i] - del);
+    }
+#pragma unroll
+    for (int ks = 0; ks < TR / 16; ++ks) {
+      const u32x4 db = pack_b<T>(dsm, ks);
+#pragma unroll
+      for (int dt = 0; dt < BD / 32; ++dt) dq_t[dt] = T::mfma(tr_op(sKt, dt, ks), db, dq_t[dt]);
+    }
+  }
+  if (qi < p.Sq) store_t<T>((uint16_t*)p.dq + (int64_t)b * p.dq_sb + (int64_t)hq * p.dq_sh, p.dq_ss, qi, dq_t, p.scale);
+}
+
+template <class T, bool CAUSAL>
+hipError_t launch_bwd_t(BwdParams& p, hipStream_t st) {
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
+  if (rows > 0) {
+    hipLaunchKernelGGL((bwd_delta_kernel<T>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.Skv > 0 && p.B * p.Hkv > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, CAUSAL>), dim3((unsigned)((p.Skv + BLK - 1) / BLK), (unsigned)(p.B * p.Hkv)),
+                       dim3(256), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (rows > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<T, CAUSAL>), dim3((unsigned)((p.Sq + BLK - 1) / BLK), (unsigned)(p.B * p.Hq)),
+                       dim3(256), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(Dt dt, bool causal, BwdParams& p, hipStream_t stream) {
+  if (dt == Dt::BF16) return causal ? launch_bwd_t<BF16, true>(p, stream) : launch_bwd_t<BF16, false>(p, stream);
+  return causal ? launch_bwd_t<F16, true>(p, stream) : launch_bwd_t<F16, false>(p, stream);
+}
+
+}  // namespace fa

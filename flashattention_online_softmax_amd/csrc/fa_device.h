@@ -40,6 +40,10 @@ struct F16 {
     const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), one, acc, false);
   }
+  // acc + a.lo b.lo + a.hi b.hi in fp32 (v_dot2_f32_f16).
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
+  }
 };
 
 struct BF16 {
@@ -56,6 +60,10 @@ struct BF16 {
   static __device__ __forceinline__ float sum2(uint32_t packed, float acc) {
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
+  }
+  // acc + a.lo b.lo + a.hi b.hi in fp32 (v_dot2_f32_bf16).
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
   }
 };
 

@@ -56,6 +56,31 @@ struct TopkParams {
   float scale_log2;
 };
 
+// Attention backward parameters (16-bit, D = 128). Strides in elements.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;   // [B, Hq, Sq] contiguous
+  float* delta;       // [B, Hq, Sq] contiguous: dO . O per row (written)
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int64_t do_sb, do_sh, do_ss;
+  int64_t dq_sb, dq_sh, dq_ss;
+  int64_t dk_sb, dk_sh, dk_ss;
+  int64_t dv_sb, dv_sh, dv_ss;
+  int32_t B, Hq, Hkv, G, Sq, Skv;
+  float scale;
+  float scale_log2;
+};
+
 // Kernel `name` of the run-time loaded code object (the 16-bit dense,
 // block-sparse and top-k kernels) on the current device (loaded on first use).
 hipError_t code_object_function(const char* name, hipFunction_t* fn);
@@ -64,5 +89,6 @@ hipError_t code_object_function(const char* name, hipFunction_t* fn);
 hipError_t launch_dense(Dt dt, int D, bool causal, bool has_mask, bool sparse,
                         FwdParams& p, hipStream_t stream);
 hipError_t launch_topk(Dt dt, TopkParams& p, hipStream_t stream);
+hipError_t launch_bwd(Dt dt, bool causal, BwdParams& p, hipStream_t stream);
 
 }  // namespace fa

@@ -168,6 +168,36 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
                              const fa_tensor* idx, float scale, const fa_tensor* o,
                              const fa_tensor* lse, void* stream);
 
+/*
+ * Attention backward (dense, optional causal mask, GQA): the gradients of the
+ * dense forward's O with respect to q, k and v, given dO. Defined by the
+ * backward formulas of the ops-transformer FlashAttentionScoreGrad pytest page
+ * (section 5.2: dV = P^T dO, dS = P * (dP - rowsum(dP * P)), dQ = scale dS K,
+ * dK = scale dS^T Q) with P recomputed from the forward's LSE as in the PyPTO
+ * BSA README (section 3); dK and dV are summed over the query heads of each KV
+ * head (BSA README, section 1).
+ *
+ *  q, k, v     as fa_fwd (f16 or bf16, D == Dv == 128)
+ *  o           the forward output for these q, k, v, causal, scale
+ *  lse         fp32 [B, Hq, Sq], contiguous: the forward's LSE
+ *  dout        [B, Hq, Sq, Dv], q's dtype: the gradient of the output
+ *  causal      0 or 1, as fa_fwd (bottom-right aligned)
+ *  scale       as fa_fwd
+ *  delta       fp32 [B, Hq, Sq], contiguous, caller-owned workspace; on
+ *              return it holds dO . O per row
+ *  dq, dk, dv  outputs shaped like q, k, v in q's dtype (written, not
+ *              accumulated into)
+ *
+ * Every tensor's rows must start 16-byte aligned (as fa_fwd). Rows without
+ * keys (LSE = -inf) contribute nothing. Returns FA_ERR_UNSUPPORTED for other
+ * head dims or fp32; the library allocates nothing and enqueues three kernels
+ * on `stream`.
+ */
+fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* o,
+                 const fa_tensor* lse, const fa_tensor* dout, int causal, float scale,
+                 const fa_tensor* delta, const fa_tensor* dq, const fa_tensor* dk,
+                 const fa_tensor* dv, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa_status_str(fa_status s);
 

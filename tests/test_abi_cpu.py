@@ -57,7 +57,7 @@ def good(B=2, Hq=4, Hkv=2, S=64, D=128, dt=fa.FA_BF16):
 
 def test_exports_every_declared_function(lib):
     names = fa.declared_functions()
-    assert {"fa_fwd", "fa_fwd_blocksparse", "fa_fwd_topk_gather", "fa_status_str",
+    assert {"fa_fwd", "fa_fwd_blocksparse", "fa_fwd_topk_gather", "fa_bwd", "fa_status_str",
             "fa_last_error", "fa_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -148,6 +148,24 @@ def test_topk_validation(lib):
     assert tk(scale=float("inf")) == "FA_ERR_VALUE"
     assert tk(q=T([0, 128, 576]), idx=T([0, 32], fa.FA_I32), o=T([0, 128, 512]),
               lse=T([0, 128], fa.FA_F32)) == "FA_OK"
+
+
+def test_bwd_validation(lib):
+    def bw(dt=fa.FA_BF16, D=128, dq_shape=None, delta_dt=fa.FA_F32, B=2, causal=1):
+        q, k, v, o, lse = good(B=B, D=D, dt=dt)
+        dout = T([B, 4, 64, D], dt)
+        dq = T(dq_shape or [B, 4, 64, D], dt)
+        dk, dv = T([B, 2, 64, D], dt), T([B, 2, 64, D], dt)
+        delta = T([B, 4, 64], delta_dt)
+        return name(lib, lib.fa_bwd(R(q), R(k), R(v), R(o), R(lse), R(dout), causal, 0.1, R(delta), R(dq),
+                                    R(dk), R(dv), None))
+
+    assert bw(dt=fa.FA_F32) == "FA_ERR_UNSUPPORTED"
+    assert bw(D=64) == "FA_ERR_UNSUPPORTED"
+    assert bw(dq_shape=[2, 4, 63, 128]) == "FA_ERR_SHAPE"
+    assert bw(delta_dt=fa.FA_BF16) == "FA_ERR_DTYPE"
+    assert bw(causal=2) == "FA_ERR_VALUE"
+    assert bw(B=0) == "FA_OK"  # nothing to do: no launch
 
 
 def test_binding_refuses_cpu_tensors(lib):
