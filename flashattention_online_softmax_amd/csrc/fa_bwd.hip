@@ -43,17 +43,29 @@ __device__ __forceinline__ int rsw(int row, int ch) { return ch ^ (row & 15); }
 __device__ __forceinline__ int tsw(int row, int ch) { return ch ^ ((row & 3) << 2); }
 
 // Cooperative copy of rows r0 .. r0+31 (clamped to n - 1; n >= 1) of a
-// row-major [*, 128] 16-bit matrix into LDS, once per requested swizzle.
-__device__ __forceinline__ void load_tile(uint16_t* dst_r, uint16_t* dst_t, const uint16_t* src,
-                                          int64_t stride, int r0, int n) {
+// row-major [*, 128] 16-bit matrix into LDS, in two halves: fetch_tile loads
+// this thread's two 16-byte chunks into registers (issued before the
+// previous tile's MFMAs, so the load latency hides behind them), put_tile
+// stores them into LDS once per requested swizzle.
+struct TileRegs {
+  u32x4 v[(TR * BD / 8) / (64 * NWB)];
+};
+__device__ __forceinline__ void fetch_tile(TileRegs& r, const uint16_t* src, int64_t stride, int r0, int n) {
 #pragma unroll
   for (int u = 0; u < (TR * BD / 8) / (64 * NWB); ++u) {
     const int id = (int)threadIdx.x + u * 64 * NWB;
     const int row = id >> 4, ch = id & 15;
     const int gr = min(r0 + row, n - 1);
-    const u32x4 v = *(const u32x4*)(src + (int64_t)gr * stride + ch * 8);
-    if (dst_r) *(u32x4*)(dst_r + row * BD + rsw(row, ch) * 8) = v;
-    if (dst_t) *(u32x4*)(dst_t + row * BD + tsw(row, ch) * 8) = v;
+    r.v[u] = *(const u32x4*)(src + (int64_t)gr * stride + ch * 8);
+  }
+}
+__device__ __forceinline__ void put_tile(const TileRegs& r, uint16_t* dst_r, uint16_t* dst_t) {
+#pragma unroll
+  for (int u = 0; u < (TR * BD / 8) / (64 * NWB); ++u) {
+    const int id = (int)threadIdx.x + u * 64 * NWB;
+    const int row = id >> 4, ch = id & 15;
+    if (dst_r) *(u32x4*)(dst_r + row * BD + rsw(row, ch) * 8) = r.v[u];
+    if (dst_t) *(u32x4*)(dst_t + row * BD + tsw(row, ch) * 8) = r.v[u];
   }
 }
 
@@ -126,7 +138,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 template <class T, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sQr[TR * BD], sQt[TR * BD], sOr[TR * BD], sOt[TR * BD];
-  __shared__ float sL[TR], sD[TR];
+  __shared__ __attribute__((aligned(16))) float sL[TR], sD[TR];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
   const int bk = blockIdx.y, b = bk / p.Hkv, hkv = bk % p.Hkv;
   const int k0 = blockIdx.x * BLK;
@@ -145,29 +157,70 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   // Query rows that can see a key of this block: i >= k0 - diag (causal).
   const int qfirst = CAUSAL ? max(0, k0 - diag) : 0;
   const int nqt = p.Sq > qfirst ? (p.Sq - qfirst + TR - 1) / TR : 0;
-  for (int hq = hkv * p.G; hq < (hkv + 1) * p.G; ++hq) {
-    const uint16_t* qg = (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh;
-    const uint16_t* dg = (const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hq * p.do_sh;
-    const float* lg = p.lse + ((int64_t)b * p.Hq + hq) * p.Sq;
-    const float* delg = p.delta + ((int64_t)b * p.Hq + hq) * p.Sq;
-    for (int t = 0; t < nqt; ++t) {
-      const int q0 = qfirst + t * TR;
-      __syncthreads();  // the previous tile's reads are done
-      load_tile(sQr, sQt, qg, p.q_ss, q0, p.Sq);
-      load_tile(sOr, sOt, dg, p.do_ss, q0, p.Sq);
-      if (threadIdx.x < TR) {
-        const int i = q0 + threadIdx.x;
-        const float l = i < p.Sq ? lg[i] : -INFINITY;
-        // rows without keys (LSE = -inf) and padding rows get P = 0
-        sL[threadIdx.x] = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
-        sD[threadIdx.x] = i < p.Sq ? delg[i] : 0.f;
-      }
-      __syncthreads();
-      f32x16 s = {}, dp = {};
+  // The sweep: step it = (query head hq, query tile t) of the group, tiles
+  // fetched one step ahead into registers.
+  const int nsteps = p.G * nqt;
+  TileRegs rq, ro;
+  float rl = 0.f, rd = 0.f;
+  auto fetch = [&](int it) __attribute__((always_inline)) {
+    const int hq = hkv * p.G + it / nqt, q0 = qfirst + (it % nqt) * TR;
+    const int64_t bh = (int64_t)b * p.Hq + hq;
+    fetch_tile(rq, (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh, p.q_ss, q0, p.Sq);
+    fetch_tile(ro, (const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hq * p.do_sh, p.do_ss, q0, p.Sq);
+    if (threadIdx.x < TR) {
+      const int i = q0 + threadIdx.x;
+      const float l = i < p.Sq ? p.lse[bh * p.Sq + i] : -INFINITY;
+      // rows without keys (LSE = -inf) and padding rows get P = 0
+      rl = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
+      rd = i < p.Sq ? p.delta[bh * p.Sq + i] : 0.f;
+    }
+  };
+  if (nsteps > 0) fetch(0);
+  for (int it = 0; it < nsteps; ++it) {
+    const int q0 = qfirst + (it % nqt) * TR;
+    __syncthreads();  // every wave is done with the previous tile
+    put_tile(rq, sQr, sQt);
+    put_tile(ro, sOr, sOt);
+    if (threadIdx.x < TR) {
+      sL[threadIdx.x] = rl;
+      sD[threadIdx.x] = rd;
+    }
+    __syncthreads();
+    if (it + 1 < nsteps) fetch(it + 1);
+    {
+      // All LDS operands of the tile first: one wave per SIMD has nothing
+      // else to hide their latency behind.
+      u32x4 qa[BD / 16], oa[BD / 16], qt[BD / 32][TR / 16], ot[BD / 32][TR / 16];
 #pragma unroll
       for (int ks = 0; ks < BD / 16; ++ks) {
-        s = T::mfma(row_op(sQr, ks), kop[ks], s);
-        dp = T::mfma(row_op(sOr, ks), vop[ks], dp);
+        qa[ks] = row_op(sQr, ks);
+        oa[ks] = row_op(sOr, ks);
+      }
+#pragma unroll
+      for (int dt = 0; dt < BD / 32; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < TR / 16; ++ks) {
+          ot[dt][ks] = tr_op(sOt, dt, ks);
+          qt[dt][ks] = tr_op(sQt, dt, ks);
+        }
+      // LSE and Delta of the lane's 16 rows: 4 groups of 4 consecutive rows.
+      float lr[16], dr[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 l4 = *(const float4*)(sL + 8 * j + 4 * h);
+        const float4 d4 = *(const float4*)(sD + 8 * j + 4 * h);
+        lr[4 * j] = l4.x; lr[4 * j + 1] = l4.y; lr[4 * j + 2] = l4.z; lr[4 * j + 3] = l4.w;
+        dr[4 * j] = d4.x; dr[4 * j + 1] = d4.y; dr[4 * j + 2] = d4.z; dr[4 * j + 3] = d4.w;
+      }
+      // S and dP as two chains each (even / odd k-steps) to halve the MFMA
+      // dependency latency.
+      f32x16 s0 = {}, s1 = {}, dp0 = {}, dp1 = {};
+#pragma unroll
+      for (int ks = 0; ks < BD / 16; ks += 2) {
+        s0 = T::mfma(qa[ks], kop[ks], s0);
+        dp0 = T::mfma(oa[ks], vop[ks], dp0);
+        s1 = T::mfma(qa[ks + 1], kop[ks + 1], s1);
+        dp1 = T::mfma(oa[ks + 1], vop[ks + 1], dp1);
       }
       // Element i: query row q0 + r, r = 8 (i / 4) + 4 h + i % 4; key `key`.
       f32x16 pm, dsm;
@@ -177,17 +230,17 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         const int qi = q0 + r;
         bool ok = key < p.Skv && qi < p.Sq;
         if (CAUSAL) ok = ok && key <= qi + diag;
-        const float pv = ok ? fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -sL[r])) : 0.f;
+        const float pv = ok ? fast_exp2(__builtin_fmaf(s0[i] + s1[i], p.scale_log2, -lr[i])) : 0.f;
         pm[i] = pv;
-        dsm[i] = pv * (dp[i] - sD[r]);
+        dsm[i] = pv * (dp0[i] + dp1[i] - dr[i]);
       }
 #pragma unroll
       for (int ks = 0; ks < TR / 16; ++ks) {
         const u32x4 pb = pack_b<T>(pm, ks), db = pack_b<T>(dsm, ks);
 #pragma unroll
         for (int dt = 0; dt < BD / 32; ++dt) {
-          dv_t[dt] = T::mfma(tr_op(sOt, dt, ks), pb, dv_t[dt]);
-          dk_t[dt] = T::mfma(tr_op(sQt, dt, ks), db, dk_t[dt]);
+          dv_t[dt] = T::mfma(ot[dt][ks], pb, dv_t[dt]);
+          dk_t[dt] = T::mfma(qt[dt][ks], db, dk_t[dt]);
         }
       }
     }
@@ -227,17 +280,38 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   // Keys any row of this block sees: j <= q0 + BLK - 1 + diag (causal).
   const int kend = CAUSAL ? max(0, min(p.Skv, q0 + BLK + diag)) : p.Skv;
   const int nkt = (kend + TR - 1) / TR;
+  TileRegs rk, rv;
+  if (nkt > 0) {
+    fetch_tile(rk, kg, p.k_ss, 0, p.Skv);
+    fetch_tile(rv, vg, p.v_ss, 0, p.Skv);
+  }
   for (int t = 0; t < nkt; ++t) {
     const int j0 = t * TR;
+    __syncthreads();  // every wave is done with the previous tile
+    put_tile(rk, sKr, sKt);
+    put_tile(rv, sVr, nullptr);
     __syncthreads();
-    load_tile(sKr, sKt, kg, p.k_ss, j0, p.Skv);
-    load_tile(sVr, nullptr, vg, p.v_ss, j0, p.Skv);
-    __syncthreads();
-    f32x16 s = {}, dp = {};
+    if (t + 1 < nkt) {  // the next tile's loads fly during this tile's MFMAs
+      fetch_tile(rk, kg, p.k_ss, j0 + TR, p.Skv);
+      fetch_tile(rv, vg, p.v_ss, j0 + TR, p.Skv);
+    }
+    u32x4 ka[BD / 16], va[BD / 16], kt[BD / 32][TR / 16];
 #pragma unroll
     for (int ks = 0; ks < BD / 16; ++ks) {
-      s = T::mfma(row_op(sKr, ks), qop[ks], s);
-      dp = T::mfma(row_op(sVr, ks), dop[ks], dp);
+      ka[ks] = row_op(sKr, ks);
+      va[ks] = row_op(sVr, ks);
+    }
+#pragma unroll
+    for (int dt = 0; dt < BD / 32; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < TR / 16; ++ks) kt[dt][ks] = tr_op(sKt, dt, ks);
+    f32x16 s0 = {}, s1 = {}, dp0 = {}, dp1 = {};
+#pragma unroll
+    for (int ks = 0; ks < BD / 16; ks += 2) {
+      s0 = T::mfma(ka[ks], qop[ks], s0);
+      dp0 = T::mfma(va[ks], dop[ks], dp0);
+      s1 = T::mfma(ka[ks + 1], qop[ks + 1], s1);
+      dp1 = T::mfma(va[ks + 1], dop[ks + 1], dp1);
     }
     // Element i: key j0 + r, r = 8 (i / 4) + 4 h + i % 4; query row qi.
     f32x16 dsm;
@@ -246,14 +320,14 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
       const int kj = j0 + 8 * (i >> 2) + 4 * h + (i & 3);
       bool ok = kj < p.Skv && qi < p.Sq;
       if (CAUSAL) ok = ok && kj <= qi + diag;
-      const float pv = ok ? fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -l2)) : 0.f;
-      dsm[i] = pv * (dp[i] - del);
+      const float pv = ok ? fast_exp2(__builtin_fmaf(s0[i] + s1[i], p.scale_log2, -l2)) : 0.f;
+      dsm[i] = pv * (dp0[i] + dp1[i] - del);
     }
 #pragma unroll
     for (int ks = 0; ks < TR / 16; ++ks) {
       const u32x4 db = pack_b<T>(dsm, ks);
 #pragma unroll
-      for (int dt = 0; dt < BD / 32; ++dt) dq_t[dt] = T::mfma(tr_op(sKt, dt, ks), db, dq_t[dt]);
+      for (int dt = 0; dt < BD / 32; ++dt) dq_t[dt] = T::mfma(kt[dt][ks], db, dq_t[dt]);
     }
   }
   if (qi < p.Sq) store_t<T>((uint16_t*)p.dq + (int64_t)b * p.dq_sb + (int64_t)hq * p.dq_sh, p.dq_ss, qi, dq_t, p.scale);
