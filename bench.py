@@ -104,6 +104,20 @@ def make_call(w, order="idx_a", rescale_threshold=8.0):
     return lambda: fa.fa_fwd_topk_gather(q, kv, vv, idx, scale=w["scale"], out=o, lse=lse)
 
 
+def make_bwd_call(w):
+    """Launcher of one backward (fa_bwd) of a dense workload: dO seeded and
+    synthetic, O and LSE from one forward with the exact running max."""
+    import flashattention_online_softmax_amd as fa
+    import synth
+    q, k, v = (w[n].to("cuda") for n in ("q", "k", "v"))
+    dout = synth.cast(synth.normal(synth.rng(1080), tuple(q.shape)), q.dtype).to("cuda")
+    o, lse = fa.fa_fwd(q, k, v, scale=w["scale"], causal=w["causal"], rescale_threshold=0.0)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    return lambda: fa.fa_bwd(q, k, v, o, lse, dout, scale=w["scale"], causal=w["causal"], dq=dq, dk=dk, dv=dv,
+                             delta=delta)
+
+
 def time_calls(call, steps, warmup, warm_seconds=1.0):
     """Returns (wall ms per step over exactly `steps` calls bracketed by device
     synchronisations, mean kernel ms from per-launch HIP events on the launch
@@ -292,6 +306,16 @@ def main():
         sec[args.workload + "_exact_max"] = {"tflops": round(flops / (km0 * 1e-3) / 1e12, 2),
                                              "kernel_ms": round(km0, 4),
                                              "cost_vs_lazy": round(km0 / kern_ms - 1.0, 4)}
+        # The backward of the headline workload (dQ, dK, dV from dO), counted
+        # as five products over the causal pairs: 2.5 times the forward's flop.
+        log("secondary %s backward" % args.workload)
+        cb = make_bwd_call(w)
+        _, kmb = time_calls(cb, max(5, args.steps // 10), 2, 0.3)
+        del cb
+        torch.cuda.empty_cache()
+        flb = 2.5 * flops
+        sec[args.workload + "_bwd"] = {"tflops": round(flb / (kmb * 1e-3) / 1e12, 2), "kernel_ms": round(kmb, 4),
+                                       "frac_mfma_peak": round(flb / (kmb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         result["secondary"] = sec
         result["page_figures"] = {
             "exact_max_fwd_cost_gb200": "+~4% (sparse-MLA training forward, T=S=16384, W=2048, H=128; NVIDIA GB200)",
