@@ -53,9 +53,16 @@ def _run(cmd, what):
     return r
 
 
+# Per-source extra flags. The backward kernels let the compiler place MFMA
+# accumulators; asking for the VGPR form keeps the scores, which the VALU
+# reads right away, out of AGPRs (fewer accumulator moves per tile).
+EXTRA_FLAGS = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-    _run([HIPCC, *FLAGS, "-I", BUILD_DIR, "-c", os.path.join(CSRC, src), "-o", obj], "hipcc " + src)
+    _run([HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-I", BUILD_DIR, "-c", os.path.join(CSRC, src), "-o", obj],
+         "hipcc " + src)
     return obj
 
 
