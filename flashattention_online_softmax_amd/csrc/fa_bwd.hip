@@ -18,7 +18,8 @@
 //     then dV^T += dO^T P and dK^T += Q^T dS on v_mfma_f32_32x32x16, P and dS
 //     rounded to 16 bits as B operands straight from the accumulator layout.
 //   * dq: a workgroup owns 128 query rows of one head (Q and dO resident) and
-//     sweeps the key tiles: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
+//     sweeps the key tiles: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T;
+//     it fits 256 registers, so two workgroups share a CU.
 // The operands read transposed (dO^T, Q^T, K^T) come from row-major LDS tiles
 // through ds_read_b64_tr_b16, in the key (query) order in which the
 // accumulator holds P and dS, so the contraction pairs the right elements.
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 template <class T, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sKr[TR * BD], sKt[TR * BD], sVr[TR * BD];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
   const int bh = blockIdx.y, b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.G;
@@ -295,23 +296,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
       fetch_tile(rk, kg, p.k_ss, j0 + TR, p.Skv);
       fetch_tile(rv, vg, p.v_ss, j0 + TR, p.Skv);
     }
-    u32x4 ka[BD / 16], va[BD / 16], kt[BD / 32][TR / 16];
+    // Two waves share each SIMD here (the register budget is 256), so the
+    // operands are read as the MFMAs consume them.
+    f32x16 s0 = {}, dp0 = {};
 #pragma unroll
     for (int ks = 0; ks < BD / 16; ++ks) {
-      ka[ks] = row_op(sKr, ks);
-      va[ks] = row_op(sVr, ks);
-    }
-#pragma unroll
-    for (int dt = 0; dt < BD / 32; ++dt)
-#pragma unroll
-      for (int ks = 0; ks < TR / 16; ++ks) kt[dt][ks] = tr_op(sKt, dt, ks);
-    f32x16 s0 = {}, s1 = {}, dp0 = {}, dp1 = {};
-#pragma unroll
-    for (int ks = 0; ks < BD / 16; ks += 2) {
-      s0 = T::mfma(ka[ks], qop[ks], s0);
-      dp0 = T::mfma(va[ks], dop[ks], dp0);
-      s1 = T::mfma(ka[ks + 1], qop[ks + 1], s1);
-      dp1 = T::mfma(va[ks + 1], dop[ks + 1], dp1);
+      s0 = T::mfma(row_op(sKr, ks), qop[ks], s0);
+      dp0 = T::mfma(row_op(sVr, ks), dop[ks], dp0);
     }
     // Element i: key j0 + r, r = 8 (i / 4) + 4 h + i % 4; query row qi.
     f32x16 dsm;
@@ -320,14 +311,14 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
       const int kj = j0 + 8 * (i >> 2) + 4 * h + (i & 3);
       bool ok = kj < p.Skv && qi < p.Sq;
       if (CAUSAL) ok = ok && kj <= qi + diag;
-      const float pv = ok ? fast_exp2(__builtin_fmaf(s0[i] + s1[i], p.scale_log2, -l2)) : 0.f;
-      dsm[i] = pv * (dp0[i] + dp1[i] - del);
+      const float pv = ok ? fast_exp2(__builtin_fmaf(s0[i], p.scale_log2, -l2)) : 0.f;
+      dsm[i] = pv * (dp0[i] - del);
     }
 #pragma unroll
     for (int ks = 0; ks < TR / 16; ++ks) {
       const u32x4 db = pack_b<T>(dsm, ks);
 #pragma unroll
-      for (int dt = 0; dt < BD / 32; ++dt) dq_t[dt] = T::mfma(kt[dt][ks], db, dq_t[dt]);
+      for (int dt = 0; dt < BD / 32; ++dt) dq_t[dt] = T::mfma(tr_op(sKt, dt, ks), db, dq_t[dt]);
     }
   }
   if (qi < p.Sq) store_t<T>((uint16_t*)p.dq + (int64_t)b * p.dq_sb + (int64_t)hq * p.dq_sh, p.dq_ss, qi, dq_t, p.scale);
