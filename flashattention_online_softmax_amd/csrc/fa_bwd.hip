@@ -12,10 +12,11 @@
 //
 // Three kernels, none of them with atomics:
 //   * delta: Delta_i = dO_i . O_i in fp32, one row per 16 lanes.
-//   * dkdv: a workgroup owns 128 keys of one KV head (4 waves x 32 keys, K and
-//     V of its keys resident as MFMA B operands) and sweeps the query tiles
-//     (32 rows) of every query head of the group: S = Q K^T, dP = dO V^T,
-//     then dV^T += dO^T P and dK^T += Q^T dS on v_mfma_f32_32x32x16, P and dS
+//   * dkdv: a workgroup owns 128 keys of one KV head (8 waves: for each 32
+//     keys one wave accumulates dV, one dK, with K (and V) of its keys
+//     resident as MFMA B operands) and sweeps the query tiles (32 rows) of
+//     every query head of the group: S = Q K^T, dP = dO V^T, then
+//     dV^T += dO^T P and dK^T += Q^T dS on v_mfma_f32_32x32x16, P and dS
 //     rounded to 16 bits as B operands straight from the accumulator layout.
 //   * dq: a workgroup owns 128 query rows of one head (Q and dO resident) and
 //     sweeps the key tiles: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T;
@@ -48,22 +49,26 @@ __device__ __forceinline__ int tsw(int row, int ch) { return ch ^ ((row & 3) << 
 // this thread's two 16-byte chunks into registers (issued before the
 // previous tile's MFMAs, so the load latency hides behind them), put_tile
 // stores them into LDS once per requested swizzle.
+template <int NT = 64 * NWB>
 struct TileRegs {
-  u32x4 v[(TR * BD / 8) / (64 * NWB)];
+  static constexpr int N = (TR * BD / 8) / NT;  // 16-byte chunks per thread
+  u32x4 v[N];
 };
-__device__ __forceinline__ void fetch_tile(TileRegs& r, const uint16_t* src, int64_t stride, int r0, int n) {
+template <int NT>
+__device__ __forceinline__ void fetch_tile(TileRegs<NT>& r, const uint16_t* src, int64_t stride, int r0, int n) {
 #pragma unroll
-  for (int u = 0; u < (TR * BD / 8) / (64 * NWB); ++u) {
-    const int id = (int)threadIdx.x + u * 64 * NWB;
+  for (int u = 0; u < TileRegs<NT>::N; ++u) {
+    const int id = (int)threadIdx.x + u * NT;
     const int row = id >> 4, ch = id & 15;
     const int gr = min(r0 + row, n - 1);
     r.v[u] = *(const u32x4*)(src + (int64_t)gr * stride + ch * 8);
   }
 }
-__device__ __forceinline__ void put_tile(const TileRegs& r, uint16_t* dst_r, uint16_t* dst_t) {
+template <int NT>
+__device__ __forceinline__ void put_tile(const TileRegs<NT>& r, uint16_t* dst_r, uint16_t* dst_t) {
 #pragma unroll
-  for (int u = 0; u < (TR * BD / 8) / (64 * NWB); ++u) {
-    const int id = (int)threadIdx.x + u * 64 * NWB;
+  for (int u = 0; u < TileRegs<NT>::N; ++u) {
+    const int id = (int)threadIdx.x + u * NT;
     const int row = id >> 4, ch = id & 15;
     if (dst_r) *(u32x4*)(dst_r + row * BD + rsw(row, ch) * 8) = r.v[u];
     if (dst_t) *(u32x4*)(dst_t + row * BD + tsw(row, ch) * 8) = r.v[u];
@@ -136,32 +141,37 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
   if (row < rows && sub == 0) p.delta[row] = acc;
 }
 
+// Two waves per key group of 32: wave g (0..3) computes S, P and dV^T +=
+// dO^T P; wave g + 4 computes S, dP, dS and dK^T += Q^T dS. Each holds one
+// gradient's accumulators, so both fit 256 registers and share a SIMD.
 template <class T, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int NT = 512;
   __shared__ __attribute__((aligned(16))) uint16_t sQr[TR * BD], sQt[TR * BD], sOr[TR * BD], sOt[TR * BD];
   __shared__ __attribute__((aligned(16))) float sL[TR], sD[TR];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
+  const bool kwave = __builtin_amdgcn_readfirstlane(w) >= 4;  // dK (else dV)
   const int bk = blockIdx.y, b = bk / p.Hkv, hkv = bk % p.Hkv;
   const int k0 = blockIdx.x * BLK;
-  const int key = k0 + 32 * w + c;  // this lane's key (column of S)
+  const int key = k0 + 32 * (w & 3) + c;  // this lane's key (column of S)
   const int diag = p.Skv - p.Sq;
   const uint16_t* kg = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh;
   const uint16_t* vg = (const uint16_t*)p.v + (int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh;
   u32x4 kop[BD / 16], vop[BD / 16];
   load_bop(kop, kg, p.k_ss, min(key, p.Skv - 1));
-  load_bop(vop, vg, p.v_ss, min(key, p.Skv - 1));
-  f32x16 dv_t[BD / 32], dk_t[BD / 32];
+  if (kwave) load_bop(vop, vg, p.v_ss, min(key, p.Skv - 1));
+  f32x16 acc[BD / 32];  // dK^T (K waves) or dV^T (V waves)
 #pragma unroll
   for (int dt = 0; dt < BD / 32; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) dv_t[dt][i] = dk_t[dt][i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
   // Query rows that can see a key of this block: i >= k0 - diag (causal).
   const int qfirst = CAUSAL ? max(0, k0 - diag) : 0;
   const int nqt = p.Sq > qfirst ? (p.Sq - qfirst + TR - 1) / TR : 0;
   // The sweep: step it = (query head hq, query tile t) of the group, tiles
   // fetched one step ahead into registers.
   const int nsteps = p.G * nqt;
-  TileRegs rq, ro;
+  TileRegs<NT> rq, ro;
   float rl = 0.f, rd = 0.f;
   auto fetch = [&](int it) __attribute__((always_inline)) {
     const int hq = hkv * p.G + it / nqt, q0 = qfirst + (it % nqt) * TR;
@@ -188,67 +198,49 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     }
     __syncthreads();
     if (it + 1 < nsteps) fetch(it + 1);
-    {
-      // All LDS operands of the tile first: one wave per SIMD has nothing
-      // else to hide their latency behind.
-      u32x4 qa[BD / 16], oa[BD / 16], qt[BD / 32][TR / 16], ot[BD / 32][TR / 16];
+    // LSE (and Delta) of the lane's 16 rows: 4 groups of 4 consecutive rows.
+    float lr[16], dr[16];
 #pragma unroll
-      for (int ks = 0; ks < BD / 16; ++ks) {
-        qa[ks] = row_op(sQr, ks);
-        oa[ks] = row_op(sOr, ks);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const float4 l4 = *(const float4*)(sL + 8 * j + 4 * h);
+      lr[4 * j] = l4.x; lr[4 * j + 1] = l4.y; lr[4 * j + 2] = l4.z; lr[4 * j + 3] = l4.w;
+    }
+    f32x16 sv = {}, dp = {};
 #pragma unroll
-      for (int dt = 0; dt < BD / 32; ++dt)
-#pragma unroll
-        for (int ks = 0; ks < TR / 16; ++ks) {
-          ot[dt][ks] = tr_op(sOt, dt, ks);
-          qt[dt][ks] = tr_op(sQt, dt, ks);
-        }
-      // LSE and Delta of the lane's 16 rows: 4 groups of 4 consecutive rows.
-      float lr[16], dr[16];
+    for (int ks = 0; ks < BD / 16; ++ks) sv = T::mfma(row_op(sQr, ks), kop[ks], sv);
+    if (kwave) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float4 l4 = *(const float4*)(sL + 8 * j + 4 * h);
         const float4 d4 = *(const float4*)(sD + 8 * j + 4 * h);
-        lr[4 * j] = l4.x; lr[4 * j + 1] = l4.y; lr[4 * j + 2] = l4.z; lr[4 * j + 3] = l4.w;
         dr[4 * j] = d4.x; dr[4 * j + 1] = d4.y; dr[4 * j + 2] = d4.z; dr[4 * j + 3] = d4.w;
       }
-      // S and dP as two chains each (even / odd k-steps) to halve the MFMA
-      // dependency latency.
-      f32x16 s0 = {}, s1 = {}, dp0 = {}, dp1 = {};
 #pragma unroll
-      for (int ks = 0; ks < BD / 16; ks += 2) {
-        s0 = T::mfma(qa[ks], kop[ks], s0);
-        dp0 = T::mfma(oa[ks], vop[ks], dp0);
-        s1 = T::mfma(qa[ks + 1], kop[ks + 1], s1);
-        dp1 = T::mfma(oa[ks + 1], vop[ks + 1], dp1);
-      }
-      // Element i: query row q0 + r, r = 8 (i / 4) + 4 h + i % 4; key `key`.
-      f32x16 pm, dsm;
+      for (int ks = 0; ks < BD / 16; ++ks) dp = T::mfma(row_op(sOr, ks), vop[ks], dp);
+    }
+    // Element i: query row q0 + r, r = 8 (i / 4) + 4 h + i % 4; key `key`.
+    f32x16 bm;  // P (V waves) or dS (K waves)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 8 * (i >> 2) + 4 * h + (i & 3);
-        const int qi = q0 + r;
-        bool ok = key < p.Skv && qi < p.Sq;
-        if (CAUSAL) ok = ok && key <= qi + diag;
-        const float pv = ok ? fast_exp2(__builtin_fmaf(s0[i] + s1[i], p.scale_log2, -lr[i])) : 0.f;
-        pm[i] = pv;
-        dsm[i] = pv * (dp0[i] + dp1[i] - dr[i]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+      const int qi = q0 + r;
+      bool ok = key < p.Skv && qi < p.Sq;
+      if (CAUSAL) ok = ok && key <= qi + diag;
+      const float pv = ok ? fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, -lr[i])) : 0.f;
+      bm[i] = kwave ? pv * (dp[i] - dr[i]) : pv;
+    }
+    const uint16_t* at = kwave ? sQt : sOt;  // Q^T for dK, dO^T for dV
 #pragma unroll
-      for (int ks = 0; ks < TR / 16; ++ks) {
-        const u32x4 pb = pack_b<T>(pm, ks), db = pack_b<T>(dsm, ks);
+    for (int ks = 0; ks < TR / 16; ++ks) {
+      const u32x4 bb = pack_b<T>(bm, ks);
 #pragma unroll
-        for (int dt = 0; dt < BD / 32; ++dt) {
-          dv_t[dt] = T::mfma(ot[dt][ks], pb, dv_t[dt]);
-          dk_t[dt] = T::mfma(qt[dt][ks], db, dk_t[dt]);
-        }
-      }
+      for (int dt = 0; dt < BD / 32; ++dt) acc[dt] = T::mfma(tr_op(at, dt, ks), bb, acc[dt]);
     }
   }
   if (key < p.Skv) {
-    store_t<T>((uint16_t*)p.dk + (int64_t)b * p.dk_sb + (int64_t)hkv * p.dk_sh, p.dk_ss, key, dk_t, p.scale);
-    store_t<T>((uint16_t*)p.dv + (int64_t)b * p.dv_sb + (int64_t)hkv * p.dv_sh, p.dv_ss, key, dv_t, 1.f);
+    if (kwave)
+      store_t<T>((uint16_t*)p.dk + (int64_t)b * p.dk_sb + (int64_t)hkv * p.dk_sh, p.dk_ss, key, acc, p.scale);
+    else
+      store_t<T>((uint16_t*)p.dv + (int64_t)b * p.dv_sb + (int64_t)hkv * p.dv_sh, p.dv_ss, key, acc, 1.f);
   }
 }
 
@@ -281,7 +273,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   // Keys any row of this block sees: j <= q0 + BLK - 1 + diag (causal).
   const int kend = CAUSAL ? max(0, min(p.Skv, q0 + BLK + diag)) : p.Skv;
   const int nkt = (kend + TR - 1) / TR;
-  TileRegs rk, rv;
+  TileRegs<> rk, rv;
   if (nkt > 0) {
     fetch_tile(rk, kg, p.k_ss, 0, p.Skv);
     fetch_tile(rv, vg, p.v_ss, 0, p.Skv);
@@ -334,7 +326,7 @@ hipError_t launch_bwd_t(BwdParams& p, hipStream_t st) {
   }
   if (p.Skv > 0 && p.B * p.Hkv > 0) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, CAUSAL>), dim3((unsigned)((p.Skv + BLK - 1) / BLK), (unsigned)(p.B * p.Hkv)),
-                       dim3(256), 0, st, p);
+                       dim3(512), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
