@@ -151,8 +151,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float sL[TR], sD[TR];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
   const bool kwave = __builtin_amdgcn_readfirstlane(w) >= 4;  // dK (else dV)
-  const int bk = blockIdx.y, b = bk / p.Hkv, hkv = bk % p.Hkv;
-  const int k0 = blockIdx.x * BLK;
+  // Workgroups in order of decreasing work (under the causal mask the first
+  // key blocks see the most query rows), the (batch, KV head) index fastest
+  // so that one head's workgroups share an XCD (workgroup i runs on XCD i % 8).
+  const int lin = blockIdx.x + blockIdx.y * gridDim.x, nbk = p.B * p.Hkv;
+  const int bk = lin % nbk, b = bk / p.Hkv, hkv = bk % p.Hkv;
+  const int k0 = (lin / nbk) * BLK;
   const int key = k0 + 32 * (w & 3) + c;  // this lane's key (column of S)
   const int diag = p.Skv - p.Sq;
   const uint16_t* kg = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh;
@@ -248,8 +252,11 @@ template <class T, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sKr[TR * BD], sKt[TR * BD], sVr[TR * BD];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
-  const int bh = blockIdx.y, b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.G;
-  const int q0 = blockIdx.x * BLK;
+  // Workgroups in order of decreasing work (under the causal mask the last
+  // query blocks see the most keys), the (batch, head) index fastest.
+  const int lin = blockIdx.x + blockIdx.y * gridDim.x, nbh = p.B * p.Hq;
+  const int bh = lin % nbh, b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.G;
+  const int q0 = (CAUSAL ? (int)gridDim.x - 1 - lin / nbh : lin / nbh) * BLK;
   const int qi = q0 + 32 * w + c;  // this lane's query row (column of S^T)
   const int diag = p.Skv - p.Sq;
   const uint16_t* qg = (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh;
