@@ -147,8 +147,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 template <class T, bool CAUSAL>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NT = 512;
-  __shared__ __attribute__((aligned(16))) uint16_t sQr[TR * BD], sQt[TR * BD], sOr[TR * BD], sOt[TR * BD];
-  __shared__ __attribute__((aligned(16))) float sL[TR], sD[TR];
+  // Two buffers of the four tile copies (Q rows, Q^T, dO rows, dO^T) and of
+  // the rows' LSE / Delta: tile it + 1 is stored while tile it is read.
+  __shared__ __attribute__((aligned(16))) uint16_t sbuf[2][4][TR * BD];
+  __shared__ __attribute__((aligned(16))) float sLD[2][2][TR];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
   const bool kwave = __builtin_amdgcn_readfirstlane(w) >= 4;  // dK (else dV)
   // Workgroups in order of decreasing work (under the causal mask the first
@@ -190,18 +192,35 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       rd = i < p.Sq ? p.delta[bh * p.Sq + i] : 0.f;
     }
   };
-  if (nsteps > 0) fetch(0);
+  auto put = [&](int it) __attribute__((always_inline)) {
+    uint16_t(&bf)[4][TR * BD] = sbuf[it & 1];
+    put_tile(rq, bf[0], bf[1]);
+    put_tile(ro, bf[2], bf[3]);
+    if (threadIdx.x < TR) {
+      sLD[it & 1][0][threadIdx.x] = rl;
+      sLD[it & 1][1][threadIdx.x] = rd;
+    }
+  };
+  if (nsteps > 0) {
+    fetch(0);
+    put(0);
+    if (nsteps > 1) fetch(1);
+  }
   for (int it = 0; it < nsteps; ++it) {
     const int q0 = qfirst + (it % nqt) * TR;
-    __syncthreads();  // every wave is done with the previous tile
-    put_tile(rq, sQr, sQt);
-    put_tile(ro, sOr, sOt);
-    if (threadIdx.x < TR) {
-      sL[threadIdx.x] = rl;
-      sD[threadIdx.x] = rd;
-    }
+    // One barrier per tile: tile it is stored (by every wave) and every wave
+    // is done reading tile it - 1, whose buffer tile it + 1 now takes.
     __syncthreads();
-    if (it + 1 < nsteps) fetch(it + 1);
+    if (it + 1 < nsteps) {
+      put(it + 1);
+      if (it + 2 < nsteps) fetch(it + 2);
+    }
+    const uint16_t* sQr = sbuf[it & 1][0];
+    const uint16_t* sQt = sbuf[it & 1][1];
+    const uint16_t* sOr = sbuf[it & 1][2];
+    const uint16_t* sOt = sbuf[it & 1][3];
+    const float* sL = sLD[it & 1][0];
+    const float* sD = sLD[it & 1][1];
     // LSE (and Delta) of the lane's 16 rows: 4 groups of 4 consecutive rows.
     float lr[16], dr[16];
 #pragma unroll
@@ -250,7 +269,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
 
 template <class T, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sKr[TR * BD], sKt[TR * BD], sVr[TR * BD];
+  // Two buffers of the three tile copies (K rows, K^T, V rows).
+  __shared__ __attribute__((aligned(16))) uint16_t sbuf[2][3][TR * BD];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
   // Workgroups in order of decreasing work (under the causal mask the last
   // query blocks see the most keys), the (batch, head) index fastest.
@@ -281,20 +301,31 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   const int kend = CAUSAL ? max(0, min(p.Skv, q0 + BLK + diag)) : p.Skv;
   const int nkt = (kend + TR - 1) / TR;
   TileRegs<> rk, rv;
+  auto fetch = [&](int t) __attribute__((always_inline)) {
+    fetch_tile(rk, kg, p.k_ss, t * TR, p.Skv);
+    fetch_tile(rv, vg, p.v_ss, t * TR, p.Skv);
+  };
+  auto put = [&](int t) __attribute__((always_inline)) {
+    put_tile(rk, sbuf[t & 1][0], sbuf[t & 1][1]);
+    put_tile(rv, sbuf[t & 1][2], nullptr);
+  };
   if (nkt > 0) {
-    fetch_tile(rk, kg, p.k_ss, 0, p.Skv);
-    fetch_tile(rv, vg, p.v_ss, 0, p.Skv);
+    fetch(0);
+    put(0);
+    if (nkt > 1) fetch(1);
   }
   for (int t = 0; t < nkt; ++t) {
     const int j0 = t * TR;
-    __syncthreads();  // every wave is done with the previous tile
-    put_tile(rk, sKr, sKt);
-    put_tile(rv, sVr, nullptr);
+    // One barrier per tile (see the dK/dV kernel); the loads of tile t + 2
+    // fly during this tile's MFMAs.
     __syncthreads();
-    if (t + 1 < nkt) {  // the next tile's loads fly during this tile's MFMAs
-      fetch_tile(rk, kg, p.k_ss, j0 + TR, p.Skv);
-      fetch_tile(rv, vg, p.v_ss, j0 + TR, p.Skv);
+    if (t + 1 < nkt) {
+      put(t + 1);
+      if (t + 2 < nkt) fetch(t + 2);
     }
+    const uint16_t* sKr = sbuf[t & 1][0];
+    const uint16_t* sKt = sbuf[t & 1][1];
+    const uint16_t* sVr = sbuf[t & 1][2];
     // Two waves share each SIMD here (the register budget is 256), so the
     // operands are read as the MFMAs consume them.
     f32x16 s0 = {}, dp0 = {};
