@@ -64,7 +64,7 @@ def load():
         lib.fa_fwd_blocksparse.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_float,
                                            ctypes.c_float, P, P, ctypes.c_void_p]
         lib.fa_fwd_topk_gather.argtypes = [P, P, P, P, ctypes.c_float, P, P, ctypes.c_void_p]
-        lib.fa_bwd.argtypes = [P, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P, P, P, P, ctypes.c_void_p]
+        lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P, P, P, P, ctypes.c_void_p]
         for f in (lib.fa_fwd, lib.fa_fwd_blocksparse, lib.fa_fwd_topk_gather, lib.fa_bwd):
             f.restype = ctypes.c_int
         lib.fa_status_str.argtypes = [ctypes.c_int]
@@ -141,13 +141,15 @@ def fa_fwd(q, k, v, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k
     return out, lse
 
 
-def fa_bwd(q, k, v, o, lse, dout, *, scale, causal=False, dq=None, dk=None, dv=None, delta=None, stream=None):
-    """Gradients (dq, dk, dv) of the dense/causal/GQA forward given its
-    output o, its lse and the output gradient dout (f16/bf16, D = 128).
+def fa_bwd(q, k, v, o, lse, dout, *, scale, causal=False, mask=None, dq=None, dk=None, dv=None, delta=None,
+           stream=None):
+    """Gradients (dq, dk, dv) of the dense/causal/masked/GQA forward given
+    its output o, its lse and the output gradient dout (f16/bf16, D = 128);
+    mask as fa_fwd's (uint8, non-zero = excluded).
     delta (fp32 [B,Hq,Sq]) is the kernels' workspace; it is allocated here
     when not given."""
     lib = load()
-    _need_gpu(q, k, v, o, lse, dout)
+    _need_gpu(q, k, v, o, lse, dout, mask)
     if dq is None:
         dq = torch.empty_like(q)
     if dk is None:
@@ -156,7 +158,7 @@ def fa_bwd(q, k, v, o, lse, dout, *, scale, causal=False, dq=None, dk=None, dv=N
         dv = torch.empty_like(v)
     if delta is None:
         delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    _check(lib.fa_bwd(_ref(describe(q)), _ref(describe(k)), _ref(describe(v)), _ref(describe(o)),
+    _check(lib.fa_bwd(_ref(describe(q)), _ref(describe(k)), _ref(describe(v)), _ref(describe(mask)), _ref(describe(o)),
                       _ref(describe(lse)), _ref(describe(dout)), int(bool(causal)), float(scale),
                       _ref(describe(delta)), _ref(describe(dq)), _ref(describe(dk)), _ref(describe(dv)),
                       _stream(stream)))

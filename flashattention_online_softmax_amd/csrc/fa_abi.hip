@@ -190,6 +190,30 @@ fa::Dt to_dt(int32_t d) { return d == FA_F32 ? fa::Dt::F32 : d == FA_F16 ? fa::D
 
 extern "C" {
 
+// The boolean mask forms shared by the forward and the backward: uint8
+// [Sq, Skv] or [B|1, Hq|1, Sq, Skv]; a broadcast dim gets stride 0.
+static fa_status parse_mask(const fa_tensor* mask, int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int64_t* sb,
+                            int64_t* sh, int64_t* ss) {
+  fa_status s;
+  if (mask->ndim != 2 && mask->ndim != 4) return fail(FA_ERR_SHAPE, "mask must have rank 2 or 4");
+  if ((s = check_tensor("mask", mask, mask->ndim, false)) != FA_OK) return s;
+  if ((s = check_dtype("mask", mask, FA_U8)) != FA_OK) return s;
+  if (mask->ndim == 2) {
+    if (mask->shape[0] != Sq || mask->shape[1] != Skv) return fail(FA_ERR_SHAPE, "mask must be [Sq, Skv]");
+    *sb = 0;
+    *sh = 0;
+    *ss = mask->stride[0];
+  } else {
+    if ((mask->shape[0] != B && mask->shape[0] != 1) || (mask->shape[1] != Hq && mask->shape[1] != 1) ||
+        mask->shape[2] != Sq || mask->shape[3] != Skv)
+      return fail(FA_ERR_SHAPE, "mask must be [B|1, Hq|1, Sq, Skv]");
+    *sb = mask->shape[0] == 1 ? 0 : mask->stride[0];
+    *sh = mask->shape[1] == 1 ? 0 : mask->stride[1];
+    *ss = mask->stride[2];
+  }
+  return FA_OK;
+}
+
 fa_status fa_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* mask,
                  const fa_tensor* seqlens_q, const fa_tensor* seqlens_k, int causal, float scale,
                  float rescale_threshold, const fa_tensor* o, const fa_tensor* lse, void* stream) {
@@ -203,22 +227,7 @@ fa_status fa_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
   fa::FwdParams p;
   fill_common(p, q, k, v, o, lse, scale, rescale_threshold);
   if (mask) {
-    if (mask->ndim != 2 && mask->ndim != 4) return fail(FA_ERR_SHAPE, "mask must have rank 2 or 4");
-    if ((s = check_tensor("mask", mask, mask->ndim, false)) != FA_OK) return s;
-    if ((s = check_dtype("mask", mask, FA_U8)) != FA_OK) return s;
-    if (mask->ndim == 2) {
-      if (mask->shape[0] != Sq || mask->shape[1] != Skv) return fail(FA_ERR_SHAPE, "mask must be [Sq, Skv]");
-      p.m_sb = 0;
-      p.m_sh = 0;
-      p.m_ss = mask->stride[0];
-    } else {
-      if ((mask->shape[0] != B && mask->shape[0] != 1) || (mask->shape[1] != Hq && mask->shape[1] != 1) ||
-          mask->shape[2] != Sq || mask->shape[3] != Skv)
-        return fail(FA_ERR_SHAPE, "mask must be [B|1, Hq|1, Sq, Skv]");
-      p.m_sb = mask->shape[0] == 1 ? 0 : mask->stride[0];
-      p.m_sh = mask->shape[1] == 1 ? 0 : mask->stride[1];
-      p.m_ss = mask->stride[mask->ndim == 4 ? 2 : 0];
-    }
+    if ((s = parse_mask(mask, B, Hq, Sq, Skv, &p.m_sb, &p.m_sh, &p.m_ss)) != FA_OK) return s;
     p.mask = (const uint8_t*)mask->data;
     p.mask_vec4 = (((uintptr_t)mask->data) % 4 == 0) && (p.m_sb % 4 == 0) && (p.m_sh % 4 == 0) &&
                   (p.m_ss % 4 == 0);
@@ -328,8 +337,8 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
   return hip_status(fa::launch_topk(to_dt(q->dtype), p, (hipStream_t)stream));
 }
 
-fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* o,
-                 const fa_tensor* lse, const fa_tensor* dout, int causal, float scale,
+fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* mask,
+                 const fa_tensor* o, const fa_tensor* lse, const fa_tensor* dout, int causal, float scale,
                  const fa_tensor* delta, const fa_tensor* dq, const fa_tensor* dk,
                  const fa_tensor* dv, void* stream) {
   clear_error();
@@ -384,8 +393,13 @@ fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
   p.Skv = (int32_t)k->shape[2];
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
+  if (mask) {
+    if ((s = parse_mask(mask, p.B, p.Hq, p.Sq, p.Skv, &p.m_sb, &p.m_sh, &p.m_ss)) != FA_OK) return s;
+    p.mask = (const uint8_t*)mask->data;
+  }
   if ((int64_t)p.B * p.Hq * p.Sq == 0 && (int64_t)p.B * p.Hkv * p.Skv == 0) return FA_OK;
-  return hip_status(fa::launch_bwd(to_dt(q->dtype), causal != 0, p, (hipStream_t)stream));
+  const bool has_mask = mask && numel(mask) > 0;
+  return hip_status(fa::launch_bwd(to_dt(q->dtype), causal != 0, has_mask, p, (hipStream_t)stream));
 }
 
 const char* fa_status_str(fa_status s) {

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 // Two waves per key group of 32: wave g (0..3) computes S, P and dV^T +=
 // dO^T P; wave g + 4 computes S, dP, dS and dK^T += Q^T dS. Each holds one
 // gradient's accumulators, so both fit 256 registers and share a SIMD.
-template <class T, bool CAUSAL>
+template <class T, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NT = 512;
   // Two buffers of the four tile copies (Q rows, Q^T, dO rows, dO^T) and of
@@ -208,6 +208,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   }
   for (int it = 0; it < nsteps; ++it) {
     const int q0 = qfirst + (it % nqt) * TR;
+    // mask bytes of this step's query head, the lane's key column
+    const uint8_t* mk = MASK ? p.mask + (int64_t)b * p.m_sb + (int64_t)(hkv * p.G + it / nqt) * p.m_sh + key : nullptr;
     // One barrier per tile: tile it is stored (by every wave) and every wave
     // is done reading tile it - 1, whose buffer tile it + 1 now takes.
     __syncthreads();
@@ -248,6 +250,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       const int qi = q0 + r;
       bool ok = key < p.Skv && qi < p.Sq;
       if (CAUSAL) ok = ok && key <= qi + diag;
+      if (MASK) ok = ok && mk[(int64_t)qi * p.m_ss] == 0;
       const float pv = ok ? fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, -lr[i])) : 0.f;
       bm[i] = kwave ? pv * (dp[i] - dr[i]) : pv;
     }
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
-template <class T, bool CAUSAL>
+template <class T, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   // Two buffers of the three tile copies (K rows, K^T, V rows).
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[2][3][TR * BD];
@@ -279,6 +282,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   const int q0 = (CAUSAL ? (int)gridDim.x - 1 - lin / nbh : lin / nbh) * BLK;
   const int qi = q0 + 32 * w + c;  // this lane's query row (column of S^T)
   const int diag = p.Skv - p.Sq;
+  // mask bytes of the lane's query row (read only where qi < Sq)
+  const uint8_t* mq = MASK ? p.mask + (int64_t)b * p.m_sb + (int64_t)hq * p.m_sh + (int64_t)qi * p.m_ss : nullptr;
   const uint16_t* qg = (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh;
   const uint16_t* dg = (const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hq * p.do_sh;
   const uint16_t* kg = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh;
@@ -341,6 +346,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       const int kj = j0 + 8 * (i >> 2) + 4 * h + (i & 3);
       bool ok = kj < p.Skv && qi < p.Sq;
       if (CAUSAL) ok = ok && kj <= qi + diag;
+      if (MASK) ok = ok && mq[kj] == 0;
       const float pv = ok ? fast_exp2(__builtin_fmaf(s0[i], p.scale_log2, -l2)) : 0.f;
       dsm[i] = pv * (dp0[i] - del);
     }
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   if (qi < p.Sq) store_t<T>((uint16_t*)p.dq + (int64_t)b * p.dq_sb + (int64_t)hq * p.dq_sh, p.dq_ss, qi, dq_t, p.scale);
 }
 
-template <class T, bool CAUSAL>
+template <class T, bool CAUSAL, bool MASK>
 hipError_t launch_bwd_t(BwdParams& p, hipStream_t st) {
   const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
   if (rows > 0) {
@@ -363,13 +369,13 @@ hipError_t launch_bwd_t(BwdParams& p, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (p.Skv > 0 && p.B * p.Hkv > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, CAUSAL>), dim3((unsigned)((p.Skv + BLK - 1) / BLK), (unsigned)(p.B * p.Hkv)),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, CAUSAL, MASK>), dim3((unsigned)((p.Skv + BLK - 1) / BLK), (unsigned)(p.B * p.Hkv)),
                        dim3(512), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (rows > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, CAUSAL>), dim3((unsigned)((p.Sq + BLK - 1) / BLK), (unsigned)(p.B * p.Hq)),
+    hipLaunchKernelGGL((bwd_dq_kernel<T, CAUSAL, MASK>), dim3((unsigned)((p.Sq + BLK - 1) / BLK), (unsigned)(p.B * p.Hq)),
                        dim3(256), 0, st, p);
   }
   return hipGetLastError();
@@ -377,9 +383,15 @@ hipError_t launch_bwd_t(BwdParams& p, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_bwd(Dt dt, bool causal, BwdParams& p, hipStream_t stream) {
-  if (dt == Dt::BF16) return causal ? launch_bwd_t<BF16, true>(p, stream) : launch_bwd_t<BF16, false>(p, stream);
-  return causal ? launch_bwd_t<F16, true>(p, stream) : launch_bwd_t<F16, false>(p, stream);
+template <class T>
+hipError_t launch_bwd_m(bool causal, bool mask, BwdParams& p, hipStream_t st) {
+  if (mask) return causal ? launch_bwd_t<T, true, true>(p, st) : launch_bwd_t<T, false, true>(p, st);
+  return causal ? launch_bwd_t<T, true, false>(p, st) : launch_bwd_t<T, false, false>(p, st);
+}
+
+hipError_t launch_bwd(Dt dt, bool causal, bool mask, BwdParams& p, hipStream_t stream) {
+  if (dt == Dt::BF16) return launch_bwd_m<BF16>(causal, mask, p, stream);
+  return launch_bwd_m<F16>(causal, mask, p, stream);
 }
 
 }  // namespace fa

@@ -74,6 +74,8 @@ struct BwdParams {
   int64_t o_sb, o_sh, o_ss;
   int64_t do_sb, do_sh, do_ss;
   int64_t dq_sb, dq_sh, dq_ss;
+  const uint8_t* mask;  // NULL, or [B|1, Hq|1, Sq, Skv] bytes, non-zero = excluded
+  int64_t m_sb, m_sh, m_ss;  // 0 for a broadcast dim
   int64_t dk_sb, dk_sh, dk_ss;
   int64_t dv_sb, dv_sh, dv_ss;
   int32_t B, Hq, Hkv, G, Sq, Skv;
@@ -89,6 +91,6 @@ hipError_t code_object_function(const char* name, hipFunction_t* fn);
 hipError_t launch_dense(Dt dt, int D, bool causal, bool has_mask, bool sparse,
                         FwdParams& p, hipStream_t stream);
 hipError_t launch_topk(Dt dt, TopkParams& p, hipStream_t stream);
-hipError_t launch_bwd(Dt dt, bool causal, BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd(Dt dt, bool causal, bool mask, BwdParams& p, hipStream_t stream);
 
 }  // namespace fa

@@ -169,7 +169,7 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
                              const fa_tensor* lse, void* stream);
 
 /*
- * Attention backward (dense, optional causal mask, GQA): the gradients of the
+ * Attention backward (dense, optional causal and boolean masks, GQA): the gradients of the
  * dense forward's O with respect to q, k and v, given dO. Defined by the
  * backward formulas of the ops-transformer FlashAttentionScoreGrad pytest page
  * (section 5.2: dV = P^T dO, dS = P * (dP - rowsum(dP * P)), dQ = scale dS K,
@@ -178,7 +178,11 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
  * head (BSA README, section 1).
  *
  *  q, k, v     as fa_fwd (f16 or bf16, D == Dv == 128)
- *  o           the forward output for these q, k, v, causal, scale
+ *  mask        NULL or a boolean mask in one of fa_fwd's forms (non-zero =
+ *              excluded); P is 0 at excluded positions, so they receive no
+ *              gradient (the atten_mask input of the FlashAttentionScoreGrad
+ *              page, section 5.2)
+ *  o           the forward output for these q, k, v, mask, causal, scale
  *  lse         fp32 [B, Hq, Sq], contiguous: the forward's LSE
  *  dout        [B, Hq, Sq, Dv], q's dtype: the gradient of the output
  *  causal      0 or 1, as fa_fwd (bottom-right aligned)
@@ -193,8 +197,8 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
  * head dims or fp32; the library allocates nothing and enqueues three kernels
  * on `stream`.
  */
-fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* o,
-                 const fa_tensor* lse, const fa_tensor* dout, int causal, float scale,
+fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* mask,
+                 const fa_tensor* o, const fa_tensor* lse, const fa_tensor* dout, int causal, float scale,
                  const fa_tensor* delta, const fa_tensor* dq, const fa_tensor* dk,
                  const fa_tensor* dv, void* stream);
 

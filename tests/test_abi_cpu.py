@@ -151,20 +151,23 @@ def test_topk_validation(lib):
 
 
 def test_bwd_validation(lib):
-    def bw(dt=fa.FA_BF16, D=128, dq_shape=None, delta_dt=fa.FA_F32, B=2, causal=1):
+    def bw(dt=fa.FA_BF16, D=128, dq_shape=None, delta_dt=fa.FA_F32, B=2, causal=1, mask=None):
         q, k, v, o, lse = good(B=B, D=D, dt=dt)
         dout = T([B, 4, 64, D], dt)
         dq = T(dq_shape or [B, 4, 64, D], dt)
         dk, dv = T([B, 2, 64, D], dt), T([B, 2, 64, D], dt)
         delta = T([B, 4, 64], delta_dt)
-        return name(lib, lib.fa_bwd(R(q), R(k), R(v), R(o), R(lse), R(dout), causal, 0.1, R(delta), R(dq),
-                                    R(dk), R(dv), None))
+        return name(lib, lib.fa_bwd(R(q), R(k), R(v), R(mask), R(o), R(lse), R(dout), causal, 0.1,
+                                    R(delta), R(dq), R(dk), R(dv), None))
 
     assert bw(dt=fa.FA_F32) == "FA_ERR_UNSUPPORTED"
     assert bw(D=64) == "FA_ERR_UNSUPPORTED"
     assert bw(dq_shape=[2, 4, 63, 128]) == "FA_ERR_SHAPE"
     assert bw(delta_dt=fa.FA_BF16) == "FA_ERR_DTYPE"
     assert bw(causal=2) == "FA_ERR_VALUE"
+    assert bw(mask=T([64, 63], fa.FA_U8)) == "FA_ERR_SHAPE"
+    assert bw(mask=T([3, 4, 64, 64], fa.FA_U8)) == "FA_ERR_SHAPE"
+    assert bw(mask=T([64, 64], fa.FA_BF16)) == "FA_ERR_DTYPE"
     assert bw(B=0) == "FA_OK"  # nothing to do: no launch
 
 

@@ -1,4 +1,4 @@
-"""GPU parity of fa_bwd (dense, causal, GQA; f16 / bf16, D = 128) against the
+"""GPU parity of fa_bwd (dense, causal, boolean mask, GQA; f16 / bf16, D = 128) against the
 fp64 backward oracle, element by element, on seeded inputs.
 
 Gate per gradient tensor (dq, dk, dv): the GPU path rounds P and dS to the
@@ -38,16 +38,18 @@ def _check(case, got, ref, dtype):
     assert mx <= 12 * u * scale, (case, mx, scale)
 
 
-def run_bwd(case, B, Hq, Hkv, Sq, Skv, dtype, causal, seed):
-    _, q, k, v = synth.dense_inputs(seed, B, Hq, Hkv, Sq, Skv, 128, 128, dtype)
+def run_bwd(case, B, Hq, Hkv, Sq, Skv, dtype, causal, seed, mask_fn=None):
+    g0, q, k, v = synth.dense_inputs(seed, B, Hq, Hkv, Sq, Skv, 128, 128, dtype)
+    mask = mask_fn(g0) if mask_fn else None
     g = synth.rng(seed + 1000)
     dout = synth.cast(synth.normal(g, (B, Hq, Sq, 128)), q.dtype)
     scale = 1 / math.sqrt(128)
     qg, kg, vg, dg = gpu(q, k, v, dout)
-    o, lse = fa.fa_fwd(qg, kg, vg, scale=scale, causal=causal, rescale_threshold=0.0)
-    dq, dk, dv = fa.fa_bwd(qg, kg, vg, o, lse, dg, scale=scale, causal=causal)
+    mg = gpu(mask) if mask is not None else None
+    o, lse = fa.fa_fwd(qg, kg, vg, scale=scale, causal=causal, mask=mg, rescale_threshold=0.0)
+    dq, dk, dv = fa.fa_bwd(qg, kg, vg, o, lse, dg, scale=scale, causal=causal, mask=mg)
     torch.cuda.synchronize()
-    rq, rk, rv = oracle.attn_dense_bwd(q, k, v, dout, scale=scale, causal=causal)
+    rq, rk, rv = oracle.attn_dense_bwd(q, k, v, dout, scale=scale, causal=causal, mask=mask)
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         _check("%s_%s" % (case, name), got, ref, q.dtype)
 
@@ -65,6 +67,25 @@ def test_bwd_cross_lengths(sq, skv):
     # Sq < Skv, Sq > Skv (bottom-right causal: the first Sq - Skv rows see no
     # key and contribute nothing) and one row past a 128-row block.
     run_bwd("bwd_cross_%d_%d" % (sq, skv), 1, 2, 1, sq, skv, "bf16", True, 70 + sq)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_boolean_mask(dtype, causal):
+    # [Sq, Skv] mask with 30% of the positions excluded (diagonal kept), on
+    # the ragged GQA shape: excluded positions get P = 0 in both kernels.
+    run_bwd("bwd_mask_%s_causal%d" % (dtype, causal), 2, 4, 2, 200, 200, dtype, causal, 90 + causal,
+            mask_fn=lambda g: synth.bernoulli_mask(g, 200, 200, 0.3))
+
+
+def test_bwd_mask_per_batch_with_empty_row():
+    # [B, 1, Sq, Skv] mask (one per batch, broadcast over heads), Sq != Skv,
+    # and one fully excluded row (LSE = -inf: it takes and gives no gradient).
+    def m4(g):
+        m = torch.from_numpy((g.random((2, 1, 150, 260)) < 0.2).astype(np.uint8))
+        m[1, 0, 7] = 1
+        return m
+    run_bwd("bwd_mask4d", 2, 4, 2, 150, 260, "bf16", False, 95, mask_fn=m4)
 
 
 def test_bwd_full_size_heads_sampled():
