@@ -78,11 +78,21 @@ def topk_work(w, idx):
     return flops, nbytes
 
 
-def make_call(w, order="idx_a", rescale_threshold=8.0):
+def make_call(w, order="idx_a", rescale_threshold=0.0):
     """Uploads a workload and returns a zero-argument launcher of one forward
-    (dense and block-sparse with the given running-max rescale threshold)."""
+    (dense and block-sparse with the given running-max rescale threshold;
+    0 = the exact running max)."""
     import flashattention_online_softmax_amd as fa
     dev = "cuda"
+    if w["kind"] == "dense" and w.get("split"):
+        q, k, v = (w[n].to(dev) for n in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        B, Hq, Sq, D = q.shape
+        n = fa.load().fa_fwd_splitkv_workspace_elems(B, Hq, Sq, k.shape[2], D, 0)
+        ws = torch.empty(max(n, 1), dtype=torch.float32, device=dev)
+        return lambda: fa.fa_fwd_splitkv(q, k, v, scale=w["scale"], causal=w["causal"], workspace=ws, out=o, lse=lse,
+                                         rescale_threshold=rescale_threshold)
     if w["kind"] == "dense":
         q, k, v = (w[n].to(dev) for n in ("q", "k", "v"))
         mask = w["mask"].to(dev) if w.get("mask") is not None else None
@@ -90,6 +100,12 @@ def make_call(w, order="idx_a", rescale_threshold=8.0):
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
         return lambda: fa.fa_fwd(q, k, v, scale=w["scale"], causal=w["causal"], mask=mask, out=o, lse=lse,
                                  rescale_threshold=rescale_threshold)
+    if w["kind"] == "varlen":
+        q, k, v, cq, ck = (w[n].to(dev) for n in ("q", "k", "v", "cu_q", "cu_k"))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        return lambda: fa.fa_fwd_varlen(q, k, v, cq, ck, w["max_q"], scale=w["scale"], causal=w["causal"], out=o,
+                                        lse=lse, rescale_threshold=rescale_threshold)
     if w["kind"] == "blocksparse":
         q, k, v = (w[n].to(dev) for n in ("q", "k", "v"))
         bi, seq = w["block_idx"].to(dev), w["seqlens"].to(dev)
@@ -102,6 +118,23 @@ def make_call(w, order="idx_a", rescale_threshold=8.0):
     o = torch.empty((q.shape[0], q.shape[1], w["dv"]), dtype=q.dtype, device=dev)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
     return lambda: fa.fa_fwd_topk_gather(q, kv, vv, idx, scale=w["scale"], out=o, lse=lse)
+
+
+def varlen_flops(w):
+    Hq, D = w["q"].shape[1], w["q"].shape[2]
+    lq, lk = np.diff(w["cu_q"].numpy()), np.diff(w["cu_k"].numpy())
+    pairs = sum(causal_pairs(int(a), int(b)) if w["causal"] else int(a) * int(b) for a, b in zip(lq, lk))
+    return 4.0 * D * pairs * Hq
+
+
+def workload_flops(w):
+    if w["kind"] == "dense":
+        return dense_flops(w)
+    if w["kind"] == "varlen":
+        return varlen_flops(w)
+    if w["kind"] == "blocksparse":
+        return blocksparse_flops(w)
+    return topk_work(w, w["idx_a"])[0]
 
 
 def make_bwd_call(w):
@@ -168,13 +201,23 @@ def measured_traffic(workload, launches_per_step=1):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, target_s, threads):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, target_s, threads, seed=99):
     """The fp64 oracle on a bounded random sample of query rows of a dense
     workload; returns TFLOP/s (algorithmic flops of the sampled rows / time)."""
     import oracle
     B, Hq, Sq, D = w["q"].shape
     Skv = w["k"].shape[2]
-    g = np.random.default_rng(99)
+    g = np.random.default_rng(seed)
     kk = w["k"].to(torch.float64).numpy()
     vv = w["v"].to(torch.float64).numpy()
 
@@ -186,6 +229,7 @@ def cpu_baseline(w, target_s, threads):
 
     def flops(rows):
         i = rows % Sq
+        # masked keys of a boolean mask are counted too (the method computes them)
         keys = np.clip(i + (Skv - Sq) + 1, 0, Skv) if w["causal"] else np.full(rows.shape, Skv)
         return 4.0 * D * float(keys.sum())
 
@@ -200,16 +244,96 @@ def cpu_baseline(w, target_s, threads):
             "seconds": t}
 
 
+def cpu_oracle_topk(w, target_s, threads):
+    """The fp64 oracle on a bounded sample of tokens of the top-k workload
+    (all heads of each sampled token); GB/s of algorithmic bytes and TFLOP/s."""
+    import oracle
+    T, Hq, Dqk = w["q"].shape
+    g = np.random.default_rng(98)
+    kv64 = w["kv"].to(torch.float64).numpy()
+    v64 = np.ascontiguousarray(kv64[:, :w["dv"]])
+    idx = w["idx_a"]
+
+    def run(toks):
+        rows = (toks[:, None] * Hq + np.arange(Hq)[None, :]).reshape(-1)
+        t0 = time.perf_counter()
+        oracle.attn_topk(w["q"], kv64, v64, idx, scale=float(np.float32(w["scale"])), rows=rows, nthreads=threads)
+        return time.perf_counter() - t0
+
+    probe = np.sort(g.choice(T, size=min(T, 4), replace=False))
+    t = run(probe)
+    n = int(min(T, max(len(probe), len(probe) * target_s / max(t, 1e-3))))
+    toks = np.sort(g.choice(T, size=n, replace=False))
+    t = run(toks)
+    sub = idx[torch.from_numpy(toks)]
+    valid = int((sub >= 0).sum())
+    es = w["q"].element_size()
+    nbytes = valid * Dqk * es + n * Hq * (Dqk + w["dv"]) * es + sub.numel() * 4 + n * Hq * 4
+    flops = 2.0 * (Dqk + w["dv"]) * valid * Hq
+    return {"gbs": nbytes / t / 1e9, "tflops": flops / t / 1e12, "cores": threads,
+            "sample": "%d random tokens of %d, all %d heads (%.1f s)" % (n, T, Hq, t)}
+
+
+def cpu_oracle_blocksparse(w, target_s, threads):
+    """The fp64 oracle on a bounded sample of query rows of the block-sparse
+    workload; TFLOP/s over the sampled rows' key counts."""
+    import oracle
+    B, Hq, Sq, D = w["q"].shape
+    g = np.random.default_rng(97)
+    lists = w["block_idx"].numpy()
+    seq = w["seqlens"].numpy()
+    blk = w["block"]
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.attn_blocksparse(w["q"], w["k"], w["v"], w["block_idx"], scale=float(np.float32(w["scale"])),
+                                seqlens=w["seqlens"], rows=rows, nthreads=threads)
+        return time.perf_counter() - t0
+
+    def flops(rows):
+        tot = 0
+        for r in rows:
+            i, b = int(r % Sq), int(r // (Hq * Sq))
+            L = int(seq[b])
+            if i >= L:
+                continue
+            tot += sum(max(0, min(L, (x + 1) * blk) - x * blk) for x in lists[i // blk] if x >= 0)
+        return 4.0 * D * tot
+
+    probe = np.sort(g.choice(B * Hq * Sq, size=64 * threads, replace=False))
+    t = run(probe)
+    n = int(min(B * Hq * Sq, max(len(probe), len(probe) * target_s / max(t, 1e-3))))
+    rows = np.sort(g.choice(B * Hq * Sq, size=n, replace=False))
+    t = run(rows)
+    return {"tflops": flops(rows) / t / 1e12, "cores": threads,
+            "sample": "%d random query rows of %d (%.1f s)" % (n, B * Hq * Sq, t)}
+
+
+def time_secondary(name, w, steps, rescale_threshold=0.0):
+    """Kernel time and throughput of one forward workload (secondary figure)."""
+    fl = workload_flops(w)
+    c = make_call(w, rescale_threshold=rescale_threshold)
+    _, km = time_calls(c, steps, 2, 0.3)
+    del c
+    torch.cuda.empty_cache()
+    return {"tflops": round(fl / (km * 1e-3) / 1e12, 2), "kernel_ms": round(km, 4),
+            "frac_mfma_peak": round(fl / (km * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "rescale_threshold_log2": rescale_threshold, "traffic": measured_traffic(name)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="causal_bf16_s4096")
-    ap.add_argument("--no-secondary", action="store_true", help="skip the S=8192 and top-k figures")
-    ap.add_argument("--all", action="store_true", help="also time the GQA+mask and block-sparse workloads")
+    ap.add_argument("--no-secondary", action="store_true", help="skip every secondary figure")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", default=None,
+                    help="time only this workload (any kind) for --steps calls and print its figure; "
+                         "for profiling one kernel")
+    ap.add_argument("--threshold", type=float, default=0.0, help="rescale threshold of --only (log2 units)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the benchmark, run --steps plain device copies of this many "
                          "bytes (the reference kernel for scaling HBM byte counters)")
@@ -236,12 +360,26 @@ def main():
     import flashattention_online_softmax_amd as fa
     fa.load()  # raises if the HIP library is not built
 
+    if args.only:
+        log("only %s (threshold %g)" % (args.only, args.threshold))
+        w = synth.workload(args.only)
+        fl = workload_flops(w)
+        c = make_call(w, rescale_threshold=args.threshold)
+        wall, km = time_calls(c, args.steps, args.warmup, 0.3)
+        out = {"workload": args.only, "kernel_ms": round(km, 4), "tflops": round(fl / (km * 1e-3) / 1e12, 2),
+               "rescale_threshold_log2": args.threshold}
+        if w["kind"] == "topk":
+            out["gbs"] = round(topk_work(w, w["idx_a"])[1] / (km * 1e-3) / 1e9, 1)
+        print(json.dumps(out), flush=True)
+        return
+
     log("generating %s" % args.workload)
     w = synth.workload(args.workload)
     if w["kind"] != "dense":
         raise SystemExit("headline workload must be a dense one")
     flops = dense_flops(w)
-    call = make_call(w)
+    # The contract path: the exact running max (rescale threshold 0).
+    call = make_call(w, rescale_threshold=0.0)
     log("timing %d steps after %d warmup" % (args.steps, args.warmup))
     wall_ms, kern_ms = time_calls(call, args.steps, args.warmup)
     value = flops / (wall_ms * 1e-3) / 1e12
@@ -263,26 +401,35 @@ def main():
         "data": "synthetic (seeded N(0,1), cast to bf16)",
         "config": {"workload": args.workload, "B": B, "H": H, "S": S, "D": D,
                    "causal": bool(w["causal"]), "flops_per_step": flops,
-                   "rescale_threshold_log2": 8.0},
+                   "rescale_threshold_log2": 0.0},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kern_ms, 4)},
     }
     torch.cuda.synchronize()
+    nsec = max(5, args.steps // 2)
 
     if not args.no_secondary:
         sec = {}
-        for name in ["causal_bf16_s8192"] + (["gqa_mask_f16_s8192", "blocksparse_f16_s8192"] if args.all else []):
+        # The lazy rescale (threshold 8) on the same inputs: this machine's
+        # cost of the exact running max.
+        log("secondary %s lazy rescale" % args.workload)
+        c8 = make_call(w, rescale_threshold=8.0)
+        _, km8 = time_calls(c8, nsec, 2, 0.3)
+        del c8
+        sec[args.workload + "_lazy8"] = {"tflops": round(flops / (km8 * 1e-3) / 1e12, 2), "kernel_ms": round(km8, 4),
+                                         "frac_mfma_peak": round(flops / (km8 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                         "exact_max_cost": round(kern_ms / km8 - 1.0, 4)}
+        for name in ("causal_bf16_s8192", "gqa_mask_f16_s8192", "blocksparse_f16_s8192"):
             log("secondary %s" % name)
             w2 = synth.workload(name)
-            fl = dense_flops(w2) if w2["kind"] == "dense" else blocksparse_flops(w2)
-            c2 = make_call(w2)
-            _, km = time_calls(c2, max(5, args.steps // 2), 2, 0.3)
-            sec[name] = {"tflops": round(fl / (km * 1e-3) / 1e12, 2), "kernel_ms": round(km, 4),
-                         "frac_mfma_peak": round(fl / (km * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                         "traffic": measured_traffic(name)}
-            del c2, w2
-            torch.cuda.empty_cache()
+            sec[name] = time_secondary(name, w2, nsec, 0.0)
+            if name == "causal_bf16_s8192":
+                lz = time_secondary(name, w2, nsec, 8.0)
+                lz.pop("traffic")
+                sec[name + "_lazy8"] = lz
+                lz["exact_max_cost"] = round(sec[name]["kernel_ms"] / lz["kernel_ms"] - 1.0, 4)
+            del w2
         log("secondary topk_mla_bf16_t4096")
         w5 = synth.workload("topk_mla_bf16_t4096")
         topk_traffic = measured_traffic("topk_mla_bf16_t4096")
@@ -295,17 +442,7 @@ def main():
                 "kernel_ms": round(km, 4), "frac_hbm_peak": round(nb / (km * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                 "algorithmic_bytes": nb, "traffic": topk_traffic}
             del c5
-        del w5
         torch.cuda.empty_cache()
-        # The headline workload with the exact running max (rescale threshold
-        # 0) instead of the lazy default 8: this machine's cost of exactness.
-        log("secondary %s with the exact running max" % args.workload)
-        c0 = make_call(w, rescale_threshold=0.0)
-        _, km0 = time_calls(c0, max(5, args.steps // 2), 2, 0.3)
-        del c0
-        sec[args.workload + "_exact_max"] = {"tflops": round(flops / (km0 * 1e-3) / 1e12, 2),
-                                             "kernel_ms": round(km0, 4),
-                                             "cost_vs_lazy": round(km0 / kern_ms - 1.0, 4)}
         # The backward of the headline workload (dQ, dK, dV from dO), counted
         # as five products over the causal pairs: 2.5 times the forward's flop.
         log("secondary %s backward" % args.workload)
@@ -323,11 +460,31 @@ def main():
 
     del call
     if not args.no_cpu_baseline:
+        # The machine's CPU share for one GPU is 16 threads; more would oversubscribe it.
         threads = min(16, os.cpu_count() or 1)
         log("cpu baseline (oracle, %d threads, ~%.0f s)" % (threads, args.cpu_seconds))
         cb = cpu_baseline(w, args.cpu_seconds, threads)
         cb.pop("seconds")
         cb["value"] = round(cb["value"], 6)
+        cb["cpu_model"] = cpu_model()
+        cb["threads_note"] = "capped at 16, the host CPU share of one GPU (os.cpu_count() = %d)" % (os.cpu_count() or 0)
+        if not args.no_secondary:
+            # The oracle per configuration, each on a bounded sample (~3 s).
+            per = {}
+            for name in ("dense_f32_s128", "causal_bf16_s8192", "gqa_mask_f16_s8192"):
+                log("cpu oracle %s" % name)
+                w2 = synth.workload(name)
+                r = cpu_baseline(w2, 3.0, threads, seed=96)
+                per[name] = {"tflops": round(r["value"], 6), "sample": r["sample"]}
+                del w2
+            log("cpu oracle blocksparse_f16_s8192")
+            r = cpu_oracle_blocksparse(synth.workload("blocksparse_f16_s8192"), 3.0, threads)
+            per["blocksparse_f16_s8192"] = {"tflops": round(r["tflops"], 6), "sample": r["sample"]}
+            log("cpu oracle topk_mla_bf16_t4096")
+            r = cpu_oracle_topk(synth.workload("topk_mla_bf16_t4096"), 3.0, threads)
+            per["topk_mla_bf16_t4096"] = {"gbs": round(r["gbs"], 3), "tflops": round(r["tflops"], 6),
+                                          "sample": r["sample"]}
+            cb["per_config"] = per
         result["cpu_baseline"] = cb
 
     print(json.dumps(result), flush=True)

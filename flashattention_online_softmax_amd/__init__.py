@@ -8,9 +8,9 @@ built library or on a CPU tensor these functions raise.
 
 Functions (same names as the C entry points):
   fa_fwd(q, k, v, scale=..., causal=False, mask=None, seqlens_q=None, seqlens_k=None,
-         rescale_threshold=8.0)
+         rescale_threshold=0.0)
   fa_fwd_blocksparse(q, k, v, block_idx, scale=..., block_q=128, block_k=128, seqlens=None,
-                     rescale_threshold=8.0)
+                     rescale_threshold=0.0)
   fa_fwd_topk_gather(q, k, v, idx, scale=...)
 each returning (o, lse).
 """
@@ -47,7 +47,7 @@ _lib = None
 def declared_functions():
     """Names of the functions include/fa.h declares."""
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:fa_status|const char\s*\*|int)\s+(fa_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:fa_status|const char\s*\*|int|int64_t)\s+(fa_\w+)\s*\(", text, re.M)))
 
 
 def load():
@@ -59,13 +59,23 @@ def load():
                           "%s is missing; build it with flashattention_online_softmax_amd.build" % LIB_PATH)
         lib = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER(FaTensor)
-        lib.fa_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_int, ctypes.c_float, ctypes.c_float, P, P,
+        lib.fa_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_int, ctypes.c_float, ctypes.c_float, P, P, P,
                                ctypes.c_void_p]
         lib.fa_fwd_blocksparse.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_float,
                                            ctypes.c_float, P, P, ctypes.c_void_p]
-        lib.fa_fwd_topk_gather.argtypes = [P, P, P, P, ctypes.c_float, P, P, ctypes.c_void_p]
-        lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P, P, P, P, ctypes.c_void_p]
-        for f in (lib.fa_fwd, lib.fa_fwd_blocksparse, lib.fa_fwd_topk_gather, lib.fa_bwd):
+        lib.fa_fwd_topk_gather.argtypes = [P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_void_p]
+        lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P, P, P, P,
+                               ctypes.c_void_p]
+        lib.fa_fwd_varlen.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                      P, P, ctypes.c_void_p]
+        lib.fa_fwd_splitkv.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_int,
+                                       P, P, P, ctypes.c_void_p]
+        lib.fa_fwd_splitkv_splits.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
+        lib.fa_fwd_splitkv_splits.restype = ctypes.c_int
+        lib.fa_fwd_splitkv_workspace_elems.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int]
+        lib.fa_fwd_splitkv_workspace_elems.restype = ctypes.c_int64
+        for f in (lib.fa_fwd, lib.fa_fwd_blocksparse, lib.fa_fwd_topk_gather, lib.fa_bwd, lib.fa_fwd_varlen,
+                  lib.fa_fwd_splitkv):
             f.restype = ctypes.c_int
         lib.fa_status_str.argtypes = [ctypes.c_int]
         lib.fa_status_str.restype = ctypes.c_char_p
@@ -115,18 +125,33 @@ def _stream(stream):
 
 
 # Rescale threshold (log2 units) of the dense and block-sparse entry points when
-# none is given: the lazy default of the flash-attention forward described on the
-# sparse-MLA page (threshold-branch section). 0 selects the exact running max.
-DEFAULT_RESCALE_THRESHOLD = 8.0
+# none is given: 0, the exact running max (a row's reference max moves on every
+# growth, so its largest weight is exactly 1 before P.V). The lazy rescale of the
+# flash-attention sparse-MLA page (threshold-branch section) is the opt-in
+# rescale_threshold=8.
+DEFAULT_RESCALE_THRESHOLD = 0.0
+
+
+def _o_lo(want, o_lo, out):
+    """The fp32 rounding-residual output: the caller's tensor, a new one when
+    asked for (want=True), or None."""
+    if o_lo is not None:
+        return o_lo
+    if want:
+        return torch.empty(out.shape, dtype=torch.float32, device=out.device)
+    return None
 
 
 def fa_fwd(q, k, v, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k=None,
-           rescale_threshold=DEFAULT_RESCALE_THRESHOLD, out=None, lse=None, stream=None):
+           rescale_threshold=DEFAULT_RESCALE_THRESHOLD, out=None, lse=None, return_o_lo=False, o_lo=None,
+           stream=None):
     """Dense/causal/masked/GQA attention forward. q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D];
     mask uint8/bool [Sq,Skv] or [B|1,Hq|1,Sq,Skv] (nonzero = excluded);
-    rescale_threshold in [0, 10] (0 = exact running max)."""
+    rescale_threshold in [0, 10] (0 = exact running max). Returns (o, lse),
+    or (o, lse, o_lo) with return_o_lo / o_lo given: o_lo = fp32(O) - o,
+    the output's rounding residual."""
     lib = load()
-    _need_gpu(q, k, v, mask, seqlens_q, seqlens_k)
+    _need_gpu(q, k, v, mask, seqlens_q, seqlens_k, o_lo)
     B, Hq, Sq, _ = q.shape
     if out is None:
         out = torch.empty((B, Hq, Sq, v.shape[3]), dtype=q.dtype, device=q.device)
@@ -134,22 +159,24 @@ def fa_fwd(q, k, v, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     if mask is not None and mask.dtype == torch.bool:
         mask = mask.view(torch.uint8)
+    lo = _o_lo(return_o_lo, o_lo, out)
     _check(lib.fa_fwd(_ref(describe(q)), _ref(describe(k)), _ref(describe(v)), _ref(describe(mask)),
                       _ref(describe(seqlens_q)), _ref(describe(seqlens_k)), int(bool(causal)),
-                      float(scale), float(rescale_threshold), _ref(describe(out)), _ref(describe(lse)),
-                      _stream(stream)))
-    return out, lse
+                      float(scale), float(rescale_threshold), _ref(describe(out)), _ref(describe(lo)),
+                      _ref(describe(lse)), _stream(stream)))
+    return (out, lse) if lo is None else (out, lse, lo)
 
 
-def fa_bwd(q, k, v, o, lse, dout, *, scale, causal=False, mask=None, dq=None, dk=None, dv=None, delta=None,
-           stream=None):
+def fa_bwd(q, k, v, o, lse, dout, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k=None, o_lo=None,
+           dq=None, dk=None, dv=None, delta=None, stream=None):
     """Gradients (dq, dk, dv) of the dense/causal/masked/GQA forward given
     its output o, its lse and the output gradient dout (f16/bf16, D = 128);
-    mask as fa_fwd's (uint8, non-zero = excluded).
+    mask and sequence lengths as fa_fwd's; o_lo (the forward's rounding
+    residual) makes Delta = dO . (o + o_lo).
     delta (fp32 [B,Hq,Sq]) is the kernels' workspace; it is allocated here
     when not given."""
     lib = load()
-    _need_gpu(q, k, v, o, lse, dout, mask)
+    _need_gpu(q, k, v, o, lse, dout, mask, seqlens_q, seqlens_k, o_lo)
     if dq is None:
         dq = torch.empty_like(q)
     if dk is None:
@@ -158,7 +185,10 @@ def fa_bwd(q, k, v, o, lse, dout, *, scale, causal=False, mask=None, dq=None, dk
         dv = torch.empty_like(v)
     if delta is None:
         delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    _check(lib.fa_bwd(_ref(describe(q)), _ref(describe(k)), _ref(describe(v)), _ref(describe(mask)), _ref(describe(o)),
+    if mask is not None and mask.dtype == torch.bool:
+        mask = mask.view(torch.uint8)
+    _check(lib.fa_bwd(_ref(describe(q)), _ref(describe(k)), _ref(describe(v)), _ref(describe(mask)),
+                      _ref(describe(seqlens_q)), _ref(describe(seqlens_k)), _ref(describe(o)), _ref(describe(o_lo)),
                       _ref(describe(lse)), _ref(describe(dout)), int(bool(causal)), float(scale),
                       _ref(describe(delta)), _ref(describe(dq)), _ref(describe(dk)), _ref(describe(dv)),
                       _stream(stream)))
@@ -183,21 +213,68 @@ def fa_fwd_blocksparse(q, k, v, block_idx, *, scale, block_q=128, block_k=128, s
     return out, lse
 
 
-def fa_fwd_topk_gather(q, k, v, idx, *, scale, out=None, lse=None, stream=None):
+def fa_fwd_topk_gather(q, k, v, idx, *, scale, out=None, lse=None, return_o_lo=False, o_lo=None, stream=None):
     """Top-k gathered MLA attention forward. q [T,Hq,Dqk], k [S,Dqk], v [S,Dv]
-    (v may be k[:, :Dv]), idx int32 [T,W] (negative = unused)."""
+    (v may be k[:, :Dv]), idx int32 [T,W] (negative = unused). Returns
+    (o, lse), or (o, lse, o_lo) as fa_fwd."""
     lib = load()
-    _need_gpu(q, k, v, idx)
+    _need_gpu(q, k, v, idx, o_lo)
     T, Hq, _ = q.shape
     if out is None:
         out = torch.empty((T, Hq, v.shape[1]), dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    lo = _o_lo(return_o_lo, o_lo, out)
     _check(lib.fa_fwd_topk_gather(_ref(describe(q)), _ref(describe(k)), _ref(describe(v)),
-                                  _ref(describe(idx)), float(scale), _ref(describe(out)),
+                                  _ref(describe(idx)), float(scale), _ref(describe(out)), _ref(describe(lo)),
                                   _ref(describe(lse)), _stream(stream)))
-    return out, lse
+    return (out, lse) if lo is None else (out, lse, lo)
 
 
 def version():
     return load().fa_version()
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, *, scale, causal=False,
+                  rescale_threshold=DEFAULT_RESCALE_THRESHOLD, out=None, lse=None, stream=None):
+    """Packed variable-length (TND) forward: q [Tq,Hq,D], k/v [Tk,Hkv,D],
+    cu_seqlens_q / cu_seqlens_k int32 [B+1] on the GPU; returns (o [Tq,Hq,Dv],
+    lse [Tq,Hq])."""
+    lib = load()
+    _need_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if out is None:
+        out = torch.zeros((q.shape[0], q.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.full((q.shape[0], q.shape[1]), float("-inf"), dtype=torch.float32, device=q.device)
+    _check(lib.fa_fwd_varlen(_ref(describe(q)), _ref(describe(k)), _ref(describe(v)), _ref(describe(cu_seqlens_q)),
+                             _ref(describe(cu_seqlens_k)), int(max_seqlen_q), int(bool(causal)), float(scale),
+                             float(rescale_threshold), _ref(describe(out)), _ref(describe(lse)), _stream(stream)))
+    return out, lse
+
+
+def splitkv_splits(B, Hq, Sq, Skv, num_splits=0):
+    """Number of key ranges fa_fwd_splitkv uses for these sizes."""
+    return load().fa_fwd_splitkv_splits(B, Hq, Sq, Skv, num_splits)
+
+
+def fa_fwd_splitkv(q, k, v, *, scale, causal=False, seqlens_q=None, seqlens_k=None, num_splits=0,
+                   rescale_threshold=DEFAULT_RESCALE_THRESHOLD, workspace=None, out=None, lse=None, stream=None):
+    """Split-KV forward (fa_fwd's semantics, for few rows over many keys); the
+    fp32 workspace is allocated here when not given."""
+    lib = load()
+    _need_gpu(q, k, v, seqlens_q, seqlens_k, workspace)
+    B, Hq, Sq, _ = q.shape
+    Skv, Dv = k.shape[2], v.shape[3]
+    if out is None:
+        out = torch.empty((B, Hq, Sq, Dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = lib.fa_fwd_splitkv_workspace_elems(B, Hq, Sq, Skv, Dv, int(num_splits))
+        if n > 0:
+            workspace = torch.empty(n, dtype=torch.float32, device=q.device)
+    _check(lib.fa_fwd_splitkv(_ref(describe(q)), _ref(describe(k)), _ref(describe(v)), _ref(describe(seqlens_q)),
+                              _ref(describe(seqlens_k)), int(bool(causal)), float(scale), float(rescale_threshold),
+                              int(num_splits), _ref(describe(workspace)), _ref(describe(out)), _ref(describe(lse)),
+                              _stream(stream)))
+    return out, lse

@@ -21,7 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["fa_abi.hip", "fa_dense.hip", "fa_topk.hip", "fa_module.hip", "fa_bwd.hip"]
+SOURCES = ["fa_abi.hip", "fa_dense.hip", "fa_topk.hip", "fa_module.hip", "fa_bwd.hip", "fa_split.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 LLVM_BIN = os.environ.get("FA_LLVM_BIN", "/opt/rocm/lib/llvm/bin")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

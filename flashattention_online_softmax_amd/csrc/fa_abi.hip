@@ -1,5 +1,6 @@
 // C ABI of libfa.so: argument validation on the host, then dispatch to the
 // gfx950 kernels on the caller's stream. See include/fa.h for the contract.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -103,6 +104,18 @@ fa_status check_seqlens(const char* name, const fa_tensor* t, int64_t B) {
   return FA_OK;
 }
 
+// Optional fp32 rounding residual shaped like o (16-byte aligned rows).
+fa_status check_o_lo(const fa_tensor* o_lo, const fa_tensor* o) {
+  if (!o_lo) return FA_OK;
+  fa_status s = check_tensor("o_lo", o_lo, o->ndim, true);
+  if (s != FA_OK) return s;
+  if ((s = check_dtype("o_lo", o_lo, FA_F32)) != FA_OK) return s;
+  for (int i = 0; i < o->ndim; ++i)
+    if (o_lo->shape[i] != o->shape[i]) return fail(FA_ERR_SHAPE, "o_lo must be shaped like o");
+  if (o->dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "o_lo is for 16-bit outputs");
+  return FA_OK;
+}
+
 fa_status hip_status(hipError_t e) {
   if (e == hipSuccess) return FA_OK;
   return fail(FA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
@@ -182,6 +195,33 @@ void fill_common(fa::FwdParams& p, const fa_tensor* q, const fa_tensor* k, const
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.rescale_thr = rescale_threshold;
+  p.lse_sb = (int64_t)p.Hq * p.Sq;
+  p.lse_sh = p.Sq;
+  p.lse_ss = 1;
+  p.n_splits = 1;
+}
+
+// Split-KV sizing shared by the entry points and the sizing helpers: the
+// number of key ranges (the requested count, or with 0 enough workgroups to
+// give every compute unit two, at least 384 keys per range, at most 64
+// ranges), each a multiple of 192 keys (whole 64- and 96-key tiles); ranges
+// past the keys are dropped.
+constexpr int kSplitGranule = 192;
+constexpr int kMaxSplits = 64;
+
+int split_plan(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int requested, int* split_len) {
+  if (B < 0 || Hq < 0 || Sq < 0 || Skv < 0 || requested < 0) return -1;
+  int ns = requested;
+  if (ns == 0) {
+    const int64_t base = ((Sq + 255) / 256) * B * Hq;
+    ns = base > 0 ? (int)std::min<int64_t>(kMaxSplits, (512 + base - 1) / base) : 1;
+    ns = (int)std::min<int64_t>(ns, std::max<int64_t>(1, Skv / 384));
+  }
+  ns = std::max(1, std::min(ns, kMaxSplits));
+  int64_t len = Skv > 0 ? (Skv + ns - 1) / ns : kSplitGranule;
+  len = (len + kSplitGranule - 1) / kSplitGranule * kSplitGranule;
+  if (split_len) *split_len = (int)len;
+  return Skv > 0 ? (int)((Skv + len - 1) / len) : 1;
 }
 
 fa::Dt to_dt(int32_t d) { return d == FA_F32 ? fa::Dt::F32 : d == FA_F16 ? fa::Dt::F16 : fa::Dt::BF16; }
@@ -216,10 +256,12 @@ static fa_status parse_mask(const fa_tensor* mask, int64_t B, int64_t Hq, int64_
 
 fa_status fa_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* mask,
                  const fa_tensor* seqlens_q, const fa_tensor* seqlens_k, int causal, float scale,
-                 float rescale_threshold, const fa_tensor* o, const fa_tensor* lse, void* stream) {
+                 float rescale_threshold, const fa_tensor* o, const fa_tensor* o_lo, const fa_tensor* lse,
+                 void* stream) {
   clear_error();
   fa_status s = check_bnsd(q, k, v, o, lse, scale, rescale_threshold);
   if (s != FA_OK) return s;
+  if ((s = check_o_lo(o_lo, o)) != FA_OK) return s;
   if (causal != 0 && causal != 1) return fail(FA_ERR_VALUE, "causal must be 0 or 1");
   const int64_t B = q->shape[0], Hq = q->shape[1], Sq = q->shape[2], Skv = k->shape[2];
   if ((s = check_seqlens("seqlens_q", seqlens_q, B)) != FA_OK) return s;
@@ -236,6 +278,12 @@ fa_status fa_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
   }
   p.seqlens_q = seqlens_q ? (const int32_t*)seqlens_q->data : nullptr;
   p.seqlens_k = seqlens_k ? (const int32_t*)seqlens_k->data : nullptr;
+  if (o_lo && numel(o_lo) > 0) {
+    p.o_lo = (float*)o_lo->data;
+    p.ol_sb = o_lo->stride[0];
+    p.ol_sh = o_lo->stride[1];
+    p.ol_ss = o_lo->stride[2];
+  }
   if (B * Hq * Sq == 0) return FA_OK;
   const bool has_mask = mask && numel(mask) > 0;
   if (mask && !has_mask && Skv > 0) return fail(FA_ERR_SHAPE, "mask is empty");
@@ -282,7 +330,7 @@ fa_status fa_fwd_blocksparse(const fa_tensor* q, const fa_tensor* k, const fa_te
 
 fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
                              const fa_tensor* idx, float scale, const fa_tensor* o,
-                             const fa_tensor* lse, void* stream) {
+                             const fa_tensor* o_lo, const fa_tensor* lse, void* stream) {
   clear_error();
   fa_status s;
   if ((s = check_tensor("q", q, 3, true)) != FA_OK) return s;
@@ -308,7 +356,6 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
   if ((s = check_contiguous("lse", lse)) != FA_OK) return s;
   if (!scale_ok(scale)) return fail(FA_ERR_VALUE, "scale must be finite and > 0");
   if (Dqk != 576 || Dv != 512) return fail(FA_ERR_UNSUPPORTED, "only Dqk = 576, Dv = 512 is supported");
-  if (Hq % 32 != 0) return fail(FA_ERR_UNSUPPORTED, "Hq (%lld) must be a multiple of 32", (long long)Hq);
   if (W > 4096) return fail(FA_ERR_UNSUPPORTED, "W (%lld) > 4096", (long long)W);
   if (!fits_i32(T * Hq) || !fits_i32(S) || !fits_i32(W)) return fail(FA_ERR_UNSUPPORTED, "problem too large");
   // Bytes spanned by k and v (the gathers address them with 32-bit offsets).
@@ -316,6 +363,7 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
   const int64_t v_bytes = S > 0 ? (S - 1) * v->stride[0] * 2 + Dv * 2 : 0;
   if (k_bytes > 0xFFFFFFFFLL || v_bytes > 0xFFFFFFFFLL)
     return fail(FA_ERR_UNSUPPORTED, "k and v must each span less than 4 GiB");
+  if ((s = check_o_lo(o_lo, o)) != FA_OK) return s;
   if (T * Hq == 0) return FA_OK;
   if (W > 0 && !idx->data) return fail(FA_ERR_NULL, "idx.data is NULL");
   fa::TopkParams p;
@@ -329,6 +377,11 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
   p.q_st = q->stride[0]; p.q_sh = q->stride[1];
   p.k_ss = k->stride[0]; p.v_ss = v->stride[0];
   p.o_st = o->stride[0]; p.o_sh = o->stride[1];
+  if (o_lo && numel(o_lo) > 0) {
+    p.o_lo = (float*)o_lo->data;
+    p.ol_st = o_lo->stride[0];
+    p.ol_sh = o_lo->stride[1];
+  }
   p.idx_st = idx->stride[0];
   p.T = (int32_t)T; p.Hq = (int32_t)Hq; p.S = (int32_t)S; p.W = (int32_t)W;
   p.k_bytes = (uint32_t)k_bytes; p.v_bytes = (uint32_t)v_bytes;
@@ -338,13 +391,17 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
 }
 
 fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* mask,
-                 const fa_tensor* o, const fa_tensor* lse, const fa_tensor* dout, int causal, float scale,
+                 const fa_tensor* seqlens_q, const fa_tensor* seqlens_k, const fa_tensor* o,
+                 const fa_tensor* o_lo, const fa_tensor* lse, const fa_tensor* dout, int causal, float scale,
                  const fa_tensor* delta, const fa_tensor* dq, const fa_tensor* dk,
                  const fa_tensor* dv, void* stream) {
   clear_error();
   fa_status s = check_bnsd(q, k, v, o, lse, scale, 0.f);
   if (s != FA_OK) return s;
   if (causal != 0 && causal != 1) return fail(FA_ERR_VALUE, "causal must be 0 or 1");
+  if ((s = check_seqlens("seqlens_q", seqlens_q, q->shape[0])) != FA_OK) return s;
+  if ((s = check_seqlens("seqlens_k", seqlens_k, q->shape[0])) != FA_OK) return s;
+  if ((s = check_o_lo(o_lo, o)) != FA_OK) return s;
   if (q->dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "the backward takes f16 or bf16");
   if (q->shape[3] != 128) return fail(FA_ERR_UNSUPPORTED, "the backward supports head dim 128 only");
   if ((s = check_tensor("dout", dout, 4, true)) != FA_OK) return s;
@@ -397,9 +454,157 @@ fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
     if ((s = parse_mask(mask, p.B, p.Hq, p.Sq, p.Skv, &p.m_sb, &p.m_sh, &p.m_ss)) != FA_OK) return s;
     p.mask = (const uint8_t*)mask->data;
   }
+  p.seqlens_q = seqlens_q ? (const int32_t*)seqlens_q->data : nullptr;
+  p.seqlens_k = seqlens_k ? (const int32_t*)seqlens_k->data : nullptr;
+  if (o_lo && numel(o_lo) > 0) {
+    p.o_lo = (const float*)o_lo->data;
+    p.ol_sb = o_lo->stride[0];
+    p.ol_sh = o_lo->stride[1];
+    p.ol_ss = o_lo->stride[2];
+  }
   if ((int64_t)p.B * p.Hq * p.Sq == 0 && (int64_t)p.B * p.Hkv * p.Skv == 0) return FA_OK;
   const bool has_mask = mask && numel(mask) > 0;
   return hip_status(fa::launch_bwd(to_dt(q->dtype), causal != 0, has_mask, p, (hipStream_t)stream));
+}
+
+fa_status fa_fwd_varlen(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* cu_seqlens_q,
+                        const fa_tensor* cu_seqlens_k, int max_seqlen_q, int causal, float scale,
+                        float rescale_threshold, const fa_tensor* o, const fa_tensor* lse, void* stream) {
+  clear_error();
+  fa_status s;
+  if ((s = check_tensor("q", q, 3, true)) != FA_OK) return s;
+  if ((s = check_tensor("k", k, 3, true)) != FA_OK) return s;
+  if ((s = check_tensor("v", v, 3, true)) != FA_OK) return s;
+  if ((s = check_tensor("o", o, 3, true)) != FA_OK) return s;
+  if ((s = check_tensor("lse", lse, 2, false)) != FA_OK) return s;
+  if ((s = check_tensor("cu_seqlens_q", cu_seqlens_q, 1, false)) != FA_OK) return s;
+  if ((s = check_tensor("cu_seqlens_k", cu_seqlens_k, 1, false)) != FA_OK) return s;
+  if (q->dtype != FA_F16 && q->dtype != FA_BF16)
+    return fail(FA_ERR_DTYPE, "q dtype must be f16 or bf16, got %s", dtype_name(q->dtype));
+  if ((s = check_dtype("k", k, q->dtype)) != FA_OK) return s;
+  if ((s = check_dtype("v", v, q->dtype)) != FA_OK) return s;
+  if ((s = check_dtype("o", o, q->dtype)) != FA_OK) return s;
+  if ((s = check_dtype("lse", lse, FA_F32)) != FA_OK) return s;
+  if ((s = check_dtype("cu_seqlens_q", cu_seqlens_q, FA_I32)) != FA_OK) return s;
+  if ((s = check_dtype("cu_seqlens_k", cu_seqlens_k, FA_I32)) != FA_OK) return s;
+  const int64_t Tq = q->shape[0], Hq = q->shape[1], D = q->shape[2];
+  const int64_t Tk = k->shape[0], Hkv = k->shape[1], Dv = v->shape[2];
+  const int64_t nb = cu_seqlens_q->shape[0];
+  if (nb < 1 || cu_seqlens_k->shape[0] != nb)
+    return fail(FA_ERR_SHAPE, "cu_seqlens_q and cu_seqlens_k must both have B + 1 >= 1 entries");
+  if (k->shape[2] != D) return fail(FA_ERR_SHAPE, "k head dim differs from q's");
+  if (v->shape[0] != Tk || v->shape[1] != Hkv) return fail(FA_ERR_SHAPE, "v must match k in rows and heads");
+  if (o->shape[0] != Tq || o->shape[1] != Hq || o->shape[2] != Dv) return fail(FA_ERR_SHAPE, "o must be [Tq, Hq, Dv]");
+  if (lse->shape[0] != Tq || lse->shape[1] != Hq) return fail(FA_ERR_SHAPE, "lse must be [Tq, Hq]");
+  if ((s = check_contiguous("lse", lse)) != FA_OK) return s;
+  if (Hkv == 0 && Tq * Hq > 0) return fail(FA_ERR_SHAPE, "k has no heads");
+  if (Hkv > 0 && Hq % Hkv != 0) return fail(FA_ERR_SHAPE, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_VALUE, "causal must be 0 or 1");
+  if (max_seqlen_q < 0) return fail(FA_ERR_VALUE, "max_seqlen_q must be >= 0");
+  if (!scale_ok(scale)) return fail(FA_ERR_VALUE, "scale must be finite and > 0");
+  if (!(rescale_threshold >= 0.f && rescale_threshold <= kMaxRescaleThreshold))
+    return fail(FA_ERR_VALUE, "rescale_threshold must be in [0, %g]", (double)kMaxRescaleThreshold);
+  if (D != Dv) return fail(FA_ERR_UNSUPPORTED, "D (%lld) != Dv (%lld) is not supported", (long long)D, (long long)Dv);
+  if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "head dim %lld not supported (64 or 128)", (long long)D);
+  if (!fits_i32(Tq) || !fits_i32(Tk) || !fits_i32(nb * Hq) || !fits_i32(Tq * Hq))
+    return fail(FA_ERR_UNSUPPORTED, "problem too large for 32-bit row indexing");
+  if (k->stride[0] > (1 << 22) || v->stride[0] > (1 << 22))
+    return fail(FA_ERR_UNSUPPORTED, "k/v row stride above 2^22 elements is not supported");
+  const int64_t B = nb - 1;
+  if (B * Hq * (int64_t)max_seqlen_q == 0 || Tq == 0) return FA_OK;
+  fa::FwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q->data;
+  p.k = k->data;
+  p.v = v->data;
+  p.o = o->data;
+  p.lse = (float*)lse->data;
+  p.q_sh = q->stride[1]; p.q_ss = q->stride[0];
+  p.k_sh = k->stride[1]; p.k_ss = k->stride[0];
+  p.v_sh = v->stride[1]; p.v_ss = v->stride[0];
+  p.o_sh = o->stride[1]; p.o_ss = o->stride[0];
+  p.lse_sh = lse->stride[1]; p.lse_ss = lse->stride[0];
+  p.B = (int32_t)B;
+  p.Hq = (int32_t)Hq;
+  p.Hkv = (int32_t)Hkv;
+  p.G = (int32_t)(Hq / Hkv);
+  p.Sq = max_seqlen_q;
+  p.Skv = (int32_t)Tk;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.rescale_thr = rescale_threshold;
+  p.n_splits = 1;
+  p.cu_q = (const int32_t*)cu_seqlens_q->data;
+  p.cu_k = (const int32_t*)cu_seqlens_k->data;
+  return hip_status(fa::launch_varlen(to_dt(q->dtype), (int)D, causal != 0, p, (hipStream_t)stream));
+}
+
+int fa_fwd_splitkv_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int num_splits) {
+  return split_plan(B, Hq, Sq, Skv, num_splits, nullptr);
+}
+
+int64_t fa_fwd_splitkv_workspace_elems(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int64_t Dv, int num_splits) {
+  const int ns = split_plan(B, Hq, Sq, Skv, num_splits, nullptr);
+  if (ns < 0 || Dv < 0) return -1;
+  return ns > 1 ? (int64_t)ns * B * Hq * Sq * (Dv + 1) : 0;
+}
+
+// Body of the split-KV entry point: the partial results go to the caller's
+// workspace tensor.
+static fa_status splitkv_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* seqlens_q,
+                              const fa_tensor* seqlens_k, int causal, float scale, float rescale_threshold,
+                              int num_splits, const fa_tensor* workspace, bool static_scratch, const fa_tensor* o,
+                              const fa_tensor* lse, void* stream);
+
+fa_status fa_fwd_splitkv(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* seqlens_q,
+                         const fa_tensor* seqlens_k, int causal, float scale, float rescale_threshold, int num_splits,
+                         const fa_tensor* workspace, const fa_tensor* o, const fa_tensor* lse, void* stream) {
+  clear_error();
+  return splitkv_impl(q, k, v, seqlens_q, seqlens_k, causal, scale, rescale_threshold, num_splits, workspace,
+                      false, o, lse, stream);
+}
+
+static fa_status splitkv_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* seqlens_q,
+                              const fa_tensor* seqlens_k, int causal, float scale, float rescale_threshold,
+                              int num_splits, const fa_tensor* workspace, bool static_scratch, const fa_tensor* o,
+                              const fa_tensor* lse, void* stream) {
+  fa_status s = check_bnsd(q, k, v, o, lse, scale, rescale_threshold);
+  if (s != FA_OK) return s;
+  if (q->dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "the split-KV forward takes f16 or bf16");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_VALUE, "causal must be 0 or 1");
+  if (num_splits < 0 || num_splits > kMaxSplits) return fail(FA_ERR_VALUE, "num_splits must be in [0, %d]", kMaxSplits);
+  const int64_t B = q->shape[0], Hq = q->shape[1], Sq = q->shape[2], Skv = k->shape[2], Dv = v->shape[3];
+  if ((s = check_seqlens("seqlens_q", seqlens_q, B)) != FA_OK) return s;
+  if ((s = check_seqlens("seqlens_k", seqlens_k, B)) != FA_OK) return s;
+  fa::FwdParams p;
+  fill_common(p, q, k, v, o, lse, scale, rescale_threshold);
+  p.seqlens_q = seqlens_q ? (const int32_t*)seqlens_q->data : nullptr;
+  p.seqlens_k = seqlens_k ? (const int32_t*)seqlens_k->data : nullptr;
+  int split_len = 0;
+  const int ns = split_plan(B, Hq, Sq, Skv, num_splits, &split_len);
+  if (B * Hq * Sq == 0) return FA_OK;
+  if (ns <= 1)  // one key range: the plain forward, no workspace
+    return hip_status(fa::launch_dense(to_dt(q->dtype), (int)q->shape[3], causal != 0, false, false, p,
+                                       (hipStream_t)stream));
+  const int64_t need = (int64_t)ns * B * Hq * Sq * (Dv + 1);
+  float* ws = nullptr;
+  if (!static_scratch) {
+    if ((s = check_tensor("workspace", workspace, 1, true)) != FA_OK) return s;
+    if ((s = check_dtype("workspace", workspace, FA_F32)) != FA_OK) return s;
+    if (workspace->shape[0] < need)
+      return fail(FA_ERR_SHAPE, "workspace holds %lld floats, %d key ranges need %lld", (long long)workspace->shape[0],
+                  ns, (long long)need);
+    ws = (float*)workspace->data;
+  } else {
+    return fail(FA_ERR_NULL, "workspace is NULL");
+  }
+  if (!fits_i32((int64_t)ns * B * Hq * ((Sq + 255) / 256)))  // one workgroup per (range, 256 rows, head)
+    return fail(FA_ERR_UNSUPPORTED, "too many workgroups");
+  p.n_splits = ns;
+  p.split_len = split_len;
+  p.part_o = ws;
+  p.part_lse = p.part_o + (int64_t)ns * B * Hq * Sq * Dv;
+  return hip_status(fa::launch_splitkv(to_dt(q->dtype), (int)q->shape[3], causal != 0, p, (hipStream_t)stream));
 }
 
 const char* fa_status_str(fa_status s) {
@@ -418,6 +623,6 @@ const char* fa_status_str(fa_status s) {
 
 const char* fa_last_error(void) { return g_err; }
 
-int fa_version(void) { return 200; }
+int fa_version(void) { return 300; }
 
 }  // extern "C"

@@ -122,6 +122,12 @@ __device__ __forceinline__ void store_t(uint16_t* base, int64_t stride, int r, c
     }
 }
 
+// Sequence lengths of batch b (without the vectors: Sq and Skv).
+__device__ __forceinline__ void batch_lengths(const BwdParams& p, int b, int& lq, int& lk) {
+  lq = p.seqlens_q ? max(0, min(p.seqlens_q[b], p.Sq)) : p.Sq;
+  lk = p.seqlens_k ? max(0, min(p.seqlens_k[b], p.Skv)) : p.Skv;
+}
+
 template <class T>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
   const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
@@ -135,6 +141,19 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
     const u32x4 ov = *(const u32x4*)o, dv = *(const u32x4*)d;
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc = T::dot2(ov[e], dv[e], acc);
+    if (p.o_lo) {
+      // The forward's rounding residual: Delta from O + o_lo, the unrounded
+      // fp32 output (the precise dpsum of the sparse-MLA page).
+      const float* lo = p.o_lo + b * p.ol_sb + hq * p.ol_sh + i * p.ol_ss + 8 * sub;
+      const float4 l0 = *(const float4*)lo, l1 = *(const float4*)(lo + 4);
+      const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 dd = T::unpack2(dv[e]);
+        acc = __builtin_fmaf(dd[0], lv[2 * e], acc);
+        acc = __builtin_fmaf(dd[1], lv[2 * e + 1], acc);
+      }
+    }
   }
 #pragma unroll
   for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
@@ -160,7 +179,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   const int bk = lin % nbk, b = bk / p.Hkv, hkv = bk % p.Hkv;
   const int k0 = (lin / nbk) * BLK;
   const int key = k0 + 32 * (w & 3) + c;  // this lane's key (column of S)
-  const int diag = p.Skv - p.Sq;
+  int Lq, Lk;
+  batch_lengths(p, b, Lq, Lk);
+  const int diag = Lk - Lq;  // key j is visible to row i iff j <= i + diag
   const uint16_t* kg = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh;
   const uint16_t* vg = (const uint16_t*)p.v + (int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh;
   u32x4 kop[BD / 16], vop[BD / 16];
@@ -173,7 +194,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
   // Query rows that can see a key of this block: i >= k0 - diag (causal).
   const int qfirst = CAUSAL ? max(0, k0 - diag) : 0;
-  const int nqt = p.Sq > qfirst ? (p.Sq - qfirst + TR - 1) / TR : 0;
+  const int nqt = (k0 < Lk && Lq > qfirst) ? (Lq - qfirst + TR - 1) / TR : 0;
   // The sweep: step it = (query head hq, query tile t) of the group, tiles
   // fetched one step ahead into registers.
   const int nsteps = p.G * nqt;
@@ -248,7 +269,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
     for (int i = 0; i < 16; ++i) {
       const int r = 8 * (i >> 2) + 4 * h + (i & 3);
       const int qi = q0 + r;
-      bool ok = key < p.Skv && qi < p.Sq;
+      bool ok = key < Lk && qi < Lq;
       if (CAUSAL) ok = ok && key <= qi + diag;
       if (MASK) ok = ok && mk[(int64_t)qi * p.m_ss] == 0;
       const float pv = ok ? fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, -lr[i])) : 0.f;
@@ -281,7 +302,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   const int bh = lin % nbh, b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.G;
   const int q0 = (CAUSAL ? (int)gridDim.x - 1 - lin / nbh : lin / nbh) * BLK;
   const int qi = q0 + 32 * w + c;  // this lane's query row (column of S^T)
-  const int diag = p.Skv - p.Sq;
+  int Lq, Lk;
+  batch_lengths(p, b, Lq, Lk);
+  const int diag = Lk - Lq;
   // mask bytes of the lane's query row (read only where qi < Sq)
   const uint8_t* mq = MASK ? p.mask + (int64_t)b * p.m_sb + (int64_t)hq * p.m_sh + (int64_t)qi * p.m_ss : nullptr;
   const uint16_t* qg = (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh;
@@ -292,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   load_bop(qop, qg, p.q_ss, min(qi, p.Sq - 1));
   load_bop(dop, dg, p.do_ss, min(qi, p.Sq - 1));
   float l2 = INFINITY, del = 0.f;  // padding rows and rows without keys: P = 0
-  if (qi < p.Sq) {
+  if (qi < Lq) {
     const float l = p.lse[((int64_t)b * p.Hq + hq) * p.Sq + qi];
     l2 = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
     del = p.delta[((int64_t)b * p.Hq + hq) * p.Sq + qi];
@@ -303,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dq_t[dt][i] = 0.f;
   // Keys any row of this block sees: j <= q0 + BLK - 1 + diag (causal).
-  const int kend = CAUSAL ? max(0, min(p.Skv, q0 + BLK + diag)) : p.Skv;
+  const int kend = q0 >= Lq ? 0 : CAUSAL ? max(0, min(Lk, q0 + BLK + diag)) : Lk;
   const int nkt = (kend + TR - 1) / TR;
   TileRegs<> rk, rv;
   auto fetch = [&](int t) __attribute__((always_inline)) {
@@ -344,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kj = j0 + 8 * (i >> 2) + 4 * h + (i & 3);
-      bool ok = kj < p.Skv && qi < p.Sq;
+      bool ok = kj < Lk && qi < Lq;
       if (CAUSAL) ok = ok && kj <= qi + diag;
       if (MASK) ok = ok && mq[kj] == 0;
       const float pv = ok ? fast_exp2(__builtin_fmaf(s0[i], p.scale_log2, -l2)) : 0.f;

@@ -85,7 +85,7 @@ __global__ void __launch_bounds__(256) fwd32_kernel(const FwdParams p) {
     __syncthreads();
     n_iter = s_n;
   } else {
-    n_iter = dense_tiles<CAUSAL>(wk, MPH, BN32);
+    n_iter = dense_tiles<CAUSAL>(wk, MPH, BN32, diag);
   }
 
   const float* qg = (const float*)p.q + wk.b * p.q_sb + wk.hq * p.q_sh;
@@ -206,16 +206,18 @@ void set_grid(FwdParams& p, dim3& grid) {
   grid = dim3((unsigned)p.n_mblocks * p.B * p.Hkv * p.n_hgroups);
 }
 
-// Launches kernel fa_fwd16_<tn>_d<D>_w<NW>_q<QT>_h<HP>_c<C>m<M>s<S> of the
-// 16-bit code object.
+// Launches kernel fa_fwd16_<tn>_d<D>_w<NW>_q<QT>_h<HP>_c<C>m<M>s<S>x<XM> of
+// the 16-bit code object (XM: 0 BNSD, 1 packed variable-length, 2 split-KV
+// partials, one workgroup per key range as well).
 template <int NW, int QT, int HP>
 hipError_t launch16_named(const char* tn, int D, bool causal, bool mask, bool sparse, FwdParams& p,
-                          hipStream_t st) {
+                          hipStream_t st, int xm = 0) {
   dim3 grid;
   set_grid<NW, QT, HP>(p, grid);
-  char name[80];
-  snprintf(name, sizeof(name), "fa_fwd16_%s_d%d_w%d_q%d_h%d_c%dm%ds%d", tn, D, NW, QT, HP,
-           causal ? 1 : 0, mask ? 1 : 0, sparse ? 1 : 0);
+  if (xm == 2) grid.x *= (unsigned)p.n_splits;
+  char name[96];
+  snprintf(name, sizeof(name), "fa_fwd16_%s_d%d_w%d_q%d_h%d_c%dm%ds%dx%d", tn, D, NW, QT, HP,
+           causal ? 1 : 0, mask ? 1 : 0, sparse ? 1 : 0, xm);
   hipFunction_t fn = nullptr;
   hipError_t e = code_object_function(name, &fn);
   if (e != hipSuccess) return e;
@@ -256,6 +258,29 @@ hipError_t launch_dense(Dt dt, int D, bool causal, bool has_mask, bool sparse, F
   if (dt == Dt::F32) return D == 128 ? launch32d<128>(causal, has_mask, sparse, p, stream)
                                      : launch32d<64>(causal, has_mask, sparse, p, stream);
   return launch16(dt == Dt::F16 ? "f16" : "bf16", D, causal, has_mask, sparse, p, stream);
+}
+
+hipError_t launch_varlen(Dt dt, int D, bool causal, FwdParams& p, hipStream_t stream) {
+  return launch16_named<8, 1, 1>(dt == Dt::F16 ? "f16" : "bf16", D, causal, false, false, p, stream, 1);
+}
+
+hipError_t launch_splitkv(Dt dt, int D, bool causal, FwdParams& p, hipStream_t stream) {
+  hipError_t e = launch16_named<8, 1, 1>(dt == Dt::F16 ? "f16" : "bf16", D, causal, false, false, p, stream, 2);
+  if (e != hipSuccess) return e;
+  MergeParams m;
+  m.part_o = p.part_o;
+  m.part_lse = p.part_lse;
+  m.o = p.o;
+  m.lse = p.lse;
+  m.o_sb = p.o_sb;
+  m.o_sh = p.o_sh;
+  m.o_ss = p.o_ss;
+  m.B = p.B;
+  m.Hq = p.Hq;
+  m.Sq = p.Sq;
+  m.Dv = D;
+  m.n_splits = p.n_splits;
+  return launch_merge(dt, m, stream);
 }
 
 }  // namespace fa

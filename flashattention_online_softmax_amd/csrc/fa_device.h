@@ -44,6 +44,10 @@ struct F16 {
   static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
   }
+  // The two packed values as floats (exact).
+  static __device__ __forceinline__ f32x2 unpack2(uint32_t w) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+  }
 };
 
 struct BF16 {
@@ -64,6 +68,10 @@ struct BF16 {
   // acc + a.lo b.lo + a.hi b.hi in fp32 (v_dot2_f32_bf16).
   static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+  }
+  // The two packed values as floats (exact: a bf16 is the upper half of a float).
+  static __device__ __forceinline__ f32x2 unpack2(uint32_t w) {
+    return f32x2{__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
   }
 };
 

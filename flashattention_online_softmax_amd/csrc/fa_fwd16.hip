@@ -72,7 +72,12 @@ namespace {
 //
 // K and V tiles live in three-deep LDS rings (tile t in slot t % 3), filled
 // by LDS-DMA copies issued three (K) and two (V) tiles ahead of use.
-template <class T, int D, int NW, int QT, int HP, bool CAUSAL, bool MASK, bool SPARSE>
+//
+// XM = 1: packed variable-length batches (cu_q / cu_k give each batch's rows
+// and keys); XM = 2: split-KV, the workgroup sweeps only the keys
+// [split * split_len, (split + 1) * split_len) and writes its normalised fp32
+// output and LSE to the partial-result buffers instead of O and LSE.
+template <class T, int D, int NW, int QT, int HP, bool CAUSAL, bool MASK, bool SPARSE, int XM>
 __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   constexpr int WPH = NW / HP;
   constexpr int MPH = WPH * QT * 32;
@@ -102,14 +107,23 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   const int lane = tid & 63;
   const int h = lane >> 5;
   const int c = lane & 31;
-  const Work wk = decode_work<NW, QT, HP>(p);
+  Work wk = decode_work<NW, QT, HP, XM>(p);
   const int diag = wk.Lk - wk.Lq;  // key j is visible to row i iff j <= i + diag
+  // First key of this workgroup's range; under split-KV its range ends at
+  // wk.Lk (keys from there on are masked like keys past the sequence).
+  int klo = 0;
+  if (XM == 2) {
+    klo = wk.split * p.split_len;
+    wk.Lk = min(wk.Lk, klo + p.split_len);
+  }
+  // Rows of this head: Sq, or the batch's own length in the packed layout.
+  const int rlim = XM == 1 ? wk.Lq : p.Sq;
 
   int n_iter;
   if (SPARSE)
     n_iter = build_sparse_tiles(p, wk, wk.wg_row0 / 128, s_kstart, &s_n);
   else
-    n_iter = dense_tiles<CAUSAL>(wk, MPH, BNT);
+    n_iter = dense_tiles<CAUSAL>(wk, MPH, BNT, diag, klo);
   // Tiles this wave works on: none if its rows are past Lq; under the causal
   // mask only the tiles that start at or before its last visible key.
   int n_act = n_iter;
@@ -117,13 +131,13 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     n_act = 0;
   } else if (CAUSAL && !SPARSE) {
     const int last_key = min(wk.row0 + QT * 32 - 1, wk.Lq - 1) + diag;
-    n_act = last_key < 0 ? 0 : min(n_iter, last_key / BNT + 1);
+    n_act = last_key < klo ? 0 : min(n_iter, (last_key - klo) / BNT + 1);
   }
   n_act = __builtin_amdgcn_readfirstlane(n_act);
 
-  const uint16_t* qg = (const uint16_t*)p.q + wk.b * p.q_sb + wk.hq * p.q_sh;
-  const uint16_t* kg = (const uint16_t*)p.k + wk.b * p.k_sb + wk.hkv * p.k_sh;
-  const uint16_t* vg = (const uint16_t*)p.v + wk.b * p.v_sb + wk.hkv * p.v_sh;
+  const uint16_t* qg = (const uint16_t*)p.q + wk.b * p.q_sb + wk.hq * p.q_sh + (int64_t)wk.qoff * p.q_ss;
+  const uint16_t* kg = (const uint16_t*)p.k + wk.b * p.k_sb + wk.hkv * p.k_sh + (int64_t)wk.koff * p.k_ss;
+  const uint16_t* vg = (const uint16_t*)p.v + wk.b * p.v_sb + wk.hkv * p.v_sh + (int64_t)wk.koff * p.v_ss;
 
   u32x4 qop[QT][DS];  // Q^T operands, loaded after the first tile copies
 
@@ -151,7 +165,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     for (int ks = 0; ks < NKS; ++ks) pp[0][b][ks] = u32x4{0u, 0u, 0u, 0u};
   }
 
-  auto tile_start = [&](int it) __attribute__((always_inline)) { return SPARSE ? s_kstart[it] : it * BNT; };
+  auto tile_start = [&](int it) __attribute__((always_inline)) { return SPARSE ? s_kstart[it] : klo + it * BNT; };
 
   const TileCopy<D, NW, false, BNT> kcopy(kg, p.k_ss);
   const TileCopy<D, NW, true, BNT> vcopy(vg, p.v_ss);
@@ -476,7 +490,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       u32x4 z = {0u, 0u, 0u, 0u};
-      if (qrow < p.Sq) z = *(const u32x4*)(qg + (int64_t)qrow * p.q_ss + 16 * ds + 8 * h);
+      if (qrow < rlim) z = *(const u32x4*)(qg + (int64_t)qrow * p.q_ss + 16 * ds + 8 * h);
       qop[b][ds] = z;
     }
   }
@@ -538,10 +552,37 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   // (free now: every wave is past its last ring read and copy) so that each
   // store instruction writes whole rows, 16 bytes per lane; LSE = ln2 (m +
   // log2 l) in fp32. Rows with no key give O = 0 and LSE = -inf.
+  if constexpr (XM == 2) {
+    // Split-KV: this key range's normalised fp32 output and LSE (natural
+    // log; -inf and zeros when the range has no visible key) for the merge.
+    const int64_t rbase = (int64_t)wk.split * ((int64_t)p.B * p.Hq * p.Sq) + ((int64_t)wk.b * p.Hq + wk.hq) * p.Sq;
+#pragma unroll
+    for (int b = 0; b < QT; ++b) {
+      mfma_wait_v(oacc[b]);
+      const int qrow = wk.row0 + 32 * b + c;
+      const float lt = half_sum(l_run[b]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      if (qrow < p.Sq) {
+        float* dst = p.part_o + (rbase + qrow) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *(float4*)(dst + 32 * dt + 8 * g + 4 * h) =
+                make_float4(oacc[b][dt][4 * g] * inv, oacc[b][dt][4 * g + 1] * inv, oacc[b][dt][4 * g + 2] * inv,
+                            oacc[b][dt][4 * g + 3] * inv);
+        if (h == 0) p.part_lse[rbase + qrow] = lt > 0.f ? (m_ref[b] + log2f(lt)) * kLn2 : -INFINITY;
+      }
+    }
+    return;
+  }
   constexpr int OPAD = D + 8;  // padded LDS row: a 16-byte bank shift per row
   static_assert(NW * QT * 32 * OPAD <= 6 * TILE, "O staging fits in the rings");
   uint16_t* const s_o = s_ring + ((int)threadIdx.x >> 6) * (QT * 32 * OPAD);
-  uint16_t* og = (uint16_t*)p.o + wk.b * p.o_sb + wk.hq * p.o_sh;
+  uint16_t* og = (uint16_t*)p.o + wk.b * p.o_sb + wk.hq * p.o_sh + (int64_t)wk.qoff * p.o_ss;
+  // With o_lo, the fp32 residual O - rounded(O) of each element goes to HBM
+  // straight from the registers (4 consecutive columns per lane and store).
+  float* const olo = p.o_lo ? p.o_lo + wk.b * p.ol_sb + wk.hq * p.ol_sh + (int64_t)wk.qoff * p.ol_ss : nullptr;
 #pragma unroll
   for (int b = 0; b < QT; ++b) {
     mfma_wait_v(oacc[b]);
@@ -553,13 +594,20 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        const float x0 = oacc[b][dt][4 * g] * inv, x1 = oacc[b][dt][4 * g + 1] * inv;
+        const float x2 = oacc[b][dt][4 * g + 2] * inv, x3 = oacc[b][dt][4 * g + 3] * inv;
         u32x2 v;
-        v[0] = T::pack2(oacc[b][dt][4 * g] * inv, oacc[b][dt][4 * g + 1] * inv);
-        v[1] = T::pack2(oacc[b][dt][4 * g + 2] * inv, oacc[b][dt][4 * g + 3] * inv);
+        v[0] = T::pack2(x0, x1);
+        v[1] = T::pack2(x2, x3);
         *(u32x2*)(orow + 32 * dt + 8 * g + 4 * h) = v;
+        if (olo && qrow < rlim) {
+          const f32x2 r0 = T::unpack2(v[0]), r1 = T::unpack2(v[1]);
+          *(float4*)(olo + (int64_t)qrow * p.ol_ss + 32 * dt + 8 * g + 4 * h) =
+              make_float4(x0 - r0[0], x1 - r0[1], x2 - r1[0], x3 - r1[1]);
+        }
       }
-    if (h == 0 && qrow < p.Sq)
-      p.lse[((int64_t)wk.b * p.Hq + wk.hq) * p.Sq + qrow] =
+    if (h == 0 && qrow < rlim)
+      p.lse[wk.b * p.lse_sb + wk.hq * p.lse_sh + (int64_t)(wk.qoff + qrow) * p.lse_ss] =
           lt > 0.f ? (m_ref[b] + log2f(lt)) * kLn2 : -INFINITY;
   }
   // The wave reads back what its own lanes wrote (LDS operations of a wave
@@ -574,7 +622,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     const int r = k * RPI + lane / CPR, ch = lane % CPR;
     const int qrow = wk.row0 + r;
     const u32x4 v = *(const u32x4*)(s_o + r * OPAD + 8 * ch);
-    if (qrow < p.Sq) *(u32x4*)(og + (int64_t)qrow * p.o_ss + 8 * ch) = v;
+    if (qrow < rlim) *(u32x4*)(og + (int64_t)qrow * p.o_ss + 8 * ch) = v;
   }
 }
 
@@ -582,19 +630,24 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
 }  // namespace fa
 
 // Kernel entry points (names are looked up by the library at run time):
-// fa_fwd16_<dtype>_d<D>_w<waves>_q<32-row blocks per wave>_h<heads>_c<causal>m<mask>s<sparse>.
-#define FA_FWD16_KERNEL(TN, T, D, NW, QT, HP, C, M, S)                                            \
-  extern "C" __global__ void __launch_bounds__(NW * 64, 1)                                          \
-      fa_fwd16_##TN##_d##D##_w##NW##_q##QT##_h##HP##_c##C##m##M##s##S(const fa::FwdParams p) {     \
-    fa::fwd16_body<fa::T, D, NW, QT, HP, C != 0, M != 0, S != 0>(p);                                \
+// fa_fwd16_<dtype>_d<D>_w<waves>_q<32-row blocks per wave>_h<heads>_c<causal>m<mask>s<sparse>x<mode>,
+// mode 0 = BNSD, 1 = packed variable-length batches, 2 = split-KV partials.
+#define FA_FWD16_KERNEL(TN, T, D, NW, QT, HP, C, M, S, X)                                              \
+  extern "C" __global__ void __launch_bounds__(NW * 64, 1)                                             \
+      fa_fwd16_##TN##_d##D##_w##NW##_q##QT##_h##HP##_c##C##m##M##s##S##x##X(const fa::FwdParams p) {  \
+    fa::fwd16_body<fa::T, D, NW, QT, HP, C != 0, M != 0, S != 0, X>(p);                                 \
   }
-#define FA_FWD16_DTYPE_D(TN, T, D)                 \
-  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 0, 0, 0)      \
-  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 0, 1, 0)      \
-  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 1, 0, 0)      \
-  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 1, 1, 0)      \
-  FA_FWD16_KERNEL(TN, T, D, 8, 1, 2, 0, 0, 1)      \
-  FA_FWD16_KERNEL(TN, T, D, 4, 1, 1, 0, 0, 1)
+#define FA_FWD16_DTYPE_D(TN, T, D)                    \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 0, 0, 0, 0)      \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 0, 1, 0, 0)      \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 1, 0, 0, 0)      \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 1, 1, 0, 0)      \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 2, 0, 0, 1, 0)      \
+  FA_FWD16_KERNEL(TN, T, D, 4, 1, 1, 0, 0, 1, 0)      \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 0, 0, 0, 1)      \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 1, 0, 0, 1)      \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 0, 0, 0, 2)      \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 1, 0, 0, 2)
 
 FA_FWD16_DTYPE_D(f16, F16, 64)
 FA_FWD16_DTYPE_D(f16, F16, 128)

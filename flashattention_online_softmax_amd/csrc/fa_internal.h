@@ -15,6 +15,7 @@ struct FwdParams {
   const void* k;
   const void* v;
   void* o;
+  float* o_lo;             // nullable, fp32 like o: O - rounded(O)
   float* lse;              // [B, Hq, Sq] contiguous
   const uint8_t* mask;     // nullable; element (b, hq, i, j) at b*m_sb + hq*m_sh + i*m_ss + j
   const int32_t* seqlens_q;  // nullable [B]
@@ -24,6 +25,7 @@ struct FwdParams {
   int64_t k_sb, k_sh, k_ss;
   int64_t v_sb, v_sh, v_ss;
   int64_t o_sb, o_sh, o_ss;
+  int64_t ol_sb, ol_sh, ol_ss;
   int64_t m_sb, m_sh, m_ss;
   int64_t bi_sb, bi_sh, bi_sq;
   int32_t B, Hq, Hkv, G, Sq, Skv;
@@ -35,6 +37,30 @@ struct FwdParams {
   float scale;             // softmax scale (LSE is reported in these units)
   float scale_log2;        // scale * log2(e): scores enter exp2 through one FMA
   float rescale_thr;       // running-max rescale threshold, log2 units (0 = exact)
+  // LSE element (b, hq, i) at lse[b * lse_sb + hq * lse_sh + i * lse_ss].
+  int64_t lse_sb, lse_sh, lse_ss;
+  // Packed variable-length (TND) layout: the query rows of batch b are rows
+  // cu_q[b] .. cu_q[b+1]-1 of q, o and lse (Sq is the longest of them), its
+  // keys rows cu_k[b] .. cu_k[b+1]-1 of k and v; the batch strides are 0.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  // Split-KV: the keys of a row block are cut into n_splits ranges of
+  // split_len keys; each workgroup writes its range's normalised fp32 output
+  // and LSE to part_o [n_splits, B*Hq*Sq, Dv] and part_lse [n_splits, B*Hq*Sq]
+  // for the merge kernel.
+  int32_t n_splits, split_len;
+  float* part_o;
+  float* part_lse;
+};
+
+// Inputs of the split-KV merge: the partial results above into O and LSE.
+struct MergeParams {
+  const float* part_o;
+  const float* part_lse;
+  void* o;
+  float* lse;  // [B, Hq, Sq] contiguous
+  int64_t o_sb, o_sh, o_ss;
+  int32_t B, Hq, Sq, Dv, n_splits;
 };
 
 // Top-k gathered MLA forward parameters.
@@ -43,11 +69,13 @@ struct TopkParams {
   const void* k;     // [S, Dqk]
   const void* v;     // [S, Dv]
   void* o;           // [T, Hq, Dv]
+  float* o_lo;       // nullable [T, Hq, Dv] fp32: O - rounded(O)
   float* lse;        // [T, Hq]
   const int32_t* idx;  // [T, W]
   int64_t q_st, q_sh;
   int64_t k_ss, v_ss;
   int64_t o_st, o_sh;
+  int64_t ol_st, ol_sh;
   int64_t idx_st;
   int32_t T, Hq, S, W;
   uint32_t k_bytes, v_bytes;  // bytes spanned by k and v
@@ -76,6 +104,10 @@ struct BwdParams {
   int64_t dq_sb, dq_sh, dq_ss;
   const uint8_t* mask;  // NULL, or [B|1, Hq|1, Sq, Skv] bytes, non-zero = excluded
   int64_t m_sb, m_sh, m_ss;  // 0 for a broadcast dim
+  const int32_t* seqlens_q;  // nullable [B]: rows i >= Lq_b have no keys
+  const int32_t* seqlens_k;  // nullable [B]: keys j >= Lk_b are excluded
+  const float* o_lo;   // nullable [B, Hq, Sq, Dv] fp32: O - rounded(O) of the forward
+  int64_t ol_sb, ol_sh, ol_ss;
   int64_t dk_sb, dk_sh, dk_ss;
   int64_t dv_sb, dv_sh, dv_ss;
   int32_t B, Hq, Hkv, G, Sq, Skv;
@@ -90,6 +122,13 @@ hipError_t code_object_function(const char* name, hipFunction_t* fn);
 // Launchers: enqueue on `stream`, return the HIP status of the launch.
 hipError_t launch_dense(Dt dt, int D, bool causal, bool has_mask, bool sparse,
                         FwdParams& p, hipStream_t stream);
+// Packed variable-length forward (p.cu_q / p.cu_k set; 16-bit, no mask).
+hipError_t launch_varlen(Dt dt, int D, bool causal, FwdParams& p, hipStream_t stream);
+// Split-KV forward (p.n_splits > 1, p.split_len, p.part_o / p.part_lse set)
+// followed by the merge into p.o / p.lse.
+hipError_t launch_splitkv(Dt dt, int D, bool causal, FwdParams& p, hipStream_t stream);
+// The merge alone (fa_split.hip).
+hipError_t launch_merge(Dt dt, const MergeParams& m, hipStream_t stream);
 hipError_t launch_topk(Dt dt, TopkParams& p, hipStream_t stream);
 hipError_t launch_bwd(Dt dt, bool causal, bool mask, BwdParams& p, hipStream_t stream);
 

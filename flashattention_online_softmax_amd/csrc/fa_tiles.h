@@ -28,6 +28,8 @@ __device__ __forceinline__ int vswz(int row) {
 
 struct Work {
   int b, hkv, hq, wg_row0, row0, Lq, Lk;
+  int qoff, koff;  // packed layout: first row of the batch in q / k (else 0)
+  int split;       // split-KV: the key range index (else 0)
 };
 
 // Decodes blockIdx.x into (query block, head group, KV head, batch); the
@@ -39,7 +41,12 @@ struct Work {
 // different lengths (per-batch sequence lengths) no longer leave whole XCDs
 // idle; when B Hkv is a multiple of 8 n_hgroups the rotation keeps every
 // pair on its XCD.
-template <int NW, int QT, int HP>
+//
+// XM selects the extra modes of the 16-bit kernels: 1 = packed
+// variable-length batches (row and key offsets and lengths from cu_q / cu_k),
+// 2 = split-KV (the split index varies slower than the head and faster than
+// the query block).
+template <int NW, int QT, int HP, int XM = 0>
 __device__ __forceinline__ Work decode_work(const FwdParams& p) {
   constexpr int WPH = NW / HP;
   constexpr int MPH = WPH * QT * 32;
@@ -47,8 +54,17 @@ __device__ __forceinline__ Work decode_work(const FwdParams& p) {
   const int BHkv = p.B * p.Hkv;
   const int per_mb = BHkv * p.n_hgroups;
   const int id = blockIdx.x;
-  const int mb_rank = id / per_mb;
-  const int r = id - mb_rank * per_mb;
+  int mb_rank, r, split = 0;
+  if (XM == 2) {
+    const int per = per_mb * p.n_splits;
+    mb_rank = id / per;
+    const int r2 = id - mb_rank * per;
+    split = r2 / per_mb;
+    r = r2 - split * per_mb;
+  } else {
+    mb_rank = id / per_mb;
+    r = id - mb_rank * per_mb;
+  }
   const int mb = p.n_mblocks - 1 - mb_rank;
   const int hg = r / BHkv;
   const int bkv = (r - hg * BHkv + hg * (BHkv / p.n_hgroups)) % BHkv;
@@ -60,8 +76,18 @@ __device__ __forceinline__ Work decode_work(const FwdParams& p) {
   wk.wg_row0 = mb * MPH;
   wk.row0 = wk.wg_row0 + wi * QT * 32;
   int lq = p.Sq, lk = p.Skv;
-  if (p.seqlens_q) lq = max(0, min(p.seqlens_q[wk.b], p.Sq));
-  if (p.seqlens_k) lk = max(0, min(p.seqlens_k[wk.b], p.Skv));
+  wk.qoff = 0;
+  wk.koff = 0;
+  wk.split = split;
+  if (XM == 1) {
+    wk.qoff = p.cu_q[wk.b];
+    wk.koff = p.cu_k[wk.b];
+    lq = max(0, min(p.cu_q[wk.b + 1] - wk.qoff, p.Sq));
+    lk = max(0, p.cu_k[wk.b + 1] - wk.koff);
+  } else {
+    if (p.seqlens_q) lq = max(0, min(p.seqlens_q[wk.b], p.Sq));
+    if (p.seqlens_k) lk = max(0, min(p.seqlens_k[wk.b], p.Skv));
+  }
   wk.Lq = lq;
   wk.Lk = lk;
   return wk;
@@ -103,16 +129,18 @@ __device__ __forceinline__ int build_sparse_tiles(const FwdParams& p, const Work
   return *s_n;
 }
 
-// Number of bn-key tiles of a dense (optionally causal) workgroup.
+// Number of bn-key tiles of a dense (optionally causal) workgroup whose keys
+// start at klo and end before wk.Lk; key j is visible to row i iff
+// j <= i + diag under the causal mask.
 template <bool CAUSAL>
-__device__ __forceinline__ int dense_tiles(const Work& wk, int mph, int bn) {
+__device__ __forceinline__ int dense_tiles(const Work& wk, int mph, int bn, int diag, int klo = 0) {
   if (wk.wg_row0 >= wk.Lq) return 0;
   int kend = wk.Lk;
   if (CAUSAL) {
     const int last_row = min(wk.wg_row0 + mph, wk.Lq) - 1;
-    kend = min(kend, last_row + (wk.Lk - wk.Lq) + 1);
+    kend = min(kend, last_row + diag + 1);
   }
-  return kend > 0 ? (kend + bn - 1) / bn : 0;
+  return kend > klo ? (kend - klo + bn - 1) / bn : 0;
 }
 
 }  // namespace fa

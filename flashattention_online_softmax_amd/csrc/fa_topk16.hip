@@ -168,7 +168,7 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
   const int tb = (int)blockIdx.x / p.n_htiles;
   const int t = p.T - 1 - tb;
   const int head0 = ((int)blockIdx.x - tb * p.n_htiles) * 128 + w * 32;
-  const bool active = head0 < p.Hq;  // Hq is a multiple of 32
+  const bool active = head0 < p.Hq;
 
   // The index row first, into registers (thread tid owns the slots
   // [tid*spt, tid*spt + spt), spt <= 16): the compaction below then waits
@@ -193,16 +193,18 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
   asm volatile("" ::: "memory");  // keep the Q loads behind the index loads
 
   // Q^T operands (B operand of S^T): qop[ht][ks] = Q[t, head 16 ht + n,
-  // 32 ks + 8 G .. +7]. A wave past Hq computes on heads 0..31 and stores
-  // nothing.
+  // 32 ks + 8 G .. +7]. Query heads are padded to the wave's 32: a head at or
+  // past Hq computes on head Hq - 1 and stores nothing (a wave past Hq
+  // entirely stores nothing at all).
   u32x4 qop[2][KSTEP];
   {
-    const uint16_t* qb =
-        (const uint16_t*)p.q + (int64_t)t * p.q_st + (int64_t)((active ? head0 : 0) + n) * p.q_sh + 8 * G;
+    const uint16_t* qt = (const uint16_t*)p.q + (int64_t)t * p.q_st + 8 * G;
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
+    for (int ht = 0; ht < 2; ++ht) {
+      const int hh = min(head0 + 16 * ht + n, p.Hq - 1);
 #pragma unroll
-      for (int ks = 0; ks < KSTEP; ++ks) qop[ht][ks] = *(const u32x4*)(qb + 16 * ht * p.q_sh + 32 * ks);
+      for (int ks = 0; ks < KSTEP; ++ks) qop[ht][ks] = *(const u32x4*)(qt + (int64_t)hh * p.q_sh + 32 * ks);
+    }
   }
 
   // Compact the valid indices of row t into s_list (list order kept).
@@ -537,15 +539,25 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
     const float lt = quad_sum(l_run[ht]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int r = 16 * ht + n;
+    const bool head_ok = active && head0 + r < p.Hq;
+    // With o_lo, the fp32 residual O - rounded(O) goes to HBM straight from
+    // the registers (4 consecutive columns per lane and store).
+    float* const olo = (p.o_lo && head_ok) ? p.o_lo + (int64_t)t * p.ol_st + (int64_t)(head0 + r) * p.ol_sh : nullptr;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
+      const float x0 = oacc[dt][ht][0] * inv, x1 = oacc[dt][ht][1] * inv;
+      const float x2 = oacc[dt][ht][2] * inv, x3 = oacc[dt][ht][3] * inv;
       u32x2 v;
-      v[0] = T::pack2(oacc[dt][ht][0] * inv, oacc[dt][ht][1] * inv);
-      v[1] = T::pack2(oacc[dt][ht][2] * inv, oacc[dt][ht][3] * inv);
+      v[0] = T::pack2(x0, x1);
+      v[1] = T::pack2(x2, x3);
       // columns 16 dt + 4 G .. +3: chunk 2 dt + G / 2, bytes 8 (G % 2) in it
       *(u32x2*)(st_at(r, 2 * dt + (G >> 1)) + 8 * (G & 1)) = v;
+      if (olo) {
+        const f32x2 r0 = T::unpack2(v[0]), r1 = T::unpack2(v[1]);
+        *(float4*)(olo + 16 * dt + 4 * G) = make_float4(x0 - r0[0], x1 - r0[1], x2 - r1[0], x3 - r1[1]);
+      }
     }
-    if (active && G == 0)
+    if (head_ok && G == 0)
       p.lse[(int64_t)t * p.Hq + head0 + r] = lt > 0.f ? (m_run[ht] + log2f(lt)) * kLn2 : -INFINITY;
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -553,10 +565,11 @@ __device__ __forceinline__ void topk16_body(const TopkParams& p) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if (active) {
     uint16_t* const ob = (uint16_t*)p.o + (int64_t)t * p.o_st + (int64_t)head0 * p.o_sh;
+    const int nh = min(32, p.Hq - head0);  // valid heads of this wave (a padded last tile)
 #pragma unroll 8
     for (int r = 0; r < 32; ++r) {
       const u32x4 v = *(const u32x4*)st_at(r, lane);
-      *(u32x4*)(ob + (int64_t)r * p.o_sh + 8 * lane) = v;
+      if (r < nh) *(u32x4*)(ob + (int64_t)r * p.o_sh + 8 * lane) = v;
     }
   }
 }

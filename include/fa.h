@@ -102,9 +102,16 @@ typedef enum fa_status {
  *       (sequence-length-cut) query/key lengths: bottom-right alignment.
  *  scale   finite float > 0 multiplying q.k (the scale of the attention
  *       formula); scale * log2(e) must be a normal float.
- *  rescale_threshold  in [0, 10], log2 units: 0 = exact running max; the
- *       sparse-MLA page's lazy default for the forward is 8.
+ *  rescale_threshold  in [0, 10], log2 units: 0 = exact running max (the
+ *       contract path); the sparse-MLA page's lazy value for the forward
+ *       is 8 (its threshold-selection section).
  *  o    [B, Hq, Sq, Dv] in q's dtype (BNSD, strided)
+ *  o_lo NULL, or fp32 [B, Hq, Sq, Dv] (strided, rows 16-byte aligned): on
+ *       return it holds fp32(O) - rounded(O) per element, the rounding
+ *       residual of the output, so that o + o_lo is the unrounded fp32 result
+ *       (the o_lo output and its use for a precise dpsum on the sparse-MLA
+ *       page, order-invariance-test and impact-on-backward sections). Only
+ *       for fp16 / bf16 outputs.
  *  lse  fp32 [B, Hq, Sq], contiguous; natural-log LSE of the scaled scores.
  *
  * Supported: D == Dv in {64, 128}; K/V row strides up to 2^22 elements.
@@ -114,7 +121,7 @@ typedef enum fa_status {
 fa_status fa_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
                  const fa_tensor* mask, const fa_tensor* seqlens_q,
                  const fa_tensor* seqlens_k, int causal, float scale,
-                 float rescale_threshold, const fa_tensor* o,
+                 float rescale_threshold, const fa_tensor* o, const fa_tensor* o_lo,
                  const fa_tensor* lse, void* stream);
 
 /*
@@ -157,16 +164,20 @@ fa_status fa_fwd_blocksparse(const fa_tensor* q, const fa_tensor* k, const fa_te
  *      negative = unused slot (anywhere in the row). An index >= S is not
  *      detected; it reads key row S - 1 (never memory outside k or v).
  *  o   [T, Hq, Dv] in q's dtype (strided)
+ *  o_lo NULL, or fp32 [T, Hq, Dv] (strided, rows 16-byte aligned): the
+ *      output's rounding residual fp32(O) - rounded(O), as in fa_fwd
  *  lse fp32 [T, Hq], contiguous
  *
- * Supported: Dqk == 576, Dv == 512, Hq a multiple of 32, W <= 4096, and k
- * and v each spanning less than 4 GiB ((S - 1) * row stride + row length,
- * in bytes: the gathers use 32-bit byte offsets). Rows with no valid index
- * give O = 0 and LSE = -inf.
+ * Supported: Dqk == 576, Dv == 512, any Hq >= 1 (query heads are processed
+ * 32 per wave; a partial last group is padded, as the sparse-MLA page's
+ * background section pads query heads to the tile, and its padding heads
+ * store nothing), W <= 4096, and k and v each spanning less than 4 GiB
+ * ((S - 1) * row stride + row length, in bytes: the gathers use 32-bit byte
+ * offsets). Rows with no valid index give O = 0 and LSE = -inf.
  */
 fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
                              const fa_tensor* idx, float scale, const fa_tensor* o,
-                             const fa_tensor* lse, void* stream);
+                             const fa_tensor* o_lo, const fa_tensor* lse, void* stream);
 
 /*
  * Attention backward (dense, optional causal and boolean masks, GQA): the gradients of the
@@ -182,13 +193,22 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
  *              excluded); P is 0 at excluded positions, so they receive no
  *              gradient (the atten_mask input of the FlashAttentionScoreGrad
  *              page, section 5.2)
- *  o           the forward output for these q, k, v, mask, causal, scale
+ *  seqlens_q, seqlens_k  NULL or int32 [B], as fa_fwd: rows i >= seqlens_q[b]
+ *              and keys j >= seqlens_k[b] take part in nothing, and their
+ *              gradients dq / dk / dv are written as zeros (the per-batch
+ *              boundary mask of the PyPTO BSA README, section 3.2)
+ *  o           the forward output for these q, k, v, mask, lengths, causal,
+ *              scale
+ *  o_lo        NULL, or the forward's fp32 rounding residual of o (fa_fwd's
+ *              o_lo): Delta = dO . (o + o_lo), the precise dpsum of the
+ *              sparse-MLA page (order-invariance-test section)
  *  lse         fp32 [B, Hq, Sq], contiguous: the forward's LSE
  *  dout        [B, Hq, Sq, Dv], q's dtype: the gradient of the output
  *  causal      0 or 1, as fa_fwd (bottom-right aligned)
  *  scale       as fa_fwd
  *  delta       fp32 [B, Hq, Sq], contiguous, caller-owned workspace; on
- *              return it holds dO . O per row
+ *              return it holds Delta = dO . O per row (dO . (O + o_lo) with
+ *              o_lo)
  *  dq, dk, dv  outputs shaped like q, k, v in q's dtype (written, not
  *              accumulated into)
  *
@@ -198,9 +218,75 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
  * on `stream`.
  */
 fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* mask,
-                 const fa_tensor* o, const fa_tensor* lse, const fa_tensor* dout, int causal, float scale,
+                 const fa_tensor* seqlens_q, const fa_tensor* seqlens_k, const fa_tensor* o,
+                 const fa_tensor* o_lo, const fa_tensor* lse, const fa_tensor* dout, int causal, float scale,
                  const fa_tensor* delta, const fa_tensor* dq, const fa_tensor* dk,
                  const fa_tensor* dv, void* stream);
+
+/*
+ * Dense attention forward over a batch of packed variable-length sequences
+ * (the TND layout of the ops-transformer FlashAttentionScoreGrad pytest page,
+ * section 5.4, where unpad_input packs the sequences and cu_seqlens marks
+ * their bounds; the Ascend FlashAttentionScore README lists TND among the
+ * input layouts). Batch b's queries are rows cu_seqlens_q[b] ..
+ * cu_seqlens_q[b+1]-1 of q and attend to rows cu_seqlens_k[b] ..
+ * cu_seqlens_k[b+1]-1 of k and v: per sequence exactly fa_fwd on its own
+ * rows and keys (causal bottom-right aligned per sequence).
+ *
+ *  q    [Tq, Hq, D]  fp16 / bf16 (strided, last dim contiguous)
+ *  k    [Tk, Hkv, D] same dtype; Hq % Hkv == 0 (GQA as fa_fwd)
+ *  v    [Tk, Hkv, Dv] same dtype; Dv == D in {64, 128}
+ *  cu_seqlens_q, cu_seqlens_k  device int32 [B + 1], non-decreasing, first
+ *       entry 0, last entry <= Tq / Tk (unchecked: they live in device
+ *       memory)
+ *  max_seqlen_q  >= the longest query sequence; rows of a longer sequence
+ *       past it are not computed (their o and lse are left as they were)
+ *  causal, scale, rescale_threshold  as fa_fwd
+ *  o    [Tq, Hq, Dv] in q's dtype; lse fp32 [Tq, Hq], contiguous
+ *
+ * Query rows outside every sequence are not written. A sequence with no
+ * keys gives O = 0 and LSE = -inf.
+ */
+fa_status fa_fwd_varlen(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                        const fa_tensor* cu_seqlens_q, const fa_tensor* cu_seqlens_k,
+                        int max_seqlen_q, int causal, float scale, float rescale_threshold,
+                        const fa_tensor* o, const fa_tensor* lse, void* stream);
+
+/*
+ * Split-KV dense attention forward, for few query rows over many keys (the
+ * grid of fa_fwd then has too few workgroups to fill the GPU). The keys are
+ * cut into ranges; every (range, row block, head) computes the online
+ * softmax over its range alone and leaves a normalised fp32 partial output
+ * O_s and its LSE_s in `workspace`; a second kernel combines the ranges as
+ * partial softmax states (the merge of the "FlashAttention correctness
+ * verification" page, standard-vs-tiled section):
+ *   LSE = logsumexp_s LSE_s,   O = sum_s exp(LSE_s - LSE) O_s.
+ * Results equal fa_fwd's up to rounding.
+ *
+ *  q, k, v, seqlens_q, seqlens_k, causal, scale, rescale_threshold, o, lse
+ *       as fa_fwd (fp16 / bf16 only; no boolean mask)
+ *  num_splits  0 = chosen by the library (fa_fwd_splitkv_splits), else the
+ *       requested number of key ranges, <= 64; each range is a multiple of
+ *       192 keys, so fewer ranges may result
+ *  workspace   fp32, rank 1, 16-byte aligned, caller-owned, with at least
+ *       fa_fwd_splitkv_workspace_elems(...) elements; its contents on return
+ *       are unspecified. Not read when a single range results (then the call
+ *       is fa_fwd and workspace may be NULL).
+ */
+fa_status fa_fwd_splitkv(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                         const fa_tensor* seqlens_q, const fa_tensor* seqlens_k, int causal,
+                         float scale, float rescale_threshold, int num_splits,
+                         const fa_tensor* workspace, const fa_tensor* o, const fa_tensor* lse,
+                         void* stream);
+
+/* Number of key ranges fa_fwd_splitkv uses for these sizes and num_splits
+ * (-1 for negative sizes). */
+int fa_fwd_splitkv_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int num_splits);
+
+/* fp32 elements of the workspace fa_fwd_splitkv needs (0 when a single key
+ * range results; -1 for invalid sizes). */
+int64_t fa_fwd_splitkv_workspace_elems(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int64_t Dv,
+                                       int num_splits);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_str(fa_status s);

@@ -43,8 +43,9 @@ def _load():
         lib.oracle_attn_dense_bwd.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, I64,
                                               P, P, P, P, ctypes.c_int, ctypes.c_double, P, P, P,
                                               ctypes.c_int]
+        lib.oracle_attn_dense_bwd_bound.argtypes = lib.oracle_attn_dense_bwd.argtypes
         for f in (lib.oracle_attn_dense, lib.oracle_attn_blocksparse, lib.oracle_attn_topk,
-                  lib.oracle_attn_dense_bwd):
+                  lib.oracle_attn_dense_bwd, lib.oracle_attn_dense_bwd_bound):
             f.restype = ctypes.c_int
         lib.oracle_hardware_threads.restype = ctypes.c_int
         _lib = lib
@@ -209,21 +210,37 @@ def attn_topk(q, k, v, idx, *, scale, rows=None, nthreads=0):
     return o, lse
 
 
+def _bwd_call(fn, q, k, v, dout, scale, causal, mask, seqlens_q, seqlens_k, nthreads):
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Skv, Dv = v.shape
+    qa, ka, va, da = _f64(q), _f64(k), _f64(v), _f64(dout)
+    m, ms = (None, None) if mask is None else _mask_strides(mask, B, Hq, Sq, Skv)
+    sq, sk = _np(seqlens_q, np.int32), _np(seqlens_k, np.int32)
+    gq = np.zeros((B, Hq, Sq, D), dtype=np.float64)
+    gk = np.zeros((B, Hkv, Skv, D), dtype=np.float64)
+    gv = np.zeros((B, Hkv, Skv, Dv), dtype=np.float64)
+    _check(fn(_ptr(qa), _ptr(ka), _ptr(va), _ptr(da), B, Hq, Hkv, Sq, Skv, D, Dv, _ptr(m), _ptr(ms), _ptr(sq),
+              _ptr(sk), int(bool(causal)), float(scale), _ptr(gq), _ptr(gk), _ptr(gv), int(nthreads)))
+    return gq, gk, gv
+
+
+def attn_dense_bwd_bound(q, k, v, dout, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k=None,
+                         nthreads=0):
+    """First-order error scales (gq, gk, gv) of the gradients of dense
+    attention, shaped like (dq, dk, dv): every signed sum of the gradient
+    replaced by the sum of the magnitudes of its terms, plus the effect of an
+    error of at most 2 E_i in the row term Delta_i (oracle.cpp states the
+    formulas). A pipeline whose rounded quantities each carry a relative
+    error <= u is within u times these of the exact gradients (first order)."""
+    return _bwd_call(_load().oracle_attn_dense_bwd_bound, q, k, v, dout, scale, causal, mask, seqlens_q,
+                     seqlens_k, nthreads)
+
+
 def attn_dense_bwd(q, k, v, dout, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k=None,
                    nthreads=0):
     """Gradients (dq, dk, dv) of dense attention with respect to q, k, v given
     the output gradient dout [B,Hq,Sq,Dv]; same masking arguments as
     attn_dense. float64 numpy arrays shaped like q, k, v (dk, dv summed over
     the query heads of each KV head)."""
-    B, Hq, Sq, D = q.shape
-    _, Hkv, Skv, Dv = v.shape
-    qa, ka, va, da = _f64(q), _f64(k), _f64(v), _f64(dout)
-    m, ms = (None, None) if mask is None else _mask_strides(mask, B, Hq, Sq, Skv)
-    sq, sk = _np(seqlens_q, np.int32), _np(seqlens_k, np.int32)
-    dq = np.zeros((B, Hq, Sq, D), dtype=np.float64)
-    dk = np.zeros((B, Hkv, Skv, D), dtype=np.float64)
-    dv = np.zeros((B, Hkv, Skv, Dv), dtype=np.float64)
-    _check(_load().oracle_attn_dense_bwd(_ptr(qa), _ptr(ka), _ptr(va), _ptr(da), B, Hq, Hkv, Sq, Skv,
-                                         D, Dv, _ptr(m), _ptr(ms), _ptr(sq), _ptr(sk), int(bool(causal)),
-                                         float(scale), _ptr(dq), _ptr(dk), _ptr(dv), int(nthreads)))
-    return dq, dk, dv
+    return _bwd_call(_load().oracle_attn_dense_bwd, q, k, v, dout, scale, causal, mask, seqlens_q, seqlens_k,
+                     nthreads)

@@ -248,6 +248,104 @@ int oracle_attn_dense_bwd(const double* q, const double* k, const double* v, con
   });
 }
 
+// First-order error scales of the gradients above, for per-element
+// tolerances: the same key sets and the same P and dS, but every signed sum
+// replaced by the sum of the magnitudes of its terms, plus the effect of an
+// error in Delta_i = sum_j P_ij dP_ij of at most 2 E_i with
+// E_i = sum_d |dO_id| sum_j P_ij |v_jd| (a gradient pipeline that forms
+// Delta from a computed O whose error is bounded by the magnitudes of the
+// terms of P V):
+//
+//   gv_j = sum_i P_ij |dO_i|
+//   gk_j = scale sum_i (|dS_ij| + 2 P_ij E_i) |q_i|
+//   gq_i = scale sum_j (|dS_ij| + 2 P_ij E_i) |k_j|
+//
+// (elementwise over d). If each rounded quantity carries a relative error of
+// at most u, the error of dV, dK, dQ is at most u times these (to first
+// order). Same argument conventions as oracle_attn_dense_bwd; outputs
+// gq, gk, gv shaped like dq, dk, dv.
+int oracle_attn_dense_bwd_bound(const double* q, const double* k, const double* v, const double* dout,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                                int64_t Dv, const uint8_t* mask, const int64_t* ms,
+                                const int32_t* seqlens_q, const int32_t* seqlens_k, int causal,
+                                double scale, double* gq, double* gk, double* gv, int nthreads) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || D <= 0 || Dv <= 0) return ORACLE_ERR_ARG;
+  if (Hq % Hkv != 0) return ORACLE_ERR_ARG;
+  if (B * Hq * Sq > 0 && (!q || !dout || !gq)) return ORACLE_ERR_ARG;
+  if (B * Hkv * Skv > 0 && (!k || !v || !gk || !gv)) return ORACLE_ERR_ARG;
+  if (mask && !ms) return ORACLE_ERR_ARG;
+  const int64_t G = Hq / Hkv;
+  return parallel_rows(B * Hkv, nthreads, [&](int64_t bk) -> int {
+    const int64_t b = bk / Hkv, hkv = bk % Hkv;
+    const double* kb = k + bk * Skv * D;
+    const double* vb = v + bk * Skv * Dv;
+    double* gkb = gk + bk * Skv * D;
+    double* gvb = gv + bk * Skv * Dv;
+    for (int64_t x = 0; x < Skv * D; ++x) gkb[x] = 0.0;
+    for (int64_t x = 0; x < Skv * Dv; ++x) gvb[x] = 0.0;
+    const int64_t Lq = seqlens_q ? seqlens_q[b] : Sq;
+    const int64_t Lk = seqlens_k ? seqlens_k[b] : Skv;
+    std::vector<int64_t> keys;
+    std::vector<double> s, p, dp, pv(Dv);
+    for (int64_t hq = hkv * G; hq < (hkv + 1) * G; ++hq) {
+      for (int64_t i = 0; i < Sq; ++i) {
+        const int64_t row = (b * Hq + hq) * Sq + i;
+        const double* qi = q + row * D;
+        const double* doi = dout + row * Dv;
+        double* gqi = gq + row * D;
+        for (int64_t d = 0; d < D; ++d) gqi[d] = 0.0;
+        keys.clear();
+        if (i < Lq) {
+          for (int64_t j = 0; j < std::min(Lk, Skv); ++j) {
+            if (causal && j > i + (Lk - Lq)) continue;
+            if (mask && mask[b * ms[0] + hq * ms[1] + i * ms[2] + j * ms[3]] != 0) continue;
+            keys.push_back(j);
+          }
+        }
+        if (keys.empty()) continue;
+        const size_t n = keys.size();
+        s.assign(n, 0.0);
+        p.assign(n, 0.0);
+        dp.assign(n, 0.0);
+        double m = -std::numeric_limits<double>::infinity();
+        for (size_t t = 0; t < n; ++t) {
+          const double* kj = kb + keys[t] * D;
+          double dot = 0.0;
+          for (int64_t d = 0; d < D; ++d) dot += qi[d] * kj[d];
+          s[t] = scale * dot;
+          m = std::max(m, s[t]);
+        }
+        double l = 0.0;
+        for (size_t t = 0; t < n; ++t) l += std::exp(s[t] - m);
+        double delta = 0.0;
+        for (int64_t d = 0; d < Dv; ++d) pv[d] = 0.0;
+        for (size_t t = 0; t < n; ++t) {
+          p[t] = std::exp(s[t] - m) / l;
+          const double* vj = vb + keys[t] * Dv;
+          double dot = 0.0;
+          for (int64_t d = 0; d < Dv; ++d) {
+            dot += doi[d] * vj[d];
+            pv[d] += p[t] * std::fabs(vj[d]);
+          }
+          dp[t] = dot;
+          delta += p[t] * dot;
+        }
+        double e = 0.0;  // E_i
+        for (int64_t d = 0; d < Dv; ++d) e += std::fabs(doi[d]) * pv[d];
+        for (size_t t = 0; t < n; ++t) {
+          const int64_t j = keys[t];
+          const double w = std::fabs(p[t] * (dp[t] - delta)) + 2.0 * p[t] * e;
+          const double* kj = kb + j * D;
+          for (int64_t d = 0; d < D; ++d) gqi[d] += scale * w * std::fabs(kj[d]);
+          for (int64_t d = 0; d < D; ++d) gkb[j * D + d] += scale * w * std::fabs(qi[d]);
+          for (int64_t d = 0; d < Dv; ++d) gvb[j * Dv + d] += p[t] * std::fabs(doi[d]);
+        }
+      }
+    }
+    return ORACLE_OK;
+  });
+}
+
 // Block-sparse attention: row i of query block qb = i / block_q attends to the
 // union of the KV blocks [block_k * idx, block_k * idx + block_k) listed in its
 // block list, cut at the batch's sequence length.

@@ -23,6 +23,11 @@ Named workloads (sizes as the pages' configurations give them):
                        64 rope), Dv=512, one shared KV head, V = K[:, :512],
                        self key + min(W-1, t) earlier keys per token
   causal_bf16_s8192    bf16 BNSD, B=2, H=16, S=8192, D=128, causal
+  splitkv_bf16_q512_k65536  bf16 BNSD, B=1, Hq=32, Hkv=8, Sq=512, Skv=65536,
+                       D=128, causal bottom-right (the last 512 rows of a
+                       65536-token context: few query rows over many keys)
+  varlen_bf16_b16      bf16 packed TND, 16 sequences with lengths drawn
+                       uniformly from [64, 8192], Hq=32, Hkv=8, D=128, causal
 """
 import concurrent.futures
 import math
@@ -180,7 +185,33 @@ def workload(name: str) -> dict:
         return blocksparse(4, 2, 16, 4, 8192, 128, [8192, 5000])
     if name == "topk_mla_bf16_t4096":
         return topk_mla(5, 4096, 4096, 2048, 128, 576, 512)
+    if name == "splitkv_bf16_q512_k65536":
+        g, q, k, v = dense_inputs(7, 1, 32, 8, 512, 65536, 128, 128, "bf16")
+        return dict(kind="dense", q=q, k=k, v=v, scale=1.0 / math.sqrt(128), causal=True, split=True)
+    if name == "varlen_bf16_b16":
+        return varlen(8, 16, 64, 8192, 32, 8, 128)
     raise KeyError(name)
+
+
+def varlen(seed, B, lmin, lmax, Hq, Hkv, D, dtype="bf16", causal=True, lens_q=None, lens_k=None):
+    """Packed (TND) variable-length batch: sequence lengths drawn uniformly
+    from [lmin, lmax] unless lens_q is given (self-attention: keys of the same
+    lengths unless lens_k is given); q [Tq, Hq, D], k/v [Tk, Hkv, D],
+    cu_seqlens int32 [B+1]."""
+    g = rng(seed)
+    lens = g.integers(lmin, lmax + 1, size=B).astype(np.int64)
+    if lens_q is not None:
+        lens = np.asarray(lens_q, dtype=np.int64)
+    lk = lens if lens_k is None else np.asarray(lens_k, dtype=np.int64)
+    dt = DTYPES[dtype]
+    Tq, Tk = int(lens.sum()), int(lk.sum())
+    q = cast(normal(g, (Tq, Hq, D)), dt)
+    k = cast(normal(g, (Tk, Hkv, D)), dt)
+    v = cast(normal(g, (Tk, Hkv, D)), dt)
+    cu_q = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+    cu_k = torch.from_numpy(np.concatenate([[0], np.cumsum(lk)]).astype(np.int32))
+    return dict(kind="varlen", q=q, k=k, v=v, cu_q=cu_q, cu_k=cu_k, max_q=int(lens.max()),
+                scale=1.0 / math.sqrt(D), causal=causal)
 
 
 def gqa_mask(seed, B, Hq, Hkv, S, D, density=0.05, frac=0.01, factor=30.0, dtype="f16"):

@@ -45,9 +45,9 @@ def name(lib, s):
     return lib.fa_status_str(s).decode()
 
 
-def call_fwd(lib, q, k, v, o, lse, mask=None, sq=None, sk=None, causal=0, scale=0.1, thr=8.0):
-    return name(lib, lib.fa_fwd(R(q), R(k), R(v), R(mask), R(sq), R(sk), causal, scale, thr, R(o), R(lse),
-                                None))
+def call_fwd(lib, q, k, v, o, lse, mask=None, sq=None, sk=None, causal=0, scale=0.1, thr=0.0, o_lo=None):
+    return name(lib, lib.fa_fwd(R(q), R(k), R(v), R(mask), R(sq), R(sk), causal, scale, thr, R(o), R(o_lo),
+                                R(lse), None))
 
 
 def good(B=2, Hq=4, Hkv=2, S=64, D=128, dt=fa.FA_BF16):
@@ -57,11 +57,12 @@ def good(B=2, Hq=4, Hkv=2, S=64, D=128, dt=fa.FA_BF16):
 
 def test_exports_every_declared_function(lib):
     names = fa.declared_functions()
-    assert {"fa_fwd", "fa_fwd_blocksparse", "fa_fwd_topk_gather", "fa_bwd", "fa_status_str",
-            "fa_last_error", "fa_version"} <= set(names)
+    assert {"fa_fwd", "fa_fwd_blocksparse", "fa_fwd_topk_gather", "fa_bwd", "fa_fwd_varlen", "fa_fwd_splitkv",
+            "fa_fwd_splitkv_splits", "fa_fwd_splitkv_workspace_elems", "fa_status_str", "fa_last_error",
+            "fa_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.fa_version() == 200
+    assert lib.fa_version() == 300
 
 
 def test_status_names(lib):
@@ -99,6 +100,12 @@ def test_fa_fwd_validation(lib):
     assert call_fwd(lib, q, k, v, o, lse, mask=T([3, 1, 64, 64], fa.FA_U8)) == "FA_ERR_SHAPE"
     assert call_fwd(lib, q, k, v, o, lse, sq=T([2], fa.FA_F32)) == "FA_ERR_DTYPE"
     assert call_fwd(lib, q, k, v, o, lse, sk=T([3], fa.FA_I32)) == "FA_ERR_SHAPE"
+    # o_lo: fp32, shaped like o, 16-bit outputs only
+    assert call_fwd(lib, q, k, v, o, lse, o_lo=T([2, 4, 64, 128], fa.FA_BF16)) == "FA_ERR_DTYPE"
+    assert call_fwd(lib, q, k, v, o, lse, o_lo=T([2, 4, 64, 64], fa.FA_F32)) == "FA_ERR_SHAPE"
+    assert call_fwd(lib, q, k, v, o, lse, o_lo=T([2, 4, 64, 128], fa.FA_F32, data=FAKE + 4)) == "FA_ERR_STRIDE"
+    q32, k32, v32, o32, l32 = good(dt=fa.FA_F32)
+    assert call_fwd(lib, q32, k32, v32, o32, l32, o_lo=T([2, 4, 64, 128], fa.FA_F32)) == "FA_ERR_UNSUPPORTED"
 
 
 def test_empty_problems_launch_nothing(lib):
@@ -132,16 +139,17 @@ def test_blocksparse_validation(lib):
 
 def test_topk_validation(lib):
     def tk(q=T([8, 128, 576]), k=T([16, 576]), v=None, idx=T([8, 32], fa.FA_I32),
-           o=T([8, 128, 512]), lse=T([8, 128], fa.FA_F32), scale=0.04):
+           o=T([8, 128, 512]), lse=T([8, 128], fa.FA_F32), scale=0.04, o_lo=None):
         if v is None:
             v = T([16, 512], stride=[576, 1])
-        return name(lib, lib.fa_fwd_topk_gather(R(q), R(k), R(v), R(idx), scale, R(o), R(lse), None))
+        return name(lib, lib.fa_fwd_topk_gather(R(q), R(k), R(v), R(idx), scale, R(o), R(o_lo), R(lse), None))
 
     assert tk(q=T([8, 128, 576], fa.FA_F32), k=T([16, 576], fa.FA_F32), v=T([16, 512], fa.FA_F32),
               o=T([8, 128, 512], fa.FA_F32)) == "FA_ERR_DTYPE"
     assert tk(idx=T([8, 32], fa.FA_U8)) == "FA_ERR_DTYPE"
     assert tk(q=T([8, 128, 512]), k=T([16, 512])) == "FA_ERR_UNSUPPORTED"
-    assert tk(q=T([8, 100, 576]), o=T([8, 100, 512]), lse=T([8, 100], fa.FA_F32)) == "FA_ERR_UNSUPPORTED"
+    assert tk(o_lo=T([8, 128, 512], fa.FA_F16)) == "FA_ERR_DTYPE"
+    assert tk(o_lo=T([8, 100, 512], fa.FA_F32)) == "FA_ERR_SHAPE"
     assert tk(idx=T([8, 5000], fa.FA_I32)) == "FA_ERR_UNSUPPORTED"
     assert tk(idx=T([7, 32], fa.FA_I32)) == "FA_ERR_SHAPE"
     assert tk(v=T([15, 512])) == "FA_ERR_SHAPE"
@@ -151,14 +159,15 @@ def test_topk_validation(lib):
 
 
 def test_bwd_validation(lib):
-    def bw(dt=fa.FA_BF16, D=128, dq_shape=None, delta_dt=fa.FA_F32, B=2, causal=1, mask=None):
+    def bw(dt=fa.FA_BF16, D=128, dq_shape=None, delta_dt=fa.FA_F32, B=2, causal=1, mask=None, sq=None, sk=None,
+           o_lo=None):
         q, k, v, o, lse = good(B=B, D=D, dt=dt)
         dout = T([B, 4, 64, D], dt)
         dq = T(dq_shape or [B, 4, 64, D], dt)
         dk, dv = T([B, 2, 64, D], dt), T([B, 2, 64, D], dt)
         delta = T([B, 4, 64], delta_dt)
-        return name(lib, lib.fa_bwd(R(q), R(k), R(v), R(mask), R(o), R(lse), R(dout), causal, 0.1,
-                                    R(delta), R(dq), R(dk), R(dv), None))
+        return name(lib, lib.fa_bwd(R(q), R(k), R(v), R(mask), R(sq), R(sk), R(o), R(o_lo), R(lse), R(dout), causal,
+                                    0.1, R(delta), R(dq), R(dk), R(dv), None))
 
     assert bw(dt=fa.FA_F32) == "FA_ERR_UNSUPPORTED"
     assert bw(D=64) == "FA_ERR_UNSUPPORTED"
@@ -168,7 +177,60 @@ def test_bwd_validation(lib):
     assert bw(mask=T([64, 63], fa.FA_U8)) == "FA_ERR_SHAPE"
     assert bw(mask=T([3, 4, 64, 64], fa.FA_U8)) == "FA_ERR_SHAPE"
     assert bw(mask=T([64, 64], fa.FA_BF16)) == "FA_ERR_DTYPE"
+    assert bw(sq=T([3], fa.FA_I32)) == "FA_ERR_SHAPE"
+    assert bw(sk=T([2], fa.FA_F32)) == "FA_ERR_DTYPE"
+    assert bw(o_lo=T([2, 4, 64, 128], fa.FA_BF16)) == "FA_ERR_DTYPE"
+    assert bw(o_lo=T([2, 4, 63, 128], fa.FA_F32)) == "FA_ERR_SHAPE"
     assert bw(B=0) == "FA_OK"  # nothing to do: no launch
+
+
+def test_varlen_validation(lib):
+    def vl(q=T([100, 4, 128]), k=T([120, 2, 128]), v=T([120, 2, 128]), cq=T([4], fa.FA_I32), ck=T([4], fa.FA_I32),
+           maxq=50, o=T([100, 4, 128]), lse=T([100, 4], fa.FA_F32), causal=1, thr=0.0):
+        return name(lib, lib.fa_fwd_varlen(R(q), R(k), R(v), R(cq), R(ck), maxq, causal, 0.1, thr, R(o), R(lse), None))
+
+    assert vl(q=T([100, 4, 128], fa.FA_F32), k=T([120, 2, 128], fa.FA_F32), v=T([120, 2, 128], fa.FA_F32),
+              o=T([100, 4, 128], fa.FA_F32)) == "FA_ERR_DTYPE"
+    assert vl(cq=T([4], fa.FA_I32), ck=T([5], fa.FA_I32)) == "FA_ERR_SHAPE"
+    assert vl(cq=T([0], fa.FA_I32), ck=T([0], fa.FA_I32)) == "FA_ERR_SHAPE"
+    assert vl(cq=T([4], fa.FA_F32)) == "FA_ERR_DTYPE"
+    assert vl(k=T([120, 3, 128]), v=T([120, 3, 128])) == "FA_ERR_SHAPE"
+    assert vl(v=T([119, 2, 128])) == "FA_ERR_SHAPE"
+    assert vl(lse=T([100, 3], fa.FA_F32)) == "FA_ERR_SHAPE"
+    assert vl(maxq=-1) == "FA_ERR_VALUE"
+    assert vl(causal=3) == "FA_ERR_VALUE"
+    assert vl(thr=11.0) == "FA_ERR_VALUE"
+    assert vl(q=T([100, 4, 96]), k=T([120, 2, 96]), v=T([120, 2, 96]), o=T([100, 4, 96])) == "FA_ERR_UNSUPPORTED"
+    assert vl(maxq=0) == "FA_OK"  # no rows: nothing launched
+    assert vl(cq=T([1], fa.FA_I32), ck=T([1], fa.FA_I32)) == "FA_OK"  # B = 0
+
+
+def test_splitkv_sizing_and_validation(lib):
+    # sizing: ranges are multiples of 192 keys; the default fills the GPU
+    assert lib.fa_fwd_splitkv_splits(1, 1, 100, 1000, 8) == 6   # 125 -> 192 keys per range
+    assert lib.fa_fwd_splitkv_splits(1, 1, 100, 100, 8) == 1
+    assert lib.fa_fwd_splitkv_splits(2, 16, 4096, 4096, 0) == 1  # already >= 512 workgroups
+    assert lib.fa_fwd_splitkv_splits(1, 32, 512, 65536, 0) == 8
+    assert lib.fa_fwd_splitkv_splits(1, 1, 1, 1 << 20, 0) == 64
+    assert lib.fa_fwd_splitkv_splits(1, 1, 1, 1000, 0) == 2     # at least 384 keys per range
+    assert lib.fa_fwd_splitkv_splits(-1, 1, 1, 1, 0) == -1
+    assert lib.fa_fwd_splitkv_workspace_elems(1, 32, 512, 65536, 128, 0) == 8 * 32 * 512 * 129
+    assert lib.fa_fwd_splitkv_workspace_elems(1, 1, 100, 100, 128, 0) == 0
+    q, k, v, o, lse = good(S=2000)
+
+    def sk(ns=4, ws=T([4 * 2 * 4 * 2000 * 129], fa.FA_F32), q=q, k=k, v=v, o=o, causal=0):
+        return name(lib, lib.fa_fwd_splitkv(R(q), R(k), R(v), None, None, causal, 0.1, 0.0, ns, R(ws), R(o), R(lse),
+                                            None))
+
+    assert sk(ns=65) == "FA_ERR_VALUE"
+    assert sk(ns=-1) == "FA_ERR_VALUE"
+    assert sk(ws=T([1000], fa.FA_F32)) == "FA_ERR_SHAPE"
+    assert b"workspace holds" in lib.fa_last_error()
+    assert sk(ws=T([4 * 2 * 4 * 2000 * 129], fa.FA_BF16)) == "FA_ERR_DTYPE"
+    assert sk(ws=None) == "FA_ERR_NULL"
+    q32, k32, v32, o32, l32 = good(S=2000, dt=fa.FA_F32)
+    assert sk(q=q32, k=k32, v=v32, o=o32) == "FA_ERR_UNSUPPORTED"
+    assert sk(causal=2) == "FA_ERR_VALUE"
 
 
 def test_binding_refuses_cpu_tensors(lib):

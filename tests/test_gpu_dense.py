@@ -9,12 +9,13 @@ import torch
 import flashattention_online_softmax_amd as fa
 import oracle
 import synth
-from fa_testutil import absv, check, f32, gpu, sample_rows
+from fa_testutil import absv, check, f32, gpu, log, sample_rows
+from oracle import metrics
 
 pytestmark = pytest.mark.gpu
 
 
-def run_dense(case, q, k, v, scale, causal=False, mask=None, sq=None, sk=None, thr=8.0):
+def run_dense(case, q, k, v, scale, causal=False, mask=None, sq=None, sk=None, thr=0.0):
     o, lse = fa.fa_fwd(*gpu(q, k, v), scale=scale, causal=causal, mask=gpu(mask),
                        seqlens_q=gpu(sq), seqlens_k=gpu(sk), rescale_threshold=thr)
     torch.cuda.synchronize()
@@ -179,6 +180,16 @@ def test_single_key_and_single_row():
     assert torch.equal(o.cpu()[0, 0, 0], v[0, 0, 0])  # first causal row sees key 0 only
 
 
+def test_default_is_exact_running_max():
+    # The binding's default rescale threshold is 0: the exact running max.
+    _, q, k, v = synth.dense_inputs(18, 1, 2, 2, 300, 300, 128, 128, "bf16")
+    qq, kk, vv = gpu(q, k, v)
+    a, la = fa.fa_fwd(qq, kk, vv, scale=0.1, causal=True)
+    b, lb = fa.fa_fwd(qq, kk, vv, scale=0.1, causal=True, rescale_threshold=0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
 def test_empty_problems():
     _, q, k, v = synth.dense_inputs(16, 1, 2, 2, 8, 8, 64, 64, "bf16")
     qq, kk, vv = gpu(q, k, v)
@@ -193,15 +204,16 @@ def test_empty_problems():
 
 # ---------------------------------------------------------------------------
 # Full-size workloads, checked on sampled rows computed one by one by the
-# oracle, in the launch configuration the benchmark times.
+# oracle, in the launch configuration the benchmark times: the exact running
+# max (rescale threshold 0, the contract path) and the lazy rescale
+# (threshold 8) on the same inputs.
 # ---------------------------------------------------------------------------
 
-def _full_dense(name, n_rows, must_rows=()):
+def _full_dense(name, n_rows, must_rows=(), plain_cap=None):
     w = synth.workload(name)
     q, k, v = w["q"], w["k"], w["v"]
     mask = w.get("mask")
-    o, lse = fa.fa_fwd(*gpu(q, k, v), scale=w["scale"], causal=w["causal"], mask=gpu(mask))
-    torch.cuda.synchronize()
+    qg, kg, vg, mg = gpu(q, k, v, mask)
     B, Hq, Sq, D = q.shape
     g = np.random.default_rng(1234)
     must = list(must_rows)
@@ -211,28 +223,95 @@ def _full_dense(name, n_rows, must_rows=()):
     kw = dict(scale=f32(w["scale"]), causal=w["causal"], mask=mask, rows=rows)
     o_ref, lse_ref = oracle.attn_dense(q, k, v, **kw)
     o_abs, _ = oracle.attn_dense(q, k, v.abs(), **kw)
-    o_s = o.reshape(-1, D)[torch.from_numpy(rows).cuda()]
-    l_s = lse.reshape(-1)[torch.from_numpy(rows).cuda()]
-    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
-    return check("full_" + name, o_s, l_s, o_ref, lse_ref, q.dtype, o_abs, {"sampled_rows": len(rows)})
+    idx = torch.from_numpy(rows).cuda()
+    reps = {}
+    for thr in (0.0, 8.0):
+        o, lse = fa.fa_fwd(qg, kg, vg, scale=w["scale"], causal=w["causal"], mask=mg, rescale_threshold=thr)
+        torch.cuda.synchronize()
+        assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+        assert torch.all(torch.isfinite(lse))  # every row of these workloads has a key
+        reps[thr] = check("full_%s_thr%g" % (name, thr), o.reshape(-1, D)[idx], lse.reshape(-1)[idx], o_ref,
+                          lse_ref, q.dtype, o_abs, {"sampled_rows": len(rows), "rescale_threshold": thr},
+                          plain_cap=plain_cap)
+        del o, lse
+    return reps
 
 
 def test_full_dense_f32_s128():
     w = synth.workload("dense_f32_s128")
-    o, lse = fa.fa_fwd(*gpu(w["q"], w["k"], w["v"]), scale=w["scale"])
-    torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attn_dense(w["q"], w["k"], w["v"], scale=f32(w["scale"]))
     o_abs, _ = oracle.attn_dense(w["q"], w["k"], w["v"].abs(), scale=f32(w["scale"]))
-    check("full_dense_f32_s128", o, lse, o_ref, lse_ref, torch.float32, o_abs)
+    for thr in (0.0, 8.0):
+        o, lse = fa.fa_fwd(*gpu(w["q"], w["k"], w["v"]), scale=w["scale"], rescale_threshold=thr)
+        torch.cuda.synchronize()
+        check("full_dense_f32_s128_thr%g" % thr, o, lse, o_ref, lse_ref, torch.float32, o_abs)
 
 
 def test_full_causal_bf16_s4096():
-    _full_dense("causal_bf16_s4096", 384)
+    _full_dense("causal_bf16_s4096", 384, plain_cap=0.02)
 
 
 def test_full_causal_bf16_s8192():
-    _full_dense("causal_bf16_s8192", 256)
+    _full_dense("causal_bf16_s8192", 256, plain_cap=0.02)
 
 
 def test_full_gqa_mask_f16_s8192():
-    _full_dense("gqa_mask_f16_s8192", 256)
+    # fp16 at full size: the literal atol/rtol gate on every sampled element
+    _full_dense("gqa_mask_f16_s8192", 256, plain_cap=0.0)
+
+
+# ---------------------------------------------------------------------------
+# The o_lo output: fp32(O) - rounded(O), the output's rounding residual.
+# ---------------------------------------------------------------------------
+
+def check_o_lo(case, o, lo, o_ref, o_abs, dtype, n_keys):
+    """o + o_lo is the unrounded fp32 result: rounding it reproduces o bit for
+    bit, |o_lo| is at most half an ulp of o, and it lies within the error of
+    rounding P alone (no output-rounding term: u_P sum_j P_j |v_j| plus fp32
+    accumulation) of the oracle, which o itself does not."""
+    x = o.float() + lo
+    assert torch.equal(x.to(o.dtype), o), case
+    # half an ulp: relative 2^-8 (bf16) / 2^-11 (fp16), absolute 2^-25 for
+    # fp16's subnormal range
+    u_out = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -11
+    sub = 0.0 if dtype == torch.bfloat16 else 2.0 ** -25
+    assert torch.all(lo.abs() <= u_out * (1 + 2 * u_out) * o.float().abs() + sub), case
+    xn = x.cpu().numpy().astype(np.float64)
+    on = o.float().cpu().numpy().astype(np.float64)
+    o_ref = np.asarray(o_ref).reshape(xn.shape)
+    o_abs = np.asarray(o_abs).reshape(xn.shape)
+    u_p = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -11
+    gate = (u_p + n_keys * 2.0 ** -24 + 1e-4) * o_abs + 1e-6
+    err_x = np.abs(xn - o_ref)
+    rx, ro = metrics.rel_l2(xn, o_ref), metrics.rel_l2(on, o_ref)
+    log(case, {"rel_l2_o": ro, "rel_l2_o_plus_o_lo": rx, "worst_ratio": float((err_x / gate).max())})
+    assert np.all(err_x <= gate), case
+    assert rx < ro, case
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_o_lo_dense(dtype, causal):
+    _, q, k, v = synth.dense_inputs(500 + causal, 2, 4, 2, 300, 300, 128, 128, dtype)
+    o, lse, lo = fa.fa_fwd(*gpu(q, k, v), scale=0.088, causal=causal, return_o_lo=True)
+    a, la = fa.fa_fwd(*gpu(q, k, v), scale=0.088, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o, a) and torch.equal(lse, la)  # o_lo changes nothing else
+    o_ref, _ = oracle.attn_dense(q, k, v, scale=f32(0.088), causal=causal)
+    o_abs, _ = oracle.attn_dense(q, k, v.abs(), scale=f32(0.088), causal=causal)
+    check_o_lo("o_lo_%s_causal%d" % (dtype, causal), o, lo, o_ref, o_abs, q.dtype, 300)
+
+
+def test_o_lo_full_causal_bf16_s4096():
+    w = synth.workload("causal_bf16_s4096")
+    q, k, v = w["q"], w["k"], w["v"]
+    o, lse, lo = fa.fa_fwd(*gpu(q, k, v), scale=w["scale"], causal=True, return_o_lo=True)
+    torch.cuda.synchronize()
+    B, Hq, Sq, D = q.shape
+    rows = sample_rows(np.random.default_rng(4321), B * Hq * Sq, 256, [0, Sq - 1])
+    kw = dict(scale=f32(w["scale"]), causal=True, rows=rows)
+    o_ref, _ = oracle.attn_dense(q, k, v, **kw)
+    o_abs, _ = oracle.attn_dense(q, k, v.abs(), **kw)
+    idx = torch.from_numpy(rows).cuda()
+    check_o_lo("o_lo_full_causal_bf16_s4096", o.reshape(-1, D)[idx], lo.reshape(-1, D)[idx], o_ref, o_abs,
+               q.dtype, Sq)

@@ -62,11 +62,12 @@ def test_blocksparse_per_head_lists_d64():
 
 
 def test_full_blocksparse_f16_s8192():
+    # Exact running max (the contract path) and lazy rescale on the same
+    # inputs; fp16 at full size: the literal atol/rtol gate on every sampled
+    # element.
     w = synth.workload("blocksparse_f16_s8192")
     q, k, v = w["q"], w["k"], w["v"]
-    o, lse = fa.fa_fwd_blocksparse(*gpu(q, k, v), gpu(w["block_idx"]), scale=w["scale"],
-                                   seqlens=gpu(w["seqlens"]))
-    torch.cuda.synchronize()
+    qg, kg, vg, bi, sl = gpu(q, k, v, w["block_idx"], w["seqlens"])
     B, Hq, S, D = q.shape
     g = np.random.default_rng(77)
     must = [0, S - 1, S + 4999, S + 5000, 2 * S - 1, (2 * Hq - 1) * S + 4990]  # around seqlen 5000
@@ -75,11 +76,15 @@ def test_full_blocksparse_f16_s8192():
     o_ref, lse_ref = oracle.attn_blocksparse(q, k, v, w["block_idx"], **kw)
     o_abs, _ = oracle.attn_blocksparse(q, k, v.abs(), w["block_idx"], **kw)
     idx = torch.from_numpy(rows).cuda()
-    check("full_blocksparse_f16_s8192", o.reshape(-1, D)[idx], lse.reshape(-1)[idx], o_ref, lse_ref,
-          torch.float16, o_abs, {"sampled_rows": len(rows)})
-    # padded rows of batch 1 (i >= 5000) are exactly zero / -inf everywhere
-    assert torch.all(o[1, :, 5000:] == 0) and torch.all(torch.isneginf(lse[1, :, 5000:]))
-    assert torch.all(torch.isfinite(lse[0])) and torch.all(torch.isfinite(lse[1, :, :5000]))
+    for thr in (0.0, 8.0):
+        o, lse = fa.fa_fwd_blocksparse(qg, kg, vg, bi, scale=w["scale"], seqlens=sl, rescale_threshold=thr)
+        torch.cuda.synchronize()
+        check("full_blocksparse_f16_s8192_thr%g" % thr, o.reshape(-1, D)[idx], lse.reshape(-1)[idx], o_ref,
+              lse_ref, torch.float16, o_abs, {"sampled_rows": len(rows), "rescale_threshold": thr}, plain_cap=0.0)
+        # padded rows of batch 1 (i >= 5000) are exactly zero / -inf everywhere
+        assert torch.all(o[1, :, 5000:] == 0) and torch.all(torch.isneginf(lse[1, :, 5000:]))
+        assert torch.all(torch.isfinite(lse[0])) and torch.all(torch.isfinite(lse[1, :, :5000]))
+        assert not torch.isnan(o).any()
 
 
 # ---------------------------------------------------------------- top-k MLA
@@ -119,13 +124,14 @@ def test_topk_prefix_lists_equal_causal_dense():
     check("topk_prefix_causal", o, lse, o_ref, lse_ref, torch.bfloat16, o_abs)
 
 
-def _order_gates(name, w, rows, rep_extra=None):
+def _order_gates(name, w, rows, rep_extra=None, plain_cap=None):
     """Both index orders against the oracle, row gain <= 2F each, and the
     coherent part of their difference <= 2F (exact running max)."""
     outs = {}
     for order in ("idx_a", "idx_b"):
         o, lse, o_ref, lse_ref, o_abs = run_topk(name, w["q"], w["kv"], w[order], w["scale"], rows=rows)
-        rep = check("%s_%s" % (name, order), o, lse, o_ref, lse_ref, torch.bfloat16, o_abs, rep_extra)
+        rep = check("%s_%s" % (name, order), o, lse, o_ref, lse_ref, torch.bfloat16, o_abs, rep_extra,
+                    plain_cap=plain_cap)
         outs[order] = o.float().cpu().numpy().astype(np.float64)
     F = metrics.bf16_floor(o_ref)
     ga = metrics.rms(metrics.row_gain(outs["idx_a"], o_ref))
@@ -147,4 +153,34 @@ def test_full_topk_mla_bf16_t4096():
     T, Hq = w["q"].shape[:2]
     toks = np.sort(g.choice(T, size=24, replace=False))
     rows = (toks[:, None] * Hq + np.arange(Hq)[None, :]).reshape(-1)
-    _order_gates("full_topk_mla_bf16_t4096", w, rows, {"sampled_tokens": len(toks)})
+    _order_gates("full_topk_mla_bf16_t4096", w, rows, {"sampled_tokens": len(toks)}, plain_cap=0.006)
+
+
+@pytest.mark.parametrize("hq", [16, 40])
+def test_topk_query_heads_not_a_multiple_of_32(hq):
+    # Query heads padded to the wave's 32: the padding heads compute on a real
+    # head and store nothing; heads past Hq are never written.
+    w = synth.topk_mla(53, 64, 200, 96, hq, 576, 512)
+    qg, kg, ig = gpu(w["q"], w["kv"], w["idx_a"])
+    full = torch.full((64, hq + 8, 512), 7.0, dtype=torch.bfloat16, device="cuda")
+    o = full[:, :hq]
+    lse = torch.empty((64, hq), dtype=torch.float32, device="cuda")
+    fa.fa_fwd_topk_gather(qg, kg, kg[:, :512], ig, scale=w["scale"], out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(full[:, hq:] == 7.0)
+    o_ref, lse_ref = oracle.attn_topk(w["q"], w["kv"], w["kv"][:, :512], w["idx_a"], scale=f32(w["scale"]))
+    o_abs, _ = oracle.attn_topk(w["q"], w["kv"], w["kv"][:, :512].abs(), w["idx_a"], scale=f32(w["scale"]))
+    check("topk_hq%d" % hq, o, lse, o_ref, lse_ref, torch.bfloat16, o_abs)
+
+
+def test_topk_o_lo():
+    from test_gpu_dense import check_o_lo
+    w = synth.topk_mla(54, 96, 300, 128, 64, 576, 512)
+    qg, kg, ig = gpu(w["q"], w["kv"], w["idx_b"])
+    o, lse, lo = fa.fa_fwd_topk_gather(qg, kg, kg[:, :512], ig, scale=w["scale"], return_o_lo=True)
+    a, la = fa.fa_fwd_topk_gather(qg, kg, kg[:, :512], ig, scale=w["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, a) and torch.equal(lse, la)
+    o_ref, _ = oracle.attn_topk(w["q"], w["kv"], w["kv"][:, :512], w["idx_b"], scale=f32(w["scale"]))
+    o_abs, _ = oracle.attn_topk(w["q"], w["kv"], w["kv"][:, :512].abs(), w["idx_b"], scale=f32(w["scale"]))
+    check_o_lo("topk_o_lo", o, lo, o_ref, o_abs, torch.bfloat16, 128)

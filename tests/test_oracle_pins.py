@@ -454,6 +454,43 @@ def test_metrics_detect_planted_errors():
     assert metrics.lse_report(np.array([0.0, 0.0, 1.0]), l)["neginf_mismatch"] == 1
 
 
+def test_check_result_thresholds_of_the_pytest_page():
+    """The FlashAttentionScoreGrad pytest page's comparison (section 7): an
+    element violates when |a - b| > max(max(|a|, |b|) * 0.005, 2.5e-5); a case
+    fails when more than 0.5% of the elements violate or the largest
+    difference exceeds 0.1. Planted errors on both sides of every threshold."""
+    one = np.array([1.0])
+    # relative threshold of one element: 0.005 * max(|a|, |b|)
+    assert metrics.check_result(one + 0.0049, one)["violator_ratio"] == 0.0
+    assert metrics.check_result(one + 0.0052, one)["violator_ratio"] == 1.0
+    # the threshold uses the larger magnitude of the two sides (symmetric)
+    assert metrics.check_result(one, one + 0.0049)["violator_ratio"] == 0.0
+    assert metrics.check_result(-one - 0.0052, -one)["violator_ratio"] == 1.0
+    # absolute floor 2.5e-5 near zero
+    zero = np.array([0.0])
+    assert metrics.check_result(zero + 2.4e-5, zero)["violator_ratio"] == 0.0
+    assert metrics.check_result(zero + 2.6e-5, zero)["violator_ratio"] == 1.0
+    # violator ratio 0.005 passes, 0.006 fails (1000 elements)
+    ref = np.ones(1000)
+    o = ref.copy()
+    o[:5] += 0.02
+    r = metrics.check_result(o, ref)
+    assert r["violator_ratio"] == 0.005 and r["passed"]
+    o[5] += 0.02
+    r = metrics.check_result(o, ref)
+    assert r["violator_ratio"] == 0.006 and not r["passed"]
+    # the 0.1 guard on the largest difference, with no element violating
+    big = np.full(1000, 100.0)
+    o = big.copy()
+    o[17] += 0.09
+    r = metrics.check_result(o, big)
+    assert r["violator_ratio"] == 0.0 and r["passed"]
+    o[17] += 0.02
+    r = metrics.check_result(o, big)
+    assert r["violator_ratio"] == 0.0 and abs(r["diff_max"] - 0.11) < 1e-9 and not r["passed"]
+    assert abs(r["diff_sum"] - 0.11) < 1e-9
+
+
 def _p2_inputs(n_tokens, peak_dims, seed=77):
     """Top-k MLA inputs at the page's shape for a sample of tokens: K for all
     S keys, Q only for the sampled tokens, key sets = self + min(W-1, t)
@@ -577,3 +614,41 @@ def test_backward_gqa_sums_over_query_heads():
     np.testing.assert_allclose(dq, dq2, rtol=0, atol=1e-13)
     np.testing.assert_allclose(dk, dk2.reshape(B, Hkv, G, S, D).sum(2), rtol=0, atol=1e-12)
     np.testing.assert_allclose(dv, dv2.reshape(B, Hkv, G, S, D).sum(2), rtol=0, atol=1e-12)
+
+
+def test_backward_error_scales_bound_the_gradients():
+    """The first-order error scales used by the backward's per-element gate:
+    (1) each is at least the magnitude of its gradient (triangle inequality);
+    (2) the dV scale equals |dV| exactly when every dO is >= 0 (all terms of
+    dV = P^T dO then share a sign); (3) a single-key row has P = 1 and dS = 0,
+    so its dQ scale is exactly 2 scale E |k| with E = sum_d |dO_d| |v_d|;
+    (4) under a mask the scales vanish exactly where the gradients must."""
+    g = np.random.default_rng(31)
+    B, Hq, Hkv, S, D = 1, 4, 2, 12, 8
+    q = torch.from_numpy(g.standard_normal((B, Hq, S, D)))
+    k = torch.from_numpy(g.standard_normal((B, Hkv, S, D)))
+    v = torch.from_numpy(g.standard_normal((B, Hkv, S, D)))
+    do = torch.from_numpy(g.standard_normal((B, Hq, S, D)))
+    for causal in (False, True):
+        dq, dk, dv = oracle.attn_dense_bwd(q, k, v, do, scale=0.3, causal=causal)
+        gq, gk, gv = oracle.attn_dense_bwd_bound(q, k, v, do, scale=0.3, causal=causal)
+        assert np.all(gq >= np.abs(dq) - 1e-12) and np.all(gk >= np.abs(dk) - 1e-12)
+        assert np.all(gv >= np.abs(dv) - 1e-12)
+        # the bound is not trivially loose either: same order as the gradient
+        assert np.linalg.norm(gv) < 10 * np.linalg.norm(dv)
+    dq, dk, dv = oracle.attn_dense_bwd(q, k, v, do.abs(), scale=0.3, causal=True)
+    _, _, gv = oracle.attn_dense_bwd_bound(q, k, v, do.abs(), scale=0.3, causal=True)
+    assert np.allclose(gv, np.abs(dv), rtol=1e-13, atol=1e-15)
+    # causal row 0 sees key 0 only
+    gq, _, _ = oracle.attn_dense_bwd_bound(q, k, v, do, scale=0.3, causal=True)
+    for hq in range(Hq):
+        kv = hq // (Hq // Hkv)
+        e = float((do[0, hq, 0].abs() * v[0, kv, 0].abs()).sum())
+        assert np.allclose(gq[0, hq, 0], 2 * 0.3 * e * k[0, kv, 0].abs().numpy(), rtol=1e-13)
+    # a fully excluded row and a fully excluded key column
+    mask = torch.zeros((S, S), dtype=torch.uint8)
+    mask[5] = 1
+    mask[:, 9] = 1
+    gq, gk, gv = oracle.attn_dense_bwd_bound(q, k, v, do, scale=0.3, mask=mask)
+    assert np.all(gq[:, :, 5] == 0) and np.all(gk[:, :, 9] == 0) and np.all(gv[:, :, 9] == 0)
+    assert np.all(gq[:, :, 4] > 0)
