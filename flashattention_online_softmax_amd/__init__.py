@@ -70,6 +70,9 @@ def load():
                                       P, P, ctypes.c_void_p]
         lib.fa_fwd_splitkv.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_int,
                                        P, P, P, ctypes.c_void_p]
+        lib.fa_fwd_splitkv_noalloc.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                               ctypes.c_int, P, P, ctypes.c_void_p]
+        lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
         lib.fa_fwd_splitkv_splits.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
         lib.fa_fwd_splitkv_splits.restype = ctypes.c_int
         lib.fa_fwd_splitkv_workspace_elems.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int]
@@ -277,4 +280,17 @@ def fa_fwd_splitkv(q, k, v, *, scale, causal=False, seqlens_q=None, seqlens_k=No
                               _ref(describe(seqlens_k)), int(bool(causal)), float(scale), float(rescale_threshold),
                               int(num_splits), _ref(describe(workspace)), _ref(describe(out)), _ref(describe(lse)),
                               _stream(stream)))
+    return out, lse
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, *, scale, causal=False, seqlens_q=None, seqlens_k=None, num_splits=0,
+                           rescale_threshold=DEFAULT_RESCALE_THRESHOLD, out, lse, stream=None):
+    """fa_fwd_splitkv whose partial results live in the library's static
+    device scratch (no allocation in the call; out and lse are required)."""
+    lib = load()
+    _need_gpu(q, k, v, seqlens_q, seqlens_k, out, lse)
+    _check(lib.fa_fwd_splitkv_noalloc(_ref(describe(q)), _ref(describe(k)), _ref(describe(v)),
+                                      _ref(describe(seqlens_q)), _ref(describe(seqlens_k)), int(bool(causal)),
+                                      float(scale), float(rescale_threshold), int(num_splits), _ref(describe(out)),
+                                      _ref(describe(lse)), _stream(stream)))
     return out, lse

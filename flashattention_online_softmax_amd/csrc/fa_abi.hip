@@ -549,8 +549,9 @@ int64_t fa_fwd_splitkv_workspace_elems(int64_t B, int64_t Hq, int64_t Sq, int64_
   return ns > 1 ? (int64_t)ns * B * Hq * Sq * (Dv + 1) : 0;
 }
 
-// Body of the split-KV entry point: the partial results go to the caller's
-// workspace tensor.
+// Shared body of the split-KV entry points: the partial results go to the
+// caller's workspace tensor, or with static_scratch to the library's static
+// device scratch (looked up only once a split is actually needed).
 static fa_status splitkv_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* seqlens_q,
                               const fa_tensor* seqlens_k, int causal, float scale, float rescale_threshold,
                               int num_splits, const fa_tensor* workspace, bool static_scratch, const fa_tensor* o,
@@ -562,6 +563,15 @@ fa_status fa_fwd_splitkv(const fa_tensor* q, const fa_tensor* k, const fa_tensor
   clear_error();
   return splitkv_impl(q, k, v, seqlens_q, seqlens_k, causal, scale, rescale_threshold, num_splits, workspace,
                       false, o, lse, stream);
+}
+
+fa_status fa_fwd_splitkv_noalloc(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                                 const fa_tensor* seqlens_q, const fa_tensor* seqlens_k, int causal, float scale,
+                                 float rescale_threshold, int num_splits, const fa_tensor* o, const fa_tensor* lse,
+                                 void* stream) {
+  clear_error();
+  return splitkv_impl(q, k, v, seqlens_q, seqlens_k, causal, scale, rescale_threshold, num_splits, nullptr, true, o,
+                      lse, stream);
 }
 
 static fa_status splitkv_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* seqlens_q,
@@ -596,7 +606,12 @@ static fa_status splitkv_impl(const fa_tensor* q, const fa_tensor* k, const fa_t
                   ns, (long long)need);
     ws = (float*)workspace->data;
   } else {
-    return fail(FA_ERR_NULL, "workspace is NULL");
+    if (need > fa::kScratchFloats)
+      return fail(FA_ERR_UNSUPPORTED,
+                  "%d key ranges of %lld rows need %lld floats of partial results; the static scratch holds %lld "
+                  "(use fewer ranges or fa_fwd_splitkv with a workspace)",
+                  ns, (long long)(B * Hq * Sq), (long long)need, (long long)fa::kScratchFloats);
+    if ((s = hip_status(fa::scratch_address(&ws))) != FA_OK) return s;
   }
   if (!fits_i32((int64_t)ns * B * Hq * ((Sq + 255) / 256)))  // one workgroup per (range, 256 rows, head)
     return fail(FA_ERR_UNSUPPORTED, "too many workgroups");

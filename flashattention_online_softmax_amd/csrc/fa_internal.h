@@ -129,6 +129,14 @@ hipError_t launch_varlen(Dt dt, int D, bool causal, FwdParams& p, hipStream_t st
 hipError_t launch_splitkv(Dt dt, int D, bool causal, FwdParams& p, hipStream_t stream);
 // The merge alone (fa_split.hip).
 hipError_t launch_merge(Dt dt, const MergeParams& m, hipStream_t stream);
+
+// Static device scratch of the allocation-free split-KV entry point (a
+// file-scope array in fa_split.hip): 64 MiB of fp32 per GPU.
+constexpr int64_t kScratchFloats = (int64_t)16 << 20;
+constexpr int kMaxDevices = 64;
+// Device address of the current device's copy of the scratch array (looked
+// up once per device, with that device current).
+hipError_t scratch_address(float** ptr);
 hipError_t launch_topk(Dt dt, TopkParams& p, hipStream_t stream);
 hipError_t launch_bwd(Dt dt, bool causal, bool mask, BwdParams& p, hipStream_t stream);
 

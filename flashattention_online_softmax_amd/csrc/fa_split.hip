@@ -15,11 +15,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
+
+// Static partial-result buffer of the allocation-free split-KV entry point:
+// every GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory; the
+// device address comes from hipGetSymbolAddress, once per device (below).
+static __device__ __align__(256) float scratch[kScratchFloats];
+
 namespace {
+
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices] = {};
 
 constexpr int kRowsPerBlock = 4;
 
@@ -70,6 +82,23 @@ hipError_t launch_merge_t(const MergeParams& m, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t scratch_address(float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    // With this device current: its own copy of the array.
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_merge(Dt dt, const MergeParams& m, hipStream_t stream) {
   if ((int64_t)m.B * m.Hq * m.Sq == 0) return hipSuccess;

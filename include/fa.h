@@ -279,6 +279,25 @@ fa_status fa_fwd_splitkv(const fa_tensor* q, const fa_tensor* k, const fa_tensor
                          const fa_tensor* workspace, const fa_tensor* o, const fa_tensor* lse,
                          void* stream);
 
+/*
+ * fa_fwd_splitkv without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The partial results go to a static
+ * device array of the library, 64 MiB (16M fp32) per GPU, held from the
+ * first call on that GPU until the process ends; its address is looked up
+ * once per device. Arguments and results as fa_fwd_splitkv. A problem whose
+ * partial results exceed the array (num_splits * B * Hq * Sq * (Dv + 1)
+ * floats, with num_splits as fa_fwd_splitkv_splits resolves it) returns
+ * FA_ERR_UNSUPPORTED and launches nothing. Every call on one GPU shares the
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller. Nothing in the array needs to start
+ * at zero (every partial result a merge reads is written by the same call).
+ */
+fa_status fa_fwd_splitkv_noalloc(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                                 const fa_tensor* seqlens_q, const fa_tensor* seqlens_k, int causal,
+                                 float scale, float rescale_threshold, int num_splits,
+                                 const fa_tensor* o, const fa_tensor* lse, void* stream);
+
 /* Number of key ranges fa_fwd_splitkv uses for these sizes and num_splits
  * (-1 for negative sizes). */
 int fa_fwd_splitkv_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int num_splits);

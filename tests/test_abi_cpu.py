@@ -232,6 +232,18 @@ def test_splitkv_sizing_and_validation(lib):
     assert sk(q=q32, k=k32, v=v32, o=o32) == "FA_ERR_UNSUPPORTED"
     assert sk(causal=2) == "FA_ERR_VALUE"
 
+    def na(ns=4, q=q, k=k, v=v, o=o):
+        return name(lib, lib.fa_fwd_splitkv_noalloc(R(q), R(k), R(v), None, None, 0, 0.1, 0.0, ns, R(o), R(lse), None))
+
+    # validation happens before the static scratch is looked up (no GPU here)
+    assert na(ns=65) == "FA_ERR_VALUE"
+    assert na(q=q32, k=k32, v=v32, o=o32) == "FA_ERR_UNSUPPORTED"
+    big_q, big_k, big_v, big_o, big_l = good(B=2, Hq=32, Hkv=32, S=1024)
+    kk = T([2, 32, 64 * 192, 128])
+    assert name(lib, lib.fa_fwd_splitkv_noalloc(R(big_q), R(kk), R(kk), None, None, 0, 0.1, 0.0, 64, R(big_o),
+                                                R(big_l), None)) == "FA_ERR_UNSUPPORTED"
+    assert b"static scratch" in lib.fa_last_error()
+
 
 def test_binding_refuses_cpu_tensors(lib):
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
