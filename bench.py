@@ -334,6 +334,7 @@ def main():
                     help="time only this workload (any kind) for --steps calls and print its figure; "
                          "for profiling one kernel")
     ap.add_argument("--threshold", type=float, default=0.0, help="rescale threshold of --only (log2 units)")
+    ap.add_argument("--backward", action="store_true", help="with --only (a dense workload): time the backward")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the benchmark, run --steps plain device copies of this many "
                          "bytes (the reference kernel for scaling HBM byte counters)")
@@ -361,13 +362,17 @@ def main():
     fa.load()  # raises if the HIP library is not built
 
     if args.only:
-        log("only %s (threshold %g)" % (args.only, args.threshold))
+        log("only %s (threshold %g%s)" % (args.only, args.threshold, ", backward" if args.backward else ""))
         w = synth.workload(args.only)
         fl = workload_flops(w)
-        c = make_call(w, rescale_threshold=args.threshold)
+        if args.backward:
+            fl *= 2.5  # five products over the pairs against the forward's two
+            c = make_bwd_call(w)
+        else:
+            c = make_call(w, rescale_threshold=args.threshold)
         wall, km = time_calls(c, args.steps, args.warmup, 0.3)
-        out = {"workload": args.only, "kernel_ms": round(km, 4), "tflops": round(fl / (km * 1e-3) / 1e12, 2),
-               "rescale_threshold_log2": args.threshold}
+        out = {"workload": args.only + ("_bwd" if args.backward else ""), "kernel_ms": round(km, 4),
+               "tflops": round(fl / (km * 1e-3) / 1e12, 2), "rescale_threshold_log2": args.threshold}
         if w["kind"] == "topk":
             out["gbs"] = round(topk_work(w, w["idx_a"])[1] / (km * 1e-3) / 1e9, 1)
         print(json.dumps(out), flush=True)
@@ -420,10 +425,14 @@ def main():
         sec[args.workload + "_lazy8"] = {"tflops": round(flops / (km8 * 1e-3) / 1e12, 2), "kernel_ms": round(km8, 4),
                                          "frac_mfma_peak": round(flops / (km8 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                                          "exact_max_cost": round(kern_ms / km8 - 1.0, 4)}
-        for name in ("causal_bf16_s8192", "gqa_mask_f16_s8192", "blocksparse_f16_s8192"):
+        for name in ("causal_bf16_s8192", "gqa_mask_f16_s8192", "blocksparse_f16_s8192", "splitkv_bf16_q512_k65536",
+                     "varlen_bf16_b16"):
             log("secondary %s" % name)
             w2 = synth.workload(name)
             sec[name] = time_secondary(name, w2, nsec, 0.0)
+            if name == "splitkv_bf16_q512_k65536":
+                B2, H2, S2, _ = w2["q"].shape
+                sec[name]["key_ranges"] = fa.splitkv_splits(B2, H2, S2, w2["k"].shape[2])
             if name == "causal_bf16_s8192":
                 lz = time_secondary(name, w2, nsec, 8.0)
                 lz.pop("traffic")

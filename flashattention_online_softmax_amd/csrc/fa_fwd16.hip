@@ -356,10 +356,11 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     const float x0 = fast_exp2(__builtin_fmaf(sv[kt][ii], p.scale_log2, -mc[b]));
     const float x1 = fast_exp2(__builtin_fmaf(sv[kt][ii + 1], p.scale_log2, -mc[b]));
     pop[e >> 3][(e & 7) >> 1] = T::pack2(x0, x1);
+    // two running sums (pairs alternate), each started by its first pair
     if ((e >> 1) & 1)
-      rs1[b] += x0 + x1;
+      rs1[b] = e == 2 ? x0 + x1 : rs1[b] + (x0 + x1);
     else
-      rs0[b] += x0 + x1;
+      rs0[b] = e == 0 ? x0 + x1 : rs0[b] + (x0 + x1);
     // Pin the results here: otherwise the compiler sinks the exponentials
     // below the MFMAs they are meant to overlap.
     asm volatile("" ::"v"(pop[e >> 3][(e & 7) >> 1]), "v"(rs0[b]), "v"(rs1[b]));

@@ -50,7 +50,7 @@ template <int NW, int QT, int HP, int XM = 0>
 __device__ __forceinline__ Work decode_work(const FwdParams& p) {
   constexpr int WPH = NW / HP;
   constexpr int MPH = WPH * QT * 32;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform: scalar
   const int BHkv = p.B * p.Hkv;
   const int per_mb = BHkv * p.n_hgroups;
   const int id = blockIdx.x;
