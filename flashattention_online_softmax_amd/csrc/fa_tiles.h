@@ -36,11 +36,13 @@ struct Work {
 // last query block comes first (longest causal rows first) and the KV-head
 // index varies fastest, so the query heads of one KV head share an XCD
 // (workgroup i runs on XCD i % 8). Head group g takes the (batch, KV head)
-// pairs rotated by g * B Hkv / n_hgroups: with eight pairs and two head
-// groups each XCD then serves two pairs instead of one, so batches of
-// different lengths (per-batch sequence lengths) no longer leave whole XCDs
-// idle; when B Hkv is a multiple of 8 n_hgroups the rotation keeps every
-// pair on its XCD.
+// pairs rotated by g * B Hkv / n_hgroups when batches can differ in length
+// (per-batch sequence lengths or packed sequences): with eight pairs and two
+// head groups each XCD then serves two pairs instead of one, so a short batch
+// no longer leaves whole XCDs idle; when B Hkv is a multiple of 8 n_hgroups
+// the rotation keeps every pair on its XCD. Without per-batch lengths there
+// is no rotation, so the head groups of a KV head always share its XCD and
+// read its K/V tiles through one L2.
 //
 // XM selects the extra modes of the 16-bit kernels: 1 = packed
 // variable-length batches (row and key offsets and lengths from cu_q / cu_k),
@@ -67,7 +69,8 @@ __device__ __forceinline__ Work decode_work(const FwdParams& p) {
   }
   const int mb = p.n_mblocks - 1 - mb_rank;
   const int hg = r / BHkv;
-  const int bkv = (r - hg * BHkv + hg * (BHkv / p.n_hgroups)) % BHkv;
+  const bool ragged = XM == 1 || p.seqlens_q || p.seqlens_k;
+  const int bkv = ragged ? (r - hg * BHkv + hg * (BHkv / p.n_hgroups)) % BHkv : r - hg * BHkv;
   Work wk;
   wk.b = bkv / p.Hkv;
   wk.hkv = bkv - wk.b * p.Hkv;

@@ -70,11 +70,14 @@ def log(case: str, rep: dict):
             f.write(line + "\n")
 
 
-def check(case, o, lse, o_ref, lse_ref, dtype, o_abs, extra=None, plain_cap=None):
+def check(case, o, lse, o_ref, lse_ref, dtype, o_abs, extra=None, plain_cap=None, page_gate=False):
     """Compares GPU outputs (torch, any device) with the oracle (numpy fp64);
     o_abs is the oracle output with |V| (the P-rounding bound's weights).
     plain_cap overrides the dtype's cap on the fraction of elements failing
-    the literal atol/rtol gate (0 = every element must pass it).
+    the literal atol/rtol gate (0 = every element must pass it). page_gate
+    also asserts the ops-transformer pytest page's comparison (section 7:
+    at most 0.5% of elements off by more than 0.005 relative, none by more
+    than 0.1), which the full-size fp16 workloads meet.
     Asserts the gates and returns the report."""
     o = o.detach().float().cpu().numpy().astype(np.float64)
     lse = lse.detach().cpu().numpy().astype(np.float64)
@@ -95,7 +98,8 @@ def check(case, o, lse, o_ref, lse_ref, dtype, o_abs, extra=None, plain_cap=None
     lr = metrics.lse_report(lse, lse_ref)
     rep.update({"lse_max_abs": lr["max_abs"], "lse_neginf_mismatch": lr["neginf_mismatch"],
                 "lse_nan": lr["nan"]})
-    rep["check_result"] = metrics.check_result(o, o_ref)["violator_ratio"]
+    cr = metrics.check_result(o, o_ref)
+    rep["check_result"] = cr["violator_ratio"]
     if extra:
         rep.update(extra)
     log(case, rep)
@@ -108,6 +112,8 @@ def check(case, o, lse, o_ref, lse_ref, dtype, o_abs, extra=None, plain_cap=None
         assert plain["fail_frac"] <= cap, rep
     assert rep["lse_max_abs"] <= LSE_TOL, rep
     assert rep["lse_neginf_mismatch"] == 0, rep
+    if page_gate:
+        assert cr["passed"], (rep, cr)
     return rep
 
 

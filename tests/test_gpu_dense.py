@@ -209,7 +209,7 @@ def test_empty_problems():
 # (threshold 8) on the same inputs.
 # ---------------------------------------------------------------------------
 
-def _full_dense(name, n_rows, must_rows=(), plain_cap=None):
+def _full_dense(name, n_rows, must_rows=(), plain_cap=None, page_gate=False):
     w = synth.workload(name)
     q, k, v = w["q"], w["k"], w["v"]
     mask = w.get("mask")
@@ -232,7 +232,7 @@ def _full_dense(name, n_rows, must_rows=(), plain_cap=None):
         assert torch.all(torch.isfinite(lse))  # every row of these workloads has a key
         reps[thr] = check("full_%s_thr%g" % (name, thr), o.reshape(-1, D)[idx], lse.reshape(-1)[idx], o_ref,
                           lse_ref, q.dtype, o_abs, {"sampled_rows": len(rows), "rescale_threshold": thr},
-                          plain_cap=plain_cap)
+                          plain_cap=plain_cap, page_gate=page_gate)
         del o, lse
     return reps
 
@@ -257,7 +257,7 @@ def test_full_causal_bf16_s8192():
 
 def test_full_gqa_mask_f16_s8192():
     # fp16 at full size: the literal atol/rtol gate on every sampled element
-    _full_dense("gqa_mask_f16_s8192", 256, plain_cap=0.0)
+    _full_dense("gqa_mask_f16_s8192", 256, plain_cap=0.0, page_gate=True)
 
 
 # ---------------------------------------------------------------------------

@@ -80,7 +80,8 @@ def test_full_blocksparse_f16_s8192():
         o, lse = fa.fa_fwd_blocksparse(qg, kg, vg, bi, scale=w["scale"], seqlens=sl, rescale_threshold=thr)
         torch.cuda.synchronize()
         check("full_blocksparse_f16_s8192_thr%g" % thr, o.reshape(-1, D)[idx], lse.reshape(-1)[idx], o_ref,
-              lse_ref, torch.float16, o_abs, {"sampled_rows": len(rows), "rescale_threshold": thr}, plain_cap=0.0)
+              lse_ref, torch.float16, o_abs, {"sampled_rows": len(rows), "rescale_threshold": thr}, plain_cap=0.0,
+              page_gate=True)
         # padded rows of batch 1 (i >= 5000) are exactly zero / -inf everywhere
         assert torch.all(o[1, :, 5000:] == 0) and torch.all(torch.isneginf(lse[1, :, 5000:]))
         assert torch.all(torch.isfinite(lse[0])) and torch.all(torch.isfinite(lse[1, :, :5000]))
