@@ -1,40 +1,24 @@
-// Dense, causal, masked, GQA and block-sparse attention forward for gfx950.
+// Attention forward launchers and the fp32 kernel for gfx950.
 //
 // Method: the online-softmax forward of the "FlashAttention correctness
 // verification" page (tiled computation and loop-invariant sections): for each
 // KV tile, S = scale * Q K^T, m' = max(m, rowmax S), l' = l * e^(m - m') +
 // rowsum e^(S - m'), O' = O * e^(m - m') + e^(S - m') V, finally O = O / l and
-// LSE = m + ln l. The max is exact (every growth rescales), as the sparse-MLA
-// page of flash-attention prescribes for the exact-max forward.
+// LSE = m + ln l. The reference max moves only when a tile's max exceeds it by
+// more than the rescale threshold (the threshold branch of the flash-attention
+// sparse-MLA exact-running-max guide); threshold 0 is the exact running max.
 //
-// Work decomposition (MI355X): one workgroup of NW waves owns MPH consecutive
-// query rows of HP query heads that share one KV head (HP > 1 packs GQA heads
-// so that a single K/V tile in LDS serves them all). Every wave owns QT tiles
-// of 32 query rows. With 8 waves of 32 rows a wave needs < 256 registers, so
-// two waves share each SIMD and one wave's softmax (VALU) overlaps the
-// other's MFMA work. Workgroups are numbered so that the longest causal tiles
-// start first and every KV head maps to one XCD (consecutive workgroup ids go
-// to consecutive XCDs and the KV-head index is the fastest-varying part).
-//
-// Per 64-key tile:
-//   * K and V tiles are copied HBM -> VGPR -> LDS, double buffered, one tile
-//     ahead of the compute, with an XOR swizzle of the 16-byte chunks so that
-//     the MFMA operand reads below hit distinct LDS banks.
-//   * S^T = K Q^T on v_mfma_f32_32x32x16 (K from LDS as the A operand, Q^T
-//     resident in VGPRs as the B operand). In the result each lane owns one
-//     query column and 16 keys of it, so the row max and row sum are in-lane
-//     reductions plus a single v_permlane32_swap between the wave halves.
-//   * p = exp2(s * scale*log2e - m) on v_exp_f32 (one FMA + one exp per
-//     score), m being the running max already in the exp2 domain; l
-//     accumulates the fp32 p; p is rounded to 16 bits.
-//   * O^T += V^T P^T on MFMA: P^T is already in B-operand layout (each lane
-//     owns its query), V^T is read from the row-major V tile with
-//     ds_read_b64_tr_b16, whose key order is chosen to match the key order in
-//     which the S^T accumulator holds P. The rescale by e^(m - m') is then a
-//     per-lane scalar multiply.
-// Epilogue: O = acc / l rounded to the output dtype, LSE = ln2 * (m + log2 l)
-// in fp32 (m being the running max in the exp2 domain); rows with no key give
-// O = 0 and LSE = -inf.
+// This file holds
+//   * fwd32_kernel: the fp32 path (v_mfma_f32_32x32x2f32, P kept in fp32,
+//     32-key tiles staged in LDS as padded fp32 rows, one wave per 32 query
+//     rows), D in {64, 128}; it exists for exactness, not speed;
+//   * the launchers of the 16-bit kernels of fa_fwd16.hip, which live in the
+//     separately compiled code object (fa_module.hip looks them up by name):
+//     grid sizing for the dense, causal, masked, GQA and block-sparse modes,
+//     for packed sequences (cu_seqlens) and for split-KV key ranges, whose
+//     partial results the merge kernel of fa_split.hip combines.
+// The work decomposition (rows per workgroup, XCD-aware order) is decode_work
+// in fa_tiles.h, shared by every forward kernel.
 #include <cstdio>
 #include <type_traits>
 
