@@ -275,6 +275,9 @@ fa_status fa_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
                   (p.m_ss % 4 == 0);
     p.mask_vec16 = (((uintptr_t)mask->data) % 16 == 0) && (p.m_sb % 16 == 0) && (p.m_sh % 16 == 0) &&
                    (p.m_ss % 16 == 0);
+    // LDS-staged mask tiles: whole 16-byte chunks of every row up to Skv, and
+    // 32-bit offsets for 32 rows of one (batch, head) slice.
+    p.mask_lds = p.mask_vec16 && Skv % 16 == 0 && p.m_ss < (int64_t(1) << 26);
   }
   p.seqlens_q = seqlens_q ? (const int32_t*)seqlens_q->data : nullptr;
   p.seqlens_k = seqlens_k ? (const int32_t*)seqlens_k->data : nullptr;

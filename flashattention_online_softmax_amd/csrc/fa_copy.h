@@ -17,8 +17,9 @@ namespace fa {
 // that position (the XOR is an involution). The per-lane byte offset inside a
 // tile is the same for every tile and is computed once. On the last, partial
 // tile, rows at or past Lk fetch row Lk - 1 instead (finite data whose scores
-// are masked), so nothing past the valid keys is ever read.
-template <int D, int NW, bool IS_V, int ROWS = BN>
+// are masked), so nothing past the valid keys is ever read. With PERM, LDS
+// row r of the tile receives key perm_key(r) instead of key r.
+template <int D, int NW, bool IS_V, int ROWS = BN, bool PERM = false>
 struct TileCopy {
   static constexpr int CH = D / 8;
   static constexpr int NINST = ROWS * CH / 64;
@@ -32,6 +33,8 @@ struct TileCopy {
     return (((int)threadIdx.x >> 6) * PER_WAVE + j) * 64 + ((int)threadIdx.x & 63);
   }
   __device__ __forceinline__ static int chunk_row(int j) { return pos(j) / CH; }
+  // Key (row of the K or V head, from the tile start) that LDS row chunk_row(j) holds.
+  __device__ __forceinline__ static int src_row(int j) { return PERM ? perm_key(chunk_row(j)) : chunk_row(j); }
   __device__ __forceinline__ static uint32_t chunk_col_bytes(int j) {
     const int row = pos(j) / CH, ph = pos(j) % CH;
     return (uint32_t)((ph ^ (IS_V ? vswz<D>(row) : kswz<D>(row))) * 16);
@@ -41,7 +44,7 @@ struct TileCopy {
   __device__ __forceinline__ TileCopy(const uint16_t* head, int64_t row_stride)
       : g(uniform_ptr(head)), row_bytes((uint32_t)row_stride * 2u) {
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) off[j] = (uint32_t)chunk_row(j) * row_bytes + chunk_col_bytes(j);
+    for (int j = 0; j < PER_WAVE; ++j) off[j] = (uint32_t)src_row(j) * row_bytes + chunk_col_bytes(j);
   }
 
   // kstart, Lk and lds are the same in every lane of the wave.
@@ -57,7 +60,7 @@ struct TileCopy {
       const int last = Lk - 1 - kstart;
 #pragma unroll
       for (int j = 0; j < PER_WAVE; ++j) {
-        const int over = max(chunk_row(j) - last, 0);
+        const int over = max(src_row(j) - last, 0);
         lds_copy16(base, off[j] - (uint32_t)over * row_bytes, l0 + j * 1024);
       }
     }

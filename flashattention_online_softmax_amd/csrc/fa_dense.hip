@@ -194,14 +194,14 @@ void set_grid(FwdParams& p, dim3& grid) {
 // the 16-bit code object (XM: 0 BNSD, 1 packed variable-length, 2 split-KV
 // partials, one workgroup per key range as well).
 template <int NW, int QT, int HP>
-hipError_t launch16_named(const char* tn, int D, bool causal, bool mask, bool sparse, FwdParams& p,
+hipError_t launch16_named(const char* tn, int D, bool causal, int mask, bool sparse, FwdParams& p,
                           hipStream_t st, int xm = 0) {
   dim3 grid;
   set_grid<NW, QT, HP>(p, grid);
   if (xm == 2) grid.x *= (unsigned)p.n_splits;
   char name[96];
   snprintf(name, sizeof(name), "fa_fwd16_%s_d%d_w%d_q%d_h%d_c%dm%ds%dx%d", tn, D, NW, QT, HP,
-           causal ? 1 : 0, mask ? 1 : 0, sparse ? 1 : 0, xm);
+           causal ? 1 : 0, mask, sparse ? 1 : 0, xm);
   hipFunction_t fn = nullptr;
   hipError_t e = code_object_function(name, &fn);
   if (e != hipSuccess) return e;
@@ -212,12 +212,13 @@ hipError_t launch16_named(const char* tn, int D, bool causal, bool mask, bool sp
 hipError_t launch16(const char* tn, int D, bool causal, bool has_mask, bool sparse, FwdParams& p,
                     hipStream_t st) {
   // Dense: 8 waves of 32 query rows (256 rows per workgroup, two waves per
-  // SIMD).
-  if (!sparse) return launch16_named<8, 1, 1>(tn, D, causal, has_mask, false, p, st);
+  // SIMD). A boolean mask whose rows are 16-byte chunks is staged through
+  // LDS (mode 2), any other is loaded into registers (mode 1).
+  if (!sparse) return launch16_named<8, 1, 1>(tn, D, causal, has_mask ? (p.mask_lds ? 2 : 1) : 0, false, p, st);
   // Block-sparse: 128 query rows per head (one query block); with an even
   // GQA group two heads of the group share each K/V tile.
-  if (p.G % 2 == 0) return launch16_named<8, 1, 2>(tn, D, false, false, true, p, st);
-  return launch16_named<4, 1, 1>(tn, D, false, false, true, p, st);
+  if (p.G % 2 == 0) return launch16_named<8, 1, 2>(tn, D, false, 0, true, p, st);
+  return launch16_named<4, 1, 1>(tn, D, false, 0, true, p, st);
 }
 
 template <int D, bool CAUSAL, bool MASK, bool SPARSE>
@@ -245,11 +246,11 @@ hipError_t launch_dense(Dt dt, int D, bool causal, bool has_mask, bool sparse, F
 }
 
 hipError_t launch_varlen(Dt dt, int D, bool causal, FwdParams& p, hipStream_t stream) {
-  return launch16_named<8, 1, 1>(dt == Dt::F16 ? "f16" : "bf16", D, causal, false, false, p, stream, 1);
+  return launch16_named<8, 1, 1>(dt == Dt::F16 ? "f16" : "bf16", D, causal, 0, false, p, stream, 1);
 }
 
 hipError_t launch_splitkv(Dt dt, int D, bool causal, FwdParams& p, hipStream_t stream) {
-  hipError_t e = launch16_named<8, 1, 1>(dt == Dt::F16 ? "f16" : "bf16", D, causal, false, false, p, stream, 2);
+  hipError_t e = launch16_named<8, 1, 1>(dt == Dt::F16 ? "f16" : "bf16", D, causal, 0, false, p, stream, 2);
   if (e != hipSuccess) return e;
   MergeParams m;
   m.part_o = p.part_o;

@@ -77,8 +77,15 @@ namespace {
 // and keys); XM = 2: split-KV, the workgroup sweeps only the keys
 // [split * split_len, (split + 1) * split_len) and writes its normalised fp32
 // output and LSE to the partial-result buffers instead of O and LSE.
-template <class T, int D, int NW, int QT, int HP, bool CAUSAL, bool MASK, bool SPARSE, int XM>
+template <class T, int D, int NW, int QT, int HP, bool CAUSAL, int MASKM, bool SPARSE, int XM>
 __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
+  // Boolean mask: MASKM = 1 loads each wave's mask words into registers one
+  // phase ahead; MASKM = 2 copies each wave's mask rows into LDS two tiles
+  // ahead with the K/V copies (16-byte aligned masks), with the keys of the
+  // K and V tiles permuted (perm_key) so that a lane's 16 keys of a 32-key
+  // half are consecutive and their mask bytes one 16-byte chunk.
+  constexpr bool MASK = MASKM != 0;
+  constexpr bool MLDS = MASKM == 2;
   constexpr int WPH = NW / HP;
   constexpr int MPH = WPH * QT * 32;
   // 32-key halves per tile: 3 for dense D = 128 without a boolean mask; the
@@ -95,12 +102,18 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   constexpr int AHEAD = 3;    // operand pairs read ahead
   constexpr int RING = AHEAD + 1;
   static_assert(!SPARSE || MPH == 128, "block-sparse needs 128 query rows per head");
+  static_assert(!MLDS || (QT == 1 && HP == 1 && BNT == 64), "LDS-staged masks: 32 rows per wave, 64-key tiles");
 
   // K ring (3 tiles) then V ring (3 tiles); the epilogue reuses the space.
   __shared__ __attribute__((aligned(16))) uint16_t s_ring[6 * TILE];
   uint16_t* const s_kring = s_ring;
   uint16_t* const s_vring = s_ring + 3 * TILE;
   __shared__ int s_kstart[SPARSE ? 512 : 1];
+  // LDS-staged mask tiles: per wave three slots of its 32 rows x 64 bytes,
+  // 16-byte chunk c of row r at chunk position c ^ ((r >> 2) & 3) (the
+  // chunk reads of 16 consecutive rows then hit distinct banks).
+  constexpr int MSLOT = 32 * BNT;
+  __shared__ __attribute__((aligned(16))) uint8_t s_mring[MLDS ? NW * 3 * MSLOT : 16];
   __shared__ int s_n;
 
   const int tid = threadIdx.x;
@@ -167,9 +180,10 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
 
   auto tile_start = [&](int it) __attribute__((always_inline)) { return SPARSE ? s_kstart[it] : klo + it * BNT; };
 
-  const TileCopy<D, NW, false, BNT> kcopy(kg, p.k_ss);
-  const TileCopy<D, NW, true, BNT> vcopy(vg, p.v_ss);
-  constexpr int NCOPY = TileCopy<D, NW, false, BNT>::PER_WAVE + TileCopy<D, NW, true, BNT>::PER_WAVE;
+  const TileCopy<D, NW, false, BNT, MLDS> kcopy(kg, p.k_ss);
+  const TileCopy<D, NW, true, BNT, MLDS> vcopy(vg, p.v_ss);
+  constexpr int MCOPY = MLDS ? MSLOT / 1024 : 0;  // mask copy instructions per wave and tile
+  constexpr int NCOPY = TileCopy<D, NW, false, BNT, MLDS>::PER_WAVE + TileCopy<D, NW, true, BNT, MLDS>::PER_WAVE + MCOPY;
 
   // Per-lane element offsets of the MFMA operands inside a tile.
   // K operand r (A operand of S^T): key half kt = r % NKT (rows 32 kt + c),
@@ -209,7 +223,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   // the copies).
   uint32_t mwords[QT][MASK ? NKT : 1][4];
   auto mask_load = [&](int j) __attribute__((always_inline)) {
-    if constexpr (MASK) {
+    if constexpr (MASK && !MLDS) {
       const int kstart = tile_start(j);
       if (NKT == 2 && p.mask_vec16 && kstart + BNT <= p.Skv) {
         // Coalesced: the two lanes of a row load its 64 mask bytes, 32 each
@@ -265,6 +279,46 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
       }
     }
   };
+  // LDS-staged masks: lane i of copy instruction n fetches chunk position
+  // 64 n + i of the wave's slot (row r = pos / 4). Rows past Sq fetch row
+  // Sq - 1 and chunks at or past Skv the row's last chunk: finite bytes
+  // whose keys or rows the edge masking removes.
+  const int mrow_b = min(wk.row0, p.Sq - 1);
+  const uint8_t* const mbase =
+      MLDS ? p.mask + wk.b * p.m_sb + wk.hq * p.m_sh + (int64_t)mrow_b * p.m_ss : nullptr;
+  uint32_t mroff[MCOPY > 0 ? MCOPY : 1];
+  int mcol[MCOPY > 0 ? MCOPY : 1];
+#pragma unroll
+  for (int n = 0; n < MCOPY; ++n) {
+    const int pos = 64 * n + lane, r = pos >> 2;
+    mroff[n] = (uint32_t)(min(wk.row0 + r, p.Sq - 1) - mrow_b) * (uint32_t)p.m_ss;
+    mcol[n] = 16 * ((pos & 3) ^ ((r >> 2) & 3));
+  }
+  const int wv = (int)threadIdx.x >> 6;
+  auto mslot = [&](int j) __attribute__((always_inline)) -> uint8_t* { return s_mring + (wv * 3 + j % 3) * MSLOT; };
+  auto mask_copy = [&](int j) __attribute__((always_inline)) {
+    if constexpr (MLDS) {
+      const int kstart = __builtin_amdgcn_readfirstlane(tile_start(j));
+      const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr_of(mslot(j)));
+#pragma unroll
+      for (int n = 0; n < MCOPY; ++n)
+        lds_copy16(mbase + kstart, mroff[n] + (uint32_t)min(mcol[n], p.Skv - 16 - kstart), l0 + n * 1024);
+    }
+  };
+  // Mask words of tile j from LDS: key half kt of the lane's row is chunk
+  // 2 kt + h (keys 32 kt + 16 h .. +15 in the permuted tile layout).
+  auto mask_read = [&](int j) __attribute__((always_inline)) {
+    if constexpr (MLDS) {
+      const uint8_t* row = mslot(j) + c * BNT;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        const u32x4 w = *(const __attribute__((address_space(3))) u32x4*)lds_ptr(
+            lds_addr_of(row) + 16 * ((2 * kt + h) ^ ((c >> 2) & 3)));
+#pragma unroll
+        for (int g = 0; g < 4; ++g) mwords[0][kt][g] = w[g];
+      }
+    }
+  };
   auto mask_pin = [&]() __attribute__((always_inline)) {
     if constexpr (MASK) {
 #pragma unroll
@@ -310,12 +364,12 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
       const int k0 = kstart + kt * 32;
       // Key half kt entirely visible in every row: only the mask bytes apply.
       if (!MASK && k0 + 31 <= lim_lo) continue;
-      // Element i holds key k0 + 4 h + 8 (i / 4) + i % 4: visible iff
-      // 8 (i / 4) + i % 4 <= r.
-      const int r = k0 + 31 <= lim_lo ? 31 : lim - k0 - 4 * h;
+      // Element i holds key k0 + 4 h + 8 (i / 4) + i % 4 (permuted tiles:
+      // k0 + 16 h + i): visible iff 8 (i / 4) + i % 4 <= r (i <= r).
+      const int r = k0 + 31 <= lim_lo ? 31 : lim - k0 - (MLDS ? 16 : 4) * h;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        bool ok = 8 * (i >> 2) + (i & 3) <= r;
+        bool ok = (MLDS ? i : 8 * (i >> 2) + (i & 3)) <= r;
         if constexpr (MASK) ok = ok && ((mwords[b][kt][i >> 2] >> (8 * (i & 3))) & 0xffu) == 0u;
         if (!ok) sv[kt][i] = -INFINITY;
       }
@@ -458,6 +512,7 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     }
     if (m + 2 < n_iter) {
       vcopy.issue(tile_start(m + 2), wk.Lk, s_vring + ((m + 2) % 3) * TILE);
+      mask_copy(m + 2);
       any = true;
     }
     return any;
@@ -476,10 +531,12 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   if (n_iter > 0) {
     kcopy.issue(tile_start(0), wk.Lk, s_kring);
     vcopy.issue(tile_start(0), wk.Lk, s_vring);
+    mask_copy(0);
   }
   if (n_iter > 1) {
     kcopy.issue(tile_start(1), wk.Lk, s_kring + TILE);
     vcopy.issue(tile_start(1), wk.Lk, s_vring + TILE);
+    mask_copy(1);
   }
   if (n_iter > 2) kcopy.issue(tile_start(2), wk.Lk, s_kring + 2 * TILE);
   // Q^T operands (B operand of S^T = K Q^T, kept in AGPRs): block b, lane
@@ -522,7 +579,10 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   // phase; the first reader of K_{j+3} / V_{j+2} is M(j+2), two phases later.
   const int grp = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) / (NW / 2));
   if (grp == 1) end_phase(false);
-  if (n_act > 0) mask_load(0);
+  if (n_act > 0) {
+    mask_load(0);
+    mask_read(0);
+  }
   mprefetch(s_kring, s_vring, false);
   mphase(sc, pp[0], s_kring, s_vring, false);  // M(-1): S(0)
   mask_pin();
@@ -544,6 +604,9 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
     // M(j): global phase 2j+2 (group 0) or 2j+3 (group 1).
     if (j + 1 < n_act) mask_load(j + 1);
     mphase(sc, pp[0], kt_buf, vt_buf, true);
+    // Mask tile j+1 has been in LDS since the end of V(j) (this wave's own
+    // copies, issued in M(j-1), are waited for there).
+    if (j + 1 < n_act) mask_read(j + 1);
     mask_pin();
     end_phase(copies(j));
   }
@@ -636,13 +699,15 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
 #define FA_FWD16_KERNEL(TN, T, D, NW, QT, HP, C, M, S, X)                                              \
   extern "C" __global__ void __launch_bounds__(NW * 64, 1)                                             \
       fa_fwd16_##TN##_d##D##_w##NW##_q##QT##_h##HP##_c##C##m##M##s##S##x##X(const fa::FwdParams p) {  \
-    fa::fwd16_body<fa::T, D, NW, QT, HP, C != 0, M != 0, S != 0, X>(p);                                 \
+    fa::fwd16_body<fa::T, D, NW, QT, HP, C != 0, M, S != 0, X>(p);                                      \
   }
 #define FA_FWD16_DTYPE_D(TN, T, D)                    \
   FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 0, 0, 0, 0)      \
   FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 0, 1, 0, 0)      \
   FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 1, 0, 0, 0)      \
   FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 1, 1, 0, 0)      \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 0, 2, 0, 0)      \
+  FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 1, 2, 0, 0)      \
   FA_FWD16_KERNEL(TN, T, D, 8, 1, 2, 0, 0, 1, 0)      \
   FA_FWD16_KERNEL(TN, T, D, 4, 1, 1, 0, 0, 1, 0)      \
   FA_FWD16_KERNEL(TN, T, D, 8, 1, 1, 0, 0, 0, 1)      \

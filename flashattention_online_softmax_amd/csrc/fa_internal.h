@@ -32,6 +32,7 @@ struct FwdParams {
   int32_t max_sel;         // block-sparse slots per query block
   int32_t mask_vec4;       // 1: mask rows may be read 4 bytes at a time
   int32_t mask_vec16;      // 1: ... and 16 bytes at a time
+  int32_t mask_lds;        // 1: ... and mask tiles may be copied to LDS in 16-byte chunks
   int32_t n_mblocks;       // query blocks per head
   int32_t n_hgroups;       // head groups per KV head (G / heads per workgroup)
   float scale;             // softmax scale (LSE is reported in these units)

@@ -26,6 +26,16 @@ __device__ __forceinline__ int vswz(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
+// Key held by LDS tile row `slot` in the key-permuted tile layout of the
+// kernels with LDS-staged boolean masks. The S^T accumulator of a 32-key half
+// gives lane (h, c) the rows 8 g + 4 h + i (g, i in 0..3); storing key
+// 16 h + 4 g + i in row 8 g + 4 h + i hands that lane the 16 consecutive keys
+// 16 h .. 16 h + 15, whose mask bytes are one 16-byte chunk. V tiles use the
+// same rows, so P V pairs every p with its own key.
+__device__ __forceinline__ int perm_key(int slot) {
+  return (slot & ~31) | (((slot >> 2) & 1) << 4) | (((slot >> 3) & 3) << 2) | (slot & 3);
+}
+
 struct Work {
   int b, hkv, hq, wg_row0, row0, Lq, Lk;
   int qoff, koff;  // packed layout: first row of the batch in q / k (else 0)

@@ -79,6 +79,52 @@ def test_mask_aligned_rows(causal):
     run_dense("mask4d_aligned_causal%d" % causal, q, k, v, 1 / math.sqrt(128), causal, m4, thr=8.0)
 
 
+def _mask_view(mask_dev, pad):
+    """The same mask bytes in storage whose rows are `pad` bytes longer, so
+    that rows are no longer 16-byte chunks (pad 1: byte loads, pad 4: 4-byte
+    loads into registers)."""
+    *lead, sq, skv = mask_dev.shape
+    big = torch.ones(*lead, sq, skv + pad, dtype=torch.uint8, device=mask_dev.device)
+    big[..., :skv] = mask_dev
+    return big[..., :skv]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mask_lds_staged(D, causal):
+    # Masks whose rows are whole 16-byte chunks are staged through LDS with
+    # the K/V tiles (permuted key order inside each 32-key half); any other
+    # mask goes through registers. Both must match the oracle, with per-batch
+    # lengths, Sq != Skv (rows without keys under the causal mask), a partial
+    # last tile, rows past Sq in the last workgroup, a fully masked row and
+    # per-head masks broadcast over the batch.
+    g, q, k, v = synth.dense_inputs(31 + D + causal, 2, 4, 2, 290, 272, D, D, "f16")
+    m = torch.from_numpy((g.random((1, 4, 290, 272)) < 0.25).astype(np.uint8))
+    m[0, 2, 11] = 1
+    sq = torch.tensor([290, 203], dtype=torch.int32)
+    sk = torch.tensor([272, 144], dtype=torch.int32)
+    scale = 1 / math.sqrt(D)
+    run_dense("mask_lds_D%d_causal%d" % (D, causal), q, k, v, scale, causal, m, sq, sk)
+    qg, kg, vg, mg, sqg, skg = gpu(q, k, v, m, sq, sk)
+    outs = []
+    for pad in (0, 1, 4):
+        mm = mg if pad == 0 else _mask_view(mg, pad)
+        outs.append(fa.fa_fwd(qg, kg, vg, scale=scale, causal=causal, mask=mm, seqlens_q=sqg, seqlens_k=skg))
+    torch.cuda.synchronize()
+    kw = dict(scale=f32(scale), causal=causal, mask=m, seqlens_q=sq, seqlens_k=sk)
+    o_ref, lse_ref = oracle.attn_dense(q, k, v, **kw)
+    o_abs, _ = oracle.attn_dense(q, k, absv(v), **kw)
+    for pad, (o, lse) in zip((0, 1, 4), outs):
+        check("mask_lds_D%d_causal%d_pad%d" % (D, causal, pad), o, lse, o_ref, lse_ref, q.dtype, o_abs)
+    # LDS-staged and register paths sum the keys of a half in different
+    # orders: they agree to rounding, and exactly on rows without keys.
+    (o0, l0), (o1, l1) = outs[0], outs[1]
+    assert (o0.float() - o1.float()).abs().max().item() <= 2 ** -9 * max(1.0, o1.float().abs().max().item())
+    fin = torch.isfinite(l1)
+    assert torch.equal(fin, torch.isfinite(l0))
+    assert (l0[fin] - l1[fin]).abs().max().item() <= 1e-5
+
+
 def test_growing_scores_rescale_paths():
     # Scores that keep growing along the keys force a rescale on every tile
     # with the exact max and on some tiles with the lazy one; both must match.
