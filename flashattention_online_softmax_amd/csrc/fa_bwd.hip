@@ -252,28 +252,47 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       lr[4 * j] = l4.x; lr[4 * j + 1] = l4.y; lr[4 * j + 2] = l4.z; lr[4 * j + 3] = l4.w;
     }
     f32x16 sv = {}, dp = {};
-#pragma unroll
-    for (int ks = 0; ks < BD / 16; ++ks) sv = T::mfma(row_op(sQr, ks), kop[ks], sv);
     if (kwave) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float4 d4 = *(const float4*)(sD + 8 * j + 4 * h);
         dr[4 * j] = d4.x; dr[4 * j + 1] = d4.y; dr[4 * j + 2] = d4.z; dr[4 * j + 3] = d4.w;
       }
+      // S and dP chains interleaved: each MFMA's predecessor in the issue
+      // order is independent of it.
 #pragma unroll
-      for (int ks = 0; ks < BD / 16; ++ks) dp = T::mfma(row_op(sOr, ks), vop[ks], dp);
+      for (int ks = 0; ks < BD / 16; ++ks) {
+        sv = T::mfma(row_op(sQr, ks), kop[ks], sv);
+        dp = T::mfma(row_op(sOr, ks), vop[ks], dp);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < BD / 16; ++ks) sv = T::mfma(row_op(sQr, ks), kop[ks], sv);
     }
     // Element i: query row q0 + r, r = 8 (i / 4) + 4 h + i % 4; key `key`.
+    // A block every row and key of which exist and (causal) whose last key
+    // the first row sees needs no per-element test.
+    const int kw0 = k0 + 32 * (w & 3);
+    const bool inside = !MASK && __builtin_amdgcn_readfirstlane(
+                                     (kw0 + 31 < Lk && q0 + TR <= Lq && (!CAUSAL || kw0 + 31 <= q0 + diag)) ? 1 : 0);
     f32x16 bm;  // P (V waves) or dS (K waves)
+    if (inside) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 8 * (i >> 2) + 4 * h + (i & 3);
-      const int qi = q0 + r;
-      bool ok = key < Lk && qi < Lq;
-      if (CAUSAL) ok = ok && key <= qi + diag;
-      if (MASK) ok = ok && mk[(int64_t)qi * p.m_ss] == 0;
-      const float pv = ok ? fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, -lr[i])) : 0.f;
-      bm[i] = kwave ? pv * (dp[i] - dr[i]) : pv;
+      for (int i = 0; i < 16; ++i) {
+        const float pv = fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, -lr[i]));
+        bm[i] = kwave ? pv * (dp[i] - dr[i]) : pv;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+        const int qi = q0 + r;
+        bool ok = key < Lk && qi < Lq;
+        if (CAUSAL) ok = ok && key <= qi + diag;
+        if (MASK) ok = ok && mk[(int64_t)qi * p.m_ss] == 0;
+        const float pv = ok ? fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, -lr[i])) : 0.f;
+        bm[i] = kwave ? pv * (dp[i] - dr[i]) : pv;
+      }
     }
     const uint16_t* at = kwave ? sQt : sOt;  // Q^T for dK, dO^T for dV
 #pragma unroll
@@ -363,15 +382,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       dp0 = T::mfma(row_op(sVr, ks), dop[ks], dp0);
     }
     // Element i: key j0 + r, r = 8 (i / 4) + 4 h + i % 4; query row qi.
+    // A block whose keys all exist and are seen by every row of the wave
+    // needs no per-element test.
+    const int qw0 = q0 + 32 * w;
+    const bool inside = !MASK && __builtin_amdgcn_readfirstlane(
+                                     (j0 + TR <= Lk && qw0 + 31 < Lq && (!CAUSAL || j0 + 31 <= qw0 + diag)) ? 1 : 0);
     f32x16 dsm;
+    if (inside) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kj = j0 + 8 * (i >> 2) + 4 * h + (i & 3);
-      bool ok = kj < Lk && qi < Lq;
-      if (CAUSAL) ok = ok && kj <= qi + diag;
-      if (MASK) ok = ok && mq[kj] == 0;
-      const float pv = ok ? fast_exp2(__builtin_fmaf(s0[i], p.scale_log2, -l2)) : 0.f;
-      dsm[i] = pv * (dp0[i] - del);
+      for (int i = 0; i < 16; ++i) dsm[i] = fast_exp2(__builtin_fmaf(s0[i], p.scale_log2, -l2)) * (dp0[i] - del);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kj = j0 + 8 * (i >> 2) + 4 * h + (i & 3);
+        bool ok = kj < Lk && qi < Lq;
+        if (CAUSAL) ok = ok && kj <= qi + diag;
+        if (MASK) ok = ok && mq[kj] == 0;
+        const float pv = ok ? fast_exp2(__builtin_fmaf(s0[i], p.scale_log2, -l2)) : 0.f;
+        dsm[i] = pv * (dp0[i] - del);
+      }
     }
 #pragma unroll
     for (int ks = 0; ks < TR / 16; ++ks) {
