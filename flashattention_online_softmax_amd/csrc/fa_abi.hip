@@ -417,6 +417,9 @@ fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
   if ((s = check_dtype("dk", dk, q->dtype)) != FA_OK) return s;
   if ((s = check_dtype("dv", dv, q->dtype)) != FA_OK) return s;
   if ((s = check_dtype("delta", delta, FA_F32)) != FA_OK) return s;
+  // Q and dO tiles are fetched with 32-bit per-lane offsets from the tile start.
+  if (q->stride[2] > (1 << 22) || dout->stride[2] > (1 << 22))
+    return fail(FA_ERR_UNSUPPORTED, "q/dout row stride above 2^22 elements is not supported");
   for (int i = 0; i < 4; ++i) {
     if (dout->shape[i] != o->shape[i]) return fail(FA_ERR_SHAPE, "dout must be shaped like o");
     if (dq->shape[i] != q->shape[i]) return fail(FA_ERR_SHAPE, "dq must be shaped like q");

@@ -24,12 +24,13 @@
 // The operands read transposed (dO^T, Q^T, K^T) come from row-major LDS tiles
 // through ds_read_b64_tr_b16, in the key (query) order in which the
 // accumulator holds P and dS, so the contraction pairs the right elements.
-// Each LDS tile is 32 rows x 128, stored twice when it is read both ways:
-// 16-byte chunks XOR-swizzled by row & 15 for the row reads and by
-// 4 (row & 3) for the transposing reads.
+// Each LDS tile is 32 rows x 128, stored once with its 16-byte chunks
+// XOR-swizzled so that both the row reads and the transposing reads are free
+// of bank conflicts (bsw below).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_asm.h"
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -41,14 +42,19 @@ constexpr int TR = 32;     // rows of an LDS tile
 constexpr int NWB = 4;     // waves per workgroup
 constexpr int BLK = 32 * NWB;  // keys (dkdv) or query rows (dq) per workgroup
 
-__device__ __forceinline__ int rsw(int row, int ch) { return ch ^ (row & 15); }
-__device__ __forceinline__ int tsw(int row, int ch) { return ch ^ ((row & 3) << 2); }
+// One chunk swizzle serves both read patterns of a tile: the row reads
+// (16 consecutive rows, one chunk each, per 256 bytes) see 16 distinct
+// chunk positions since the XOR term is a bijection of row & 15, and the
+// transposing reads (4 consecutive rows x 4 consecutive chunks) see 16
+// distinct positions since bits 2..3 of the XOR term differ between the
+// four rows of an aligned group.
+__device__ __forceinline__ int bsw(int row, int ch) { return ch ^ (((row & 3) << 2) | ((row >> 2) & 3)); }
 
 // Cooperative copy of rows r0 .. r0+31 (clamped to n - 1; n >= 1) of a
 // row-major [*, 128] 16-bit matrix into LDS, in two halves: fetch_tile loads
 // this thread's two 16-byte chunks into registers (issued before the
 // previous tile's MFMAs, so the load latency hides behind them), put_tile
-// stores them into LDS once per requested swizzle.
+// stores them into LDS in the swizzled layout.
 template <int NT = 64 * NWB>
 struct TileRegs {
   static constexpr int N = (TR * BD / 8) / NT;  // 16-byte chunks per thread
@@ -65,20 +71,19 @@ __device__ __forceinline__ void fetch_tile(TileRegs<NT>& r, const uint16_t* src,
   }
 }
 template <int NT>
-__device__ __forceinline__ void put_tile(const TileRegs<NT>& r, uint16_t* dst_r, uint16_t* dst_t) {
+__device__ __forceinline__ void put_tile(const TileRegs<NT>& r, uint16_t* dst) {
 #pragma unroll
   for (int u = 0; u < TileRegs<NT>::N; ++u) {
     const int id = (int)threadIdx.x + u * NT;
     const int row = id >> 4, ch = id & 15;
-    if (dst_r) *(u32x4*)(dst_r + row * BD + rsw(row, ch) * 8) = r.v[u];
-    if (dst_t) *(u32x4*)(dst_t + row * BD + tsw(row, ch) * 8) = r.v[u];
+    *(u32x4*)(dst + row * BD + bsw(row, ch) * 8) = r.v[u];
   }
 }
 
 // A operand "rows": lane (c, h) holds tile row c, columns 16 ks + 8 h .. +7.
 __device__ __forceinline__ u32x4 row_op(const uint16_t* t, int ks) {
   const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
-  return *(const u32x4*)(t + c * BD + rsw(c, 2 * ks + h) * 8);
+  return *(const u32x4*)(t + c * BD + bsw(c, 2 * ks + h) * 8);
 }
 // A operand "transposed": M index = tile column 32 dt + (lane & 31); the 8 k
 // values of lane half h are tile rows 16 ks + 4 h + 0..3 and 16 ks + 8 + 4 h
@@ -87,9 +92,9 @@ __device__ __forceinline__ u32x4 tr_op(const uint16_t* t, int dt, int ks) {
   const int lane = threadIdx.x & 63, h = lane >> 5;
   const int vrow = 4 * h + ((lane & 15) >> 2);
   const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const uint16_t* p = t + (16 * ks + vrow) * BD + tsw(vrow, col >> 3) * 8 + (col & 7);
-  const u32x2 lo = lds_read_tr16(p);
-  const u32x2 hi = lds_read_tr16(p + 8 * BD);
+  const int r0 = 16 * ks + vrow, r1 = r0 + 8;
+  const u32x2 lo = lds_read_tr16(t + r0 * BD + bsw(r0, col >> 3) * 8 + (col & 7));
+  const u32x2 hi = lds_read_tr16(t + r1 * BD + bsw(r1, col >> 3) * 8 + (col & 7));
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 // B operand from global memory: lane (c, h) holds row r of a row-major
@@ -163,13 +168,20 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 // Two waves per key group of 32: wave g (0..3) computes S, P and dV^T +=
 // dO^T P; wave g + 4 computes S, dP, dS and dK^T += Q^T dS. Each holds one
 // gradient's accumulators, so both fit 256 registers and share a SIMD.
+//
+// A step's Q and dO tiles are copied HBM -> LDS by LDS-DMA (no register
+// staging) into a three-deep ring, by the dV waves, which have less MFMA
+// work per step than the dK waves: at the end of step it, dV wave g issues
+// 4 KB of the tiles of step it + 2 (tile g / 2, chunk positions
+// 64 (4 (g % 2) + n) + lane for n = 0..3; the swizzle is an involution, so a
+// lane fetches the logical chunk its position holds) and waits for its
+// copies of step it + 1; the barrier at the top of step it + 1 publishes
+// them.
 template <class T, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NT = 512;
-  // Two buffers of the four tile copies (Q rows, Q^T, dO rows, dO^T) and of
-  // the rows' LSE / Delta: tile it + 1 is stored while tile it is read.
-  __shared__ __attribute__((aligned(16))) uint16_t sbuf[2][4][TR * BD];
-  __shared__ __attribute__((aligned(16))) float sLD[2][2][TR];
+  constexpr int NB = 3;  // ring depth
+  __shared__ __attribute__((aligned(16))) uint16_t sbuf[NB][2][TR * BD];
+  __shared__ __attribute__((aligned(16))) float sLD[NB][2][TR];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
   const bool kwave = __builtin_amdgcn_readfirstlane(w) >= 4;  // dK (else dV)
   // Workgroups in order of decreasing work (under the causal mask the first
@@ -195,17 +207,36 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   // Query rows that can see a key of this block: i >= k0 - diag (causal).
   const int qfirst = CAUSAL ? max(0, k0 - diag) : 0;
   const int nqt = (k0 < Lk && Lq > qfirst) ? (Lq - qfirst + TR - 1) / TR : 0;
-  // The sweep: step it = (query head hq, query tile t) of the group, tiles
-  // fetched one step ahead into registers.
+  // The sweep: step it = (query head hq, query tile t) of the group.
   const int nsteps = p.G * nqt;
-  TileRegs<NT> rq, ro;
-  float rl = 0.f, rd = 0.f;
-  auto fetch = [&](int it) __attribute__((always_inline)) {
+  // This dV wave's share of a step's copies: tile (w & 3) / 2 (0 Q, 1 dO),
+  // per instruction the tile row and the byte offset of the logical chunk.
+  const bool c_do = (w & 2) != 0;
+  int crow[4];
+  uint32_t cchunk[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int pos = 64 * (4 * (w & 1) + n) + lane, row = pos >> 4;
+    crow[n] = row;
+    cchunk[n] = (uint32_t)(bsw(row, pos & 15) * 16);
+  }
+  const int64_t c_ss = c_do ? p.do_ss : p.q_ss;
+  const uint32_t c_rb = (uint32_t)c_ss * 2u;
+  auto dma = [&](int it) __attribute__((always_inline)) {
     const int hq = hkv * p.G + it / nqt, q0 = qfirst + (it % nqt) * TR;
-    const int64_t bh = (int64_t)b * p.Hq + hq;
-    fetch_tile(rq, (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh, p.q_ss, q0, p.Sq);
-    fetch_tile(ro, (const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hq * p.do_sh, p.do_ss, q0, p.Sq);
+    const uint16_t* base = c_do ? (const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hq * p.do_sh
+                                : (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh;
+    base += (int64_t)q0 * c_ss;
+    const int rmax = p.Sq - 1 - q0;  // rows past Sq fetch row Sq - 1
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr_of(sbuf[it % NB][c_do ? 1 : 0]) + (w & 1) * 4096);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) lds_copy16(base, (uint32_t)min(crow[n], rmax) * c_rb + cchunk[n], l0 + n * 1024);
+  };
+  float rl = 0.f, rd = 0.f;
+  auto fetch_ld = [&](int it) __attribute__((always_inline)) {
     if (threadIdx.x < TR) {
+      const int hq = hkv * p.G + it / nqt, q0 = qfirst + (it % nqt) * TR;
+      const int64_t bh = (int64_t)b * p.Hq + hq;
       const int i = q0 + threadIdx.x;
       const float l = i < p.Sq ? p.lse[bh * p.Sq + i] : -INFINITY;
       // rows without keys (LSE = -inf) and padding rows get P = 0
@@ -213,37 +244,33 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       rd = i < p.Sq ? p.delta[bh * p.Sq + i] : 0.f;
     }
   };
-  auto put = [&](int it) __attribute__((always_inline)) {
-    uint16_t(&bf)[4][TR * BD] = sbuf[it & 1];
-    put_tile(rq, bf[0], bf[1]);
-    put_tile(ro, bf[2], bf[3]);
+  auto put_ld = [&](int it) __attribute__((always_inline)) {
     if (threadIdx.x < TR) {
-      sLD[it & 1][0][threadIdx.x] = rl;
-      sLD[it & 1][1][threadIdx.x] = rd;
+      sLD[it % NB][0][threadIdx.x] = rl;
+      sLD[it % NB][1][threadIdx.x] = rd;
     }
   };
   if (nsteps > 0) {
-    fetch(0);
-    put(0);
-    if (nsteps > 1) fetch(1);
+    if (!kwave) {
+      dma(0);
+      if (nsteps > 1) dma(1);
+    }
+    fetch_ld(0);
+    put_ld(0);
+    if (nsteps > 1) fetch_ld(1);
+    wait_vmem();
   }
   for (int it = 0; it < nsteps; ++it) {
     const int q0 = qfirst + (it % nqt) * TR;
     // mask bytes of this step's query head, the lane's key column
     const uint8_t* mk = MASK ? p.mask + (int64_t)b * p.m_sb + (int64_t)(hkv * p.G + it / nqt) * p.m_sh + key : nullptr;
-    // One barrier per tile: tile it is stored (by every wave) and every wave
-    // is done reading tile it - 1, whose buffer tile it + 1 now takes.
+    // Tiles and LSE / Delta of step it are in LDS, and every wave is done
+    // with step it - 1.
     __syncthreads();
-    if (it + 1 < nsteps) {
-      put(it + 1);
-      if (it + 2 < nsteps) fetch(it + 2);
-    }
-    const uint16_t* sQr = sbuf[it & 1][0];
-    const uint16_t* sQt = sbuf[it & 1][1];
-    const uint16_t* sOr = sbuf[it & 1][2];
-    const uint16_t* sOt = sbuf[it & 1][3];
-    const float* sL = sLD[it & 1][0];
-    const float* sD = sLD[it & 1][1];
+    const uint16_t* sQ = sbuf[it % NB][0];
+    const uint16_t* sO = sbuf[it % NB][1];
+    const float* sL = sLD[it % NB][0];
+    const float* sD = sLD[it % NB][1];
     // LSE (and Delta) of the lane's 16 rows: 4 groups of 4 consecutive rows.
     float lr[16], dr[16];
 #pragma unroll
@@ -262,12 +289,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       // order is independent of it.
 #pragma unroll
       for (int ks = 0; ks < BD / 16; ++ks) {
-        sv = T::mfma(row_op(sQr, ks), kop[ks], sv);
-        dp = T::mfma(row_op(sOr, ks), vop[ks], dp);
+        sv = T::mfma(row_op(sQ, ks), kop[ks], sv);
+        dp = T::mfma(row_op(sO, ks), vop[ks], dp);
       }
     } else {
 #pragma unroll
-      for (int ks = 0; ks < BD / 16; ++ks) sv = T::mfma(row_op(sQr, ks), kop[ks], sv);
+      for (int ks = 0; ks < BD / 16; ++ks) sv = T::mfma(row_op(sQ, ks), kop[ks], sv);
     }
     // Element i: query row q0 + r, r = 8 (i / 4) + 4 h + i % 4; key `key`.
     // A block every row and key of which exist and (causal) whose last key
@@ -294,12 +321,26 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
         bm[i] = kwave ? pv * (dp[i] - dr[i]) : pv;
       }
     }
-    const uint16_t* at = kwave ? sQt : sOt;  // Q^T for dK, dO^T for dV
+    const uint16_t* at = kwave ? sQ : sO;  // Q^T for dK, dO^T for dV
 #pragma unroll
     for (int ks = 0; ks < TR / 16; ++ks) {
       const u32x4 bb = pack_b<T>(bm, ks);
 #pragma unroll
       for (int dt = 0; dt < BD / 32; ++dt) acc[dt] = T::mfma(tr_op(at, dt, ks), bb, acc[dt]);
+    }
+    if (!kwave) {
+      // LSE / Delta of step it + 1 into their ring slot (step it - 2 is long
+      // done), the copies of step it + 2 into the slot of step it - 1 (every
+      // wave passed the barrier of step it), then this wave's copies of step
+      // it + 1 complete (those of step it + 2 may still fly).
+      if (it + 1 < nsteps) put_ld(it + 1);
+      if (it + 2 < nsteps) {
+        dma(it + 2);
+        wait_vmem_below<4>();
+        fetch_ld(it + 2);
+      } else {
+        wait_vmem();
+      }
     }
   }
   if (key < p.Skv) {
@@ -312,8 +353,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
 
 template <class T, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
-  // Two buffers of the three tile copies (K rows, K^T, V rows).
-  __shared__ __attribute__((aligned(16))) uint16_t sbuf[2][3][TR * BD];
+  // Two buffers of the K and V tiles (K read both ways, V by rows).
+  __shared__ __attribute__((aligned(16))) uint16_t sbuf[2][2][TR * BD];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
   // Workgroups in order of decreasing work (under the causal mask the last
   // query blocks see the most keys), the (batch, head) index fastest.
@@ -353,8 +394,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
     fetch_tile(rv, vg, p.v_ss, t * TR, p.Skv);
   };
   auto put = [&](int t) __attribute__((always_inline)) {
-    put_tile(rk, sbuf[t & 1][0], sbuf[t & 1][1]);
-    put_tile(rv, sbuf[t & 1][2], nullptr);
+    put_tile(rk, sbuf[t & 1][0]);
+    put_tile(rv, sbuf[t & 1][1]);
   };
   if (nkt > 0) {
     fetch(0);
@@ -371,8 +412,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       if (t + 2 < nkt) fetch(t + 2);
     }
     const uint16_t* sKr = sbuf[t & 1][0];
-    const uint16_t* sKt = sbuf[t & 1][1];
-    const uint16_t* sVr = sbuf[t & 1][2];
+    const uint16_t* sKt = sKr;
+    const uint16_t* sVr = sbuf[t & 1][1];
     // Two waves share each SIMD here (the register budget is 256), so the
     // operands are read as the MFMAs consume them.
     f32x16 s0 = {}, dp0 = {};
