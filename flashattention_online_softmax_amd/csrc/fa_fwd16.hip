@@ -131,6 +131,34 @@ __device__ __forceinline__ void fwd16_body(const FwdParams& p) {
   }
   // Rows of this head: Sq, or the batch's own length in the packed layout.
   const int rlim = XM == 1 ? wk.Lq : p.Sq;
+  if constexpr (XM == 0) {
+    // A query block wholly past the batch's length: its rows (padding up to
+    // Sq) get O = 0 and LSE = -inf without the tile pipeline.
+    if (wk.wg_row0 >= wk.Lq) {
+      constexpr int CPR = D / 8, RPI = 64 / CPR;  // 16-byte chunks per row, rows per store
+      uint16_t* og0 = (uint16_t*)p.o + wk.b * p.o_sb + wk.hq * p.o_sh;
+#pragma unroll
+      for (int k = 0; k < QT * 32 / RPI; ++k) {
+        const int qrow = wk.row0 + k * RPI + lane / CPR;
+        if (qrow < p.Sq) *(u32x4*)(og0 + (int64_t)qrow * p.o_ss + 8 * (lane % CPR)) = u32x4{0u, 0u, 0u, 0u};
+      }
+      if (p.o_lo) {
+        constexpr int FPR = D / 4, FRI = 64 / FPR;  // float4 per o_lo row, rows per store
+        float* l0 = p.o_lo + wk.b * p.ol_sb + wk.hq * p.ol_sh;
+#pragma unroll
+        for (int k = 0; k < QT * 32 / FRI; ++k) {
+          const int qrow = wk.row0 + k * FRI + lane / FPR;
+          if (qrow < p.Sq) *(float4*)(l0 + (int64_t)qrow * p.ol_ss + 4 * (lane % FPR)) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < QT; ++b) {
+        const int qrow = wk.row0 + 32 * b + c;
+        if (h == 0 && qrow < p.Sq) p.lse[wk.b * p.lse_sb + wk.hq * p.lse_sh + (int64_t)qrow * p.lse_ss] = -INFINITY;
+      }
+      return;
+    }
+  }
 
   int n_iter;
   if (SPARSE)

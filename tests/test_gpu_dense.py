@@ -348,6 +348,31 @@ def test_o_lo_dense(dtype, causal):
     check_o_lo("o_lo_%s_causal%d" % (dtype, causal), o, lo, o_ref, o_abs, q.dtype, 300)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_padded_query_blocks_with_o_lo(D):
+    # A short batch leaves whole 256-row query blocks past its length: their
+    # rows (padding up to Sq) get O = 0, LSE = -inf and o_lo = 0 without the
+    # tile pipeline; the other rows match the oracle. Poisoned outputs show
+    # any row that is not written.
+    _, q, k, v = synth.dense_inputs(520 + D, 2, 4, 2, 700, 650, D, D, "bf16")
+    sq = torch.tensor([700, 190], dtype=torch.int32)
+    sk = torch.tensor([650, 120], dtype=torch.int32)
+    qg, kg, vg, sqg, skg = gpu(q, k, v, sq, sk)
+    o = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
+    lse = torch.full(q.shape[:3], 7.0, dtype=torch.float32, device="cuda")
+    lo = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    for causal in (False, True):
+        fa.fa_fwd(qg, kg, vg, scale=0.1, causal=causal, seqlens_q=sqg, seqlens_k=skg, out=o, lse=lse, o_lo=lo)
+        torch.cuda.synchronize()
+        assert torch.all(o[1, :, 190:] == 0) and torch.all(lo[1, :, 190:] == 0)
+        assert torch.all(lse[1, :, 190:] == -math.inf)
+        assert not torch.isnan(o).any() and not torch.isnan(lo).any()
+        kw = dict(scale=f32(0.1), causal=causal, seqlens_q=sq, seqlens_k=sk)
+        o_ref, lse_ref = oracle.attn_dense(q, k, v, **kw)
+        o_abs, _ = oracle.attn_dense(q, k, absv(v), **kw)
+        check("padded_blocks_D%d_causal%d" % (D, causal), o, lse, o_ref, lse_ref, q.dtype, o_abs)
+
+
 def test_o_lo_full_causal_bf16_s4096():
     w = synth.workload("causal_bf16_s4096")
     q, k, v = w["q"], w["k"], w["v"]
