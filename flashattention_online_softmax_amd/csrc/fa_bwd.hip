@@ -222,20 +222,30 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   }
   const int64_t c_ss = c_do ? p.do_ss : p.q_ss;
   const uint32_t c_rb = (uint32_t)c_ss * 2u;
-  auto dma = [&](int it) __attribute__((always_inline)) {
-    const int hq = hkv * p.G + it / nqt, q0 = qfirst + (it % nqt) * TR;
+  // Step it = (query head hkv G + it / nqt, tile it % nqt), tracked without
+  // divisions: (h, t) of the step computed and of the step two ahead, and
+  // their ring slots.
+  int h_cur = 0, t_cur = 0, h_ahd = 0, t_ahd = 0, slot = 0;
+  auto advance = [&](int& hh, int& tt) __attribute__((always_inline)) {
+    if (++tt == nqt) {
+      tt = 0;
+      ++hh;
+    }
+  };
+  auto dma = [&](int hh, int tt, int sl) __attribute__((always_inline)) {
+    const int hq = hkv * p.G + hh, q0 = qfirst + tt * TR;
     const uint16_t* base = c_do ? (const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hq * p.do_sh
                                 : (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh;
     base += (int64_t)q0 * c_ss;
     const int rmax = p.Sq - 1 - q0;  // rows past Sq fetch row Sq - 1
-    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr_of(sbuf[it % NB][c_do ? 1 : 0]) + (w & 1) * 4096);
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr_of(sbuf[sl][c_do ? 1 : 0]) + (w & 1) * 4096);
 #pragma unroll
     for (int n = 0; n < 4; ++n) lds_copy16(base, (uint32_t)min(crow[n], rmax) * c_rb + cchunk[n], l0 + n * 1024);
   };
   float rl = 0.f, rd = 0.f;
-  auto fetch_ld = [&](int it) __attribute__((always_inline)) {
+  auto fetch_ld = [&](int hh, int tt) __attribute__((always_inline)) {
     if (threadIdx.x < TR) {
-      const int hq = hkv * p.G + it / nqt, q0 = qfirst + (it % nqt) * TR;
+      const int hq = hkv * p.G + hh, q0 = qfirst + tt * TR;
       const int64_t bh = (int64_t)b * p.Hq + hq;
       const int i = q0 + threadIdx.x;
       const float l = i < p.Sq ? p.lse[bh * p.Sq + i] : -INFINITY;
@@ -244,33 +254,35 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       rd = i < p.Sq ? p.delta[bh * p.Sq + i] : 0.f;
     }
   };
-  auto put_ld = [&](int it) __attribute__((always_inline)) {
+  auto put_ld = [&](int sl) __attribute__((always_inline)) {
     if (threadIdx.x < TR) {
-      sLD[it % NB][0][threadIdx.x] = rl;
-      sLD[it % NB][1][threadIdx.x] = rd;
+      sLD[sl][0][threadIdx.x] = rl;
+      sLD[sl][1][threadIdx.x] = rd;
     }
   };
   if (nsteps > 0) {
-    if (!kwave) {
-      dma(0);
-      if (nsteps > 1) dma(1);
-    }
-    fetch_ld(0);
+    if (!kwave) dma(0, 0, 0);
+    fetch_ld(0, 0);
     put_ld(0);
-    if (nsteps > 1) fetch_ld(1);
+    advance(h_ahd, t_ahd);
+    if (nsteps > 1) {
+      if (!kwave) dma(h_ahd, t_ahd, 1);
+      fetch_ld(h_ahd, t_ahd);
+    }
+    advance(h_ahd, t_ahd);  // now step 2
     wait_vmem();
   }
   for (int it = 0; it < nsteps; ++it) {
-    const int q0 = qfirst + (it % nqt) * TR;
+    const int q0 = qfirst + t_cur * TR;
     // mask bytes of this step's query head, the lane's key column
-    const uint8_t* mk = MASK ? p.mask + (int64_t)b * p.m_sb + (int64_t)(hkv * p.G + it / nqt) * p.m_sh + key : nullptr;
+    const uint8_t* mk = MASK ? p.mask + (int64_t)b * p.m_sb + (int64_t)(hkv * p.G + h_cur) * p.m_sh + key : nullptr;
     // Tiles and LSE / Delta of step it are in LDS, and every wave is done
     // with step it - 1.
     __syncthreads();
-    const uint16_t* sQ = sbuf[it % NB][0];
-    const uint16_t* sO = sbuf[it % NB][1];
-    const float* sL = sLD[it % NB][0];
-    const float* sD = sLD[it % NB][1];
+    const uint16_t* sQ = sbuf[slot][0];
+    const uint16_t* sO = sbuf[slot][1];
+    const float* sL = sLD[slot][0];
+    const float* sD = sLD[slot][1];
     // LSE (and Delta) of the lane's 16 rows: 4 groups of 4 consecutive rows.
     float lr[16], dr[16];
 #pragma unroll
@@ -333,15 +345,19 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       // done), the copies of step it + 2 into the slot of step it - 1 (every
       // wave passed the barrier of step it), then this wave's copies of step
       // it + 1 complete (those of step it + 2 may still fly).
-      if (it + 1 < nsteps) put_ld(it + 1);
+      const int s1 = slot == NB - 1 ? 0 : slot + 1, s2 = s1 == NB - 1 ? 0 : s1 + 1;
+      if (it + 1 < nsteps) put_ld(s1);
       if (it + 2 < nsteps) {
-        dma(it + 2);
+        dma(h_ahd, t_ahd, s2);
         wait_vmem_below<4>();
-        fetch_ld(it + 2);
+        fetch_ld(h_ahd, t_ahd);
       } else {
         wait_vmem();
       }
     }
+    advance(h_cur, t_cur);
+    advance(h_ahd, t_ahd);
+    slot = slot == NB - 1 ? 0 : slot + 1;
   }
   if (key < p.Skv) {
     if (kwave)
