@@ -13,14 +13,15 @@
 // Three kernels, none of them with atomics:
 //   * delta: Delta_i = dO_i . O_i in fp32, one row per 16 lanes.
 //   * dkdv: a workgroup owns 128 keys of one KV head (8 waves: for each 32
-//     keys one wave accumulates dV, one dK, with K (and V) of its keys
-//     resident as MFMA B operands) and sweeps the query tiles (32 rows) of
-//     every query head of the group: S = Q K^T, dP = dO V^T, then
+//     keys one wave computes S and P and accumulates dV, with K of its keys
+//     resident as MFMA B operands, and one computes dP and dS and
+//     accumulates dK, with V resident) and sweeps the query tiles (32 rows)
+//     of every query head of the group: S = Q K^T, dP = dO V^T, then
 //     dV^T += dO^T P and dK^T += Q^T dS on v_mfma_f32_32x32x16, P and dS
 //     rounded to 16 bits as B operands straight from the accumulator layout.
-//   * dq: a workgroup owns 128 query rows of one head (Q and dO resident) and
-//     sweeps the key tiles: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T;
-//     it fits 256 registers, so two workgroups share a CU.
+//   * dq: a workgroup of 8 waves owns 256 query rows of one head (Q and dO
+//     resident) and sweeps the key tiles: S^T = K Q^T, dP^T = V dO^T,
+//     dQ^T += K^T dS^T.
 // The operands read transposed (dO^T, Q^T, K^T) come from row-major LDS tiles
 // through ds_read_b64_tr_b16, in the key (query) order in which the
 // accumulator holds P and dS, so the contraction pairs the right elements.
@@ -29,6 +30,8 @@
 // of bank conflicts (bsw below).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "fa_asm.h"
 #include "fa_device.h"
@@ -40,7 +43,9 @@ namespace {
 constexpr int BD = 128;    // head dim
 constexpr int TR = 32;     // rows of an LDS tile
 constexpr int NWB = 4;     // waves per workgroup
-constexpr int BLK = 32 * NWB;  // keys (dkdv) or query rows (dq) per workgroup
+constexpr int BLK = 32 * NWB;  // keys per dK/dV workgroup
+constexpr int NWQ = 8;         // waves per dQ workgroup (two per SIMD)
+constexpr int BLKQ = 32 * NWQ;  // query rows per dQ workgroup
 
 // One chunk swizzle serves both read patterns of a tile: the row reads
 // (16 consecutive rows, one chunk each, per 256 bytes) see 16 distinct
@@ -165,41 +170,71 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
   if (row < rows && sub == 0) p.delta[row] = acc;
 }
 
-// Two waves per key group of 32: wave g (0..3) computes S, P and dV^T +=
-// dO^T P; wave g + 4 computes S, dP, dS and dK^T += Q^T dS. Each holds one
-// gradient's accumulators, so both fit 256 registers and share a SIMD.
+// End of a phase of the dK/dV kernel: the workgroup barrier, with no
+// instruction of the phase (MFMAs included, which touch no memory) moved
+// past it and none of the next phase moved before it.
+__device__ __forceinline__ void phase_end() {
+  __builtin_amdgcn_sched_barrier(0);
+  barrier_keep_copies();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Two waves per key group g of 32 keys (g = w % 4; waves g and g + 4 share
+// a SIMD). The P wave (w < 4) holds K of its keys as B operands and dV^T;
+// the dS wave (w >= 4) holds V and dK^T. Per step s of the sweep (a query
+// head and a 32-row query tile):
+//   M_P(s): S(s) = Q(s) K^T, and dV^T += dO(s-1)^T P(s-1)     (P wave)
+//   V_P(s): P(s) = exp2(S scale log2e - LSE log2e), masked; stored in fp32
+//           to LDS for the dS wave and rounded to 16 bits as the P wave's
+//           next B operand
+//   M_D(s): dP(s) = dO(s) V^T, and dK^T += Q(s-1)^T dS(s-1)    (dS wave)
+//   V_D(s): dS(s) = P(s) (dP(s) - Delta), rounded to 16 bits
+// The two waves run one phase apart and every phase ends with a workgroup
+// barrier: phase 2s is M_P(s) with V_D(s-1), phase 2s+1 is V_P(s) with
+// M_D(s). Every score is computed and exponentiated once and both waves
+// issue 16 MFMAs per step. The transposed A operands of an M phase's
+// gradient update (the slower transposing LDS reads, 8 KB per wave) are
+// read during the wave's V phase before it, so on each SIMD they overlap
+// the other wave's MFMAs; the row operands (Q or dO rows) are read at the
+// start of the M phase, behind the update's MFMAs, which need no LDS.
 //
-// A step's Q and dO tiles are copied HBM -> LDS by LDS-DMA (no register
-// staging) into a three-deep ring, by the dV waves, which have less MFMA
-// work per step than the dK waves: at the end of step it, dV wave g issues
-// 4 KB of the tiles of step it + 2 (tile g / 2, chunk positions
-// 64 (4 (g % 2) + n) + lane for n = 0..3; the swizzle is an involution, so a
-// lane fetches the logical chunk its position holds) and waits for its
-// copies of step it + 1; the barrier at the top of step it + 1 publishes
-// them.
+// Tile lifetimes: Q(s) rows are read in phase 2s and dO(s) rows in phase
+// 2s + 1; dO(s)^T in phase 2s + 1 (for M_P(s + 1)) and Q(s)^T in phase
+// 2s + 2 (for M_D(s + 1)). The tiles live in a four-deep
+// LDS ring (slot s % 4), copied HBM -> LDS by LDS-DMA (no register staging)
+// by the P waves: at the start of phase 2t + 1 P wave g issues 4 KB of the
+// tiles of step t + 3 (tile g / 2, chunk positions 64 (4 (g % 2) + n) +
+// lane, n = 0..3; the swizzle is an involution, so a lane fetches the
+// logical chunk its position holds) into the slot of step t - 1, read last
+// in phase 2t, and at the end of phase 2t it waits for its copies of step
+// t + 1. LSE log2e and Delta of step s + 2 are loaded by wave 4 into
+// registers during step s and stored into their ring slot at its end.
 template <class T, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NB = 3;  // ring depth
+  constexpr int NB = 4;  // ring depth
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[NB][2][TR * BD];
-  __shared__ __attribute__((aligned(16))) float sLD[NB][2][TR];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
-  const bool kwave = __builtin_amdgcn_readfirstlane(w) >= 4;  // dK (else dV)
+  __shared__ __attribute__((aligned(16))) float sLD[NB][2 * TR];  // LSE log2e, then Delta
+  __shared__ __attribute__((aligned(16))) float pex[4][4][64][4];  // P of each key group
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5, g = w & 3;
+  // (The wave index and everything selected by it are wave-uniform scalars,
+  // so that the selects between kernel arguments stay in scalar registers.)
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const bool dswave = wu >= 4;
   // Workgroups in order of decreasing work (under the causal mask the first
   // key blocks see the most query rows), the (batch, KV head) index fastest
   // so that one head's workgroups share an XCD (workgroup i runs on XCD i % 8).
   const int lin = blockIdx.x + blockIdx.y * gridDim.x, nbk = p.B * p.Hkv;
   const int bk = lin % nbk, b = bk / p.Hkv, hkv = bk % p.Hkv;
   const int k0 = (lin / nbk) * BLK;
-  const int key = k0 + 32 * (w & 3) + c;  // this lane's key (column of S)
+  const int key = k0 + 32 * g + c;  // this lane's key (column of S)
   int Lq, Lk;
   batch_lengths(p, b, Lq, Lk);
   const int diag = Lk - Lq;  // key j is visible to row i iff j <= i + diag
   const uint16_t* kg = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh;
   const uint16_t* vg = (const uint16_t*)p.v + (int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh;
-  u32x4 kop[BD / 16], vop[BD / 16];
-  load_bop(kop, kg, p.k_ss, min(key, p.Skv - 1));
-  if (kwave) load_bop(vop, vg, p.v_ss, min(key, p.Skv - 1));
-  f32x16 acc[BD / 32];  // dK^T (K waves) or dV^T (V waves)
+  u32x4 kv_op[BD / 16];  // K (P wave) or V (dS wave) rows of the lane's key
+  load_bop(kv_op, dswave ? vg : kg, dswave ? p.v_ss : p.k_ss, min(key, p.Skv - 1));
+  f32x16 acc[BD / 32];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
   for (int dt = 0; dt < BD / 32; ++dt)
 #pragma unroll
@@ -207,160 +242,219 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   // Query rows that can see a key of this block: i >= k0 - diag (causal).
   const int qfirst = CAUSAL ? max(0, k0 - diag) : 0;
   const int nqt = (k0 < Lk && Lq > qfirst) ? (Lq - qfirst + TR - 1) / TR : 0;
-  // The sweep: step it = (query head hq, query tile t) of the group.
+  // The sweep: step s = (query head hkv G + s / nqt, tile s % nqt).
   const int nsteps = p.G * nqt;
-  // This dV wave's share of a step's copies: tile (w & 3) / 2 (0 Q, 1 dO),
-  // per instruction the tile row and the byte offset of the logical chunk.
-  const bool c_do = (w & 2) != 0;
-  int crow[4];
-  uint32_t cchunk[4];
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int pos = 64 * (4 * (w & 1) + n) + lane, row = pos >> 4;
-    crow[n] = row;
-    cchunk[n] = (uint32_t)(bsw(row, pos & 15) * 16);
-  }
-  const int64_t c_ss = c_do ? p.do_ss : p.q_ss;
-  const uint32_t c_rb = (uint32_t)c_ss * 2u;
-  // Step it = (query head hkv G + it / nqt, tile it % nqt), tracked without
-  // divisions: (h, t) of the step computed and of the step two ahead, and
-  // their ring slots.
-  int h_cur = 0, t_cur = 0, h_ahd = 0, t_ahd = 0, slot = 0;
+  // (h, t) of the step computed and of the step whose copies or LSE / Delta
+  // come next, tracked without divisions.
+  int h_cur = 0, t_cur = 0, h_ahd = 0, t_ahd = 0;
   auto advance = [&](int& hh, int& tt) __attribute__((always_inline)) {
     if (++tt == nqt) {
       tt = 0;
       ++hh;
     }
   };
+  // P wave copies: tile (w & 3) / 2 (0 Q, 1 dO); per instruction the tile
+  // row and the byte offset of the logical chunk.
+  const bool c_do = (wu & 2) != 0;
+  int crow[4];
+  uint32_t cchunk[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int pos = 64 * (4 * (wu & 1) + n) + lane, row = pos >> 4;
+    crow[n] = row;
+    cchunk[n] = (uint32_t)(bsw(row, pos & 15) * 16);
+  }
+  const int64_t c_ss = c_do ? p.do_ss : p.q_ss, c_sh = c_do ? p.do_sh : p.q_sh;
+  // the group's first query head
+  const uint16_t* c_head = c_do ? (const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hkv * p.G * p.do_sh
+                                : (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hkv * p.G * p.q_sh;
+  const uint32_t c_rb = (uint32_t)c_ss * 2u;
+  const uint32_t c_lds = lds_addr_of(sbuf[0][c_do ? 1 : 0]) + (wu & 1) * 4096;
   auto dma = [&](int hh, int tt, int sl) __attribute__((always_inline)) {
-    const int hq = hkv * p.G + hh, q0 = qfirst + tt * TR;
-    const uint16_t* base = c_do ? (const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hq * p.do_sh
-                                : (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh;
-    base += (int64_t)q0 * c_ss;
+    const int q0 = qfirst + tt * TR;
+    const uint16_t* base = c_head + (int64_t)hh * c_sh + (int64_t)q0 * c_ss;
     const int rmax = p.Sq - 1 - q0;  // rows past Sq fetch row Sq - 1
-    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr_of(sbuf[sl][c_do ? 1 : 0]) + (w & 1) * 4096);
+    const uint32_t l0 = c_lds + (uint32_t)sl * (2 * TR * BD * 2);
 #pragma unroll
     for (int n = 0; n < 4; ++n) lds_copy16(base, (uint32_t)min(crow[n], rmax) * c_rb + cchunk[n], l0 + n * 1024);
   };
-  float rl = 0.f, rd = 0.f;
+  // Wave 4: lane i < 32 loads LSE of row q0 + i, lane 32 + i Delta; the
+  // stored value (LSE log2e) is formed only when it is stored, so that the
+  // load's latency hides behind the step.
+  float ld = 0.f;
   auto fetch_ld = [&](int hh, int tt) __attribute__((always_inline)) {
-    if (threadIdx.x < TR) {
-      const int hq = hkv * p.G + hh, q0 = qfirst + tt * TR;
-      const int64_t bh = (int64_t)b * p.Hq + hq;
-      const int i = q0 + threadIdx.x;
-      const float l = i < p.Sq ? p.lse[bh * p.Sq + i] : -INFINITY;
-      // rows without keys (LSE = -inf) and padding rows get P = 0
-      rl = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
-      rd = i < p.Sq ? p.delta[bh * p.Sq + i] : 0.f;
-    }
+    const int hq = hkv * p.G + hh, i = qfirst + tt * TR + c;
+    const int64_t ri = ((int64_t)b * p.Hq + hq) * p.Sq + i;
+    ld = i >= p.Sq ? (h == 0 ? -INFINITY : 0.f) : h == 0 ? p.lse[ri] : p.delta[ri];
   };
   auto put_ld = [&](int sl) __attribute__((always_inline)) {
-    if (threadIdx.x < TR) {
-      sLD[sl][0][threadIdx.x] = rl;
-      sLD[sl][1][threadIdx.x] = rd;
-    }
+    // rows without keys (LSE = -inf) and padding rows get P = 0
+    sLD[sl][lane] = h != 0 ? ld : ld == -INFINITY ? INFINITY : ld * 1.4426950408889634f;
+  };
+  // A operands of an M phase: the rows of one tile and the transposed other.
+  u32x4 ar[BD / 16], at[BD / 16];
+  auto read_rows = [&](const uint16_t* t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < BD / 16; ++ks) ar[ks] = row_op(t, ks);
+  };
+  auto read_tr = [&](const uint16_t* t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < BD / 16; ++ks) at[ks] = tr_op(t, ks & 3, ks >> 2);
   };
   if (nsteps > 0) {
-    if (!kwave) dma(0, 0, 0);
-    fetch_ld(0, 0);
-    put_ld(0);
-    advance(h_ahd, t_ahd);
-    if (nsteps > 1) {
-      if (!kwave) dma(h_ahd, t_ahd, 1);
-      fetch_ld(h_ahd, t_ahd);
-    }
-    advance(h_ahd, t_ahd);  // now step 2
-    wait_vmem();
-  }
-  for (int it = 0; it < nsteps; ++it) {
-    const int q0 = qfirst + t_cur * TR;
-    // mask bytes of this step's query head, the lane's key column
-    const uint8_t* mk = MASK ? p.mask + (int64_t)b * p.m_sb + (int64_t)(hkv * p.G + h_cur) * p.m_sh + key : nullptr;
-    // Tiles and LSE / Delta of step it are in LDS, and every wave is done
-    // with step it - 1.
-    __syncthreads();
-    const uint16_t* sQ = sbuf[slot][0];
-    const uint16_t* sO = sbuf[slot][1];
-    const float* sL = sLD[slot][0];
-    const float* sD = sLD[slot][1];
-    // LSE (and Delta) of the lane's 16 rows: 4 groups of 4 consecutive rows.
-    float lr[16], dr[16];
+    if (!dswave) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 l4 = *(const float4*)(sL + 8 * j + 4 * h);
-      lr[4 * j] = l4.x; lr[4 * j + 1] = l4.y; lr[4 * j + 2] = l4.z; lr[4 * j + 3] = l4.w;
-    }
-    f32x16 sv = {}, dp = {};
-    if (kwave) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 d4 = *(const float4*)(sD + 8 * j + 4 * h);
-        dr[4 * j] = d4.x; dr[4 * j + 1] = d4.y; dr[4 * j + 2] = d4.z; dr[4 * j + 3] = d4.w;
-      }
-      // S and dP chains interleaved: each MFMA's predecessor in the issue
-      // order is independent of it.
-#pragma unroll
-      for (int ks = 0; ks < BD / 16; ++ks) {
-        sv = T::mfma(row_op(sQ, ks), kop[ks], sv);
-        dp = T::mfma(row_op(sO, ks), vop[ks], dp);
-      }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < BD / 16; ++ks) sv = T::mfma(row_op(sQ, ks), kop[ks], sv);
-    }
-    // Element i: query row q0 + r, r = 8 (i / 4) + 4 h + i % 4; key `key`.
-    // A block every row and key of which exist and (causal) whose last key
-    // the first row sees needs no per-element test.
-    const int kw0 = k0 + 32 * (w & 3);
-    const bool inside = !MASK && __builtin_amdgcn_readfirstlane(
-                                     (kw0 + 31 < Lk && q0 + TR <= Lq && (!CAUSAL || kw0 + 31 <= q0 + diag)) ? 1 : 0);
-    f32x16 bm;  // P (V waves) or dS (K waves)
-    if (inside) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, -lr[i]));
-        bm[i] = kwave ? pv * (dp[i] - dr[i]) : pv;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 8 * (i >> 2) + 4 * h + (i & 3);
-        const int qi = q0 + r;
-        bool ok = key < Lk && qi < Lq;
-        if (CAUSAL) ok = ok && key <= qi + diag;
-        if (MASK) ok = ok && mk[(int64_t)qi * p.m_ss] == 0;
-        const float pv = ok ? fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, -lr[i])) : 0.f;
-        bm[i] = kwave ? pv * (dp[i] - dr[i]) : pv;
-      }
-    }
-    const uint16_t* at = kwave ? sQ : sO;  // Q^T for dK, dO^T for dV
-#pragma unroll
-    for (int ks = 0; ks < TR / 16; ++ks) {
-      const u32x4 bb = pack_b<T>(bm, ks);
-#pragma unroll
-      for (int dt = 0; dt < BD / 32; ++dt) acc[dt] = T::mfma(tr_op(at, dt, ks), bb, acc[dt]);
-    }
-    if (!kwave) {
-      // LSE / Delta of step it + 1 into their ring slot (step it - 2 is long
-      // done), the copies of step it + 2 into the slot of step it - 1 (every
-      // wave passed the barrier of step it), then this wave's copies of step
-      // it + 1 complete (those of step it + 2 may still fly).
-      const int s1 = slot == NB - 1 ? 0 : slot + 1, s2 = s1 == NB - 1 ? 0 : s1 + 1;
-      if (it + 1 < nsteps) put_ld(s1);
-      if (it + 2 < nsteps) {
-        dma(h_ahd, t_ahd, s2);
+      for (int j = 0; j < 3; ++j)
+        if (j < nsteps) {
+          dma(h_ahd, t_ahd, j);
+          advance(h_ahd, t_ahd);
+        }
+      // h_ahd, t_ahd: step 3; the copies of step 0 are complete
+      if (nsteps > 2)
+        wait_vmem_below<8>();
+      else if (nsteps > 1)
         wait_vmem_below<4>();
-        fetch_ld(h_ahd, t_ahd);
-      } else {
+      else
         wait_vmem();
+    } else {
+      if (w == 4) {
+        fetch_ld(0, 0);
+        put_ld(0);
+        if (nsteps > 1) {
+          fetch_ld(0 + (nqt == 1), nqt == 1 ? 0 : 1);
+          put_ld(1);
+        }
       }
+      advance(h_ahd, t_ahd);
+      advance(h_ahd, t_ahd);  // step 2
     }
-    advance(h_cur, t_cur);
-    advance(h_ahd, t_ahd);
-    slot = slot == NB - 1 ? 0 : slot + 1;
+    barrier_keep_copies();
+  }
+  using F = std::false_type;
+  using U = std::true_type;
+  if (!dswave) {
+    u32x4 pb[2];  // P(s - 1) as the B operand of the dV update
+    f32x16 sv;
+    // Phase 2s: M_P(s); phase 2s + 1: V_P(s) and the reads for M_P(s + 1).
+    // DS: s < nsteps; DU: s > 0.
+    auto step = [&](int s, auto DS, auto DU) __attribute__((always_inline)) {
+      if (DS) read_rows(sbuf[s & (NB - 1)][0]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (DU) {
+#pragma unroll
+        for (int ks = 0; ks < BD / 16; ++ks) acc[ks & 3] = T::mfma(at[ks], pb[ks >> 2], acc[ks & 3]);
+      }
+      if (DS) {
+        sv = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < BD / 16; ++ks) sv = T::mfma(ar[ks], kv_op[ks], sv);
+      }
+      // This wave's copies of step s + 1 are complete (those of step s + 2
+      // may still fly).
+      if (s + 2 < nsteps)
+        wait_vmem_below<4>();
+      else
+        wait_vmem();
+      phase_end();
+      if (s + 3 < nsteps) dma(h_ahd, t_ahd, (s + 3) & (NB - 1));
+      if (DS) {
+        const int q0 = qfirst + t_cur * TR;
+        const float* sL = sLD[s & (NB - 1)];
+        float lr[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 l4 = *(const float4*)(sL + 8 * j + 4 * h);
+          lr[4 * j] = l4.x; lr[4 * j + 1] = l4.y; lr[4 * j + 2] = l4.z; lr[4 * j + 3] = l4.w;
+        }
+        read_tr(sbuf[s & (NB - 1)][1]);
+        // Element i: query row q0 + r, r = 8 (i / 4) + 4 h + i % 4; key `key`.
+        // A block every row and key of which exist and (causal) whose last
+        // key the first row sees needs no per-element test.
+        const int kw0 = k0 + 32 * g;
+        const bool inside = !MASK && __builtin_amdgcn_readfirstlane(
+                                         (kw0 + 31 < Lk && q0 + TR <= Lq && (!CAUSAL || kw0 + 31 <= q0 + diag)) ? 1 : 0);
+        f32x16 pv;
+        if (inside) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, -lr[i]));
+        } else {
+          const uint8_t* mk = MASK ? p.mask + (int64_t)b * p.m_sb + (int64_t)(hkv * p.G + h_cur) * p.m_sh + key : nullptr;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qi = q0 + 8 * (i >> 2) + 4 * h + (i & 3);
+            bool ok = key < Lk && qi < Lq;
+            if (CAUSAL) ok = ok && key <= qi + diag;
+            if (MASK) ok = ok && mk[(int64_t)qi * p.m_ss] == 0;
+            pv[i] = ok ? fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, -lr[i])) : 0.f;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *(float4*)pex[g][j][lane] = make_float4(pv[4 * j], pv[4 * j + 1], pv[4 * j + 2], pv[4 * j + 3]);
+        pb[0] = pack_b<T>(pv, 0);
+        pb[1] = pack_b<T>(pv, 1);
+      }
+      phase_end();
+      advance(h_cur, t_cur);
+      advance(h_ahd, t_ahd);
+    };
+    if (nsteps > 0) {
+      step(0, U{}, F{});
+      for (int s = 1; s < nsteps; ++s) step(s, U{}, U{});
+      step(nsteps, F{}, U{});
+    }
+  } else {
+    u32x4 db[2];  // dS(s - 1) as the B operand of the dK update
+    f32x16 dp;
+    // Phase 2s: V_D(s - 1) and the reads for M_D(s); phase 2s + 1: M_D(s).
+    // DS: s < nsteps; DU: s > 0.
+    auto step = [&](int s, auto DS, auto DU) __attribute__((always_inline)) {
+      const bool ldw = w == 4 && s + 2 < nsteps;
+      if (ldw) fetch_ld(h_ahd, t_ahd);
+      if (DU) {
+        const float* sD = sLD[(s - 1) & (NB - 1)] + TR;
+        float4 d4[4], p4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          d4[j] = *(const float4*)(sD + 8 * j + 4 * h);
+          p4[j] = *(const float4*)pex[g][j][lane];
+        }
+        read_tr(sbuf[(s - 1) & (NB - 1)][0]);
+        f32x16 dsv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dsv[4 * j] = p4[j].x * (dp[4 * j] - d4[j].x);
+          dsv[4 * j + 1] = p4[j].y * (dp[4 * j + 1] - d4[j].y);
+          dsv[4 * j + 2] = p4[j].z * (dp[4 * j + 2] - d4[j].z);
+          dsv[4 * j + 3] = p4[j].w * (dp[4 * j + 3] - d4[j].w);
+        }
+        db[0] = pack_b<T>(dsv, 0);
+        db[1] = pack_b<T>(dsv, 1);
+      }
+      phase_end();
+      if (DS) read_rows(sbuf[s & (NB - 1)][1]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (DU) {
+#pragma unroll
+        for (int ks = 0; ks < BD / 16; ++ks) acc[ks & 3] = T::mfma(at[ks], db[ks >> 2], acc[ks & 3]);
+      }
+      if (DS) {
+        dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < BD / 16; ++ks) dp = T::mfma(ar[ks], kv_op[ks], dp);
+      }
+      if (ldw) put_ld((s + 2) & (NB - 1));
+      phase_end();
+      advance(h_ahd, t_ahd);
+    };
+    if (nsteps > 0) {
+      step(0, U{}, F{});
+      for (int s = 1; s < nsteps; ++s) step(s, U{}, U{});
+      step(nsteps, F{}, U{});
+    }
   }
   if (key < p.Skv) {
-    if (kwave)
+    if (dswave)
       store_t<T>((uint16_t*)p.dk + (int64_t)b * p.dk_sb + (int64_t)hkv * p.dk_sh, p.dk_ss, key, acc, p.scale);
     else
       store_t<T>((uint16_t*)p.dv + (int64_t)b * p.dv_sb + (int64_t)hkv * p.dv_sh, p.dv_ss, key, acc, 1.f);
@@ -368,7 +462,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 template <class T, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
   // Two buffers of the K and V tiles (K read both ways, V by rows).
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[2][2][TR * BD];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
@@ -376,7 +470,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   // query blocks see the most keys), the (batch, head) index fastest.
   const int lin = blockIdx.x + blockIdx.y * gridDim.x, nbh = p.B * p.Hq;
   const int bh = lin % nbh, b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.G;
-  const int q0 = (CAUSAL ? (int)gridDim.x - 1 - lin / nbh : lin / nbh) * BLK;
+  const int q0 = (CAUSAL ? (int)gridDim.x - 1 - lin / nbh : lin / nbh) * BLKQ;
   const int qi = q0 + 32 * w + c;  // this lane's query row (column of S^T)
   int Lq, Lk;
   batch_lengths(p, b, Lq, Lk);
@@ -401,10 +495,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   for (int dt = 0; dt < BD / 32; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dq_t[dt][i] = 0.f;
-  // Keys any row of this block sees: j <= q0 + BLK - 1 + diag (causal).
-  const int kend = q0 >= Lq ? 0 : CAUSAL ? max(0, min(Lk, q0 + BLK + diag)) : Lk;
+  // Keys any row of this block sees: j <= q0 + BLKQ - 1 + diag (causal).
+  const int kend = q0 >= Lq ? 0 : CAUSAL ? max(0, min(Lk, q0 + BLKQ + diag)) : Lk;
   const int nkt = (kend + TR - 1) / TR;
-  TileRegs<> rk, rv;
+  TileRegs<64 * NWQ> rk, rv;
   auto fetch = [&](int t) __attribute__((always_inline)) {
     fetch_tile(rk, kg, p.k_ss, t * TR, p.Skv);
     fetch_tile(rv, vg, p.v_ss, t * TR, p.Skv);
@@ -484,8 +578,8 @@ hipError_t launch_bwd_t(BwdParams& p, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (rows > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, CAUSAL, MASK>), dim3((unsigned)((p.Sq + BLK - 1) / BLK), (unsigned)(p.B * p.Hq)),
-                       dim3(256), 0, st, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, CAUSAL, MASK>), dim3((unsigned)((p.Sq + BLKQ - 1) / BLKQ), (unsigned)(p.B * p.Hq)),
+                       dim3(64 * NWQ), 0, st, p);
   }
   return hipGetLastError();
 }
