@@ -207,13 +207,16 @@ __device__ __forceinline__ void phase_end() {
 // lane, n = 0..3; the swizzle is an involution, so a lane fetches the
 // logical chunk its position holds) into the slot of step t - 1, read last
 // in phase 2t, and at the end of phase 2t it waits for its copies of step
-// t + 1. LSE log2e and Delta of step s + 2 are loaded by wave 4 into
-// registers during step s and stored into their ring slot at its end.
+// t + 1. S and dP start from -LSE / scale and -Delta of their rows (so V_P
+// is one multiply and one exp2 per score and V_D one multiply per element,
+// with no LDS read before them); these values of step s + 2 are loaded by
+// wave 4 into registers during step s, stored into their ring slot at its
+// end, and read at the start of the M phases of step s + 2.
 template <class T, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NB = 4;  // ring depth
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[NB][2][TR * BD];
-  __shared__ __attribute__((aligned(16))) float sLD[NB][2 * TR];  // LSE log2e, then Delta
+  __shared__ __attribute__((aligned(16))) float sLD[NB][2 * TR];  // -LSE / scale, then -Delta
   __shared__ __attribute__((aligned(16))) float pex[4][4][64][4];  // P of each key group
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5, g = w & 3;
   // (The wave index and everything selected by it are wave-uniform scalars,
@@ -279,17 +282,20 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
     for (int n = 0; n < 4; ++n) lds_copy16(base, (uint32_t)min(crow[n], rmax) * c_rb + cchunk[n], l0 + n * 1024);
   };
   // Wave 4: lane i < 32 loads LSE of row q0 + i, lane 32 + i Delta; the
-  // stored value (LSE log2e) is formed only when it is stored, so that the
+  // stored values (-LSE / scale and -Delta, the initial values of the S and
+  // dP accumulators) are formed only when they are stored, so that the
   // load's latency hides behind the step.
   float ld = 0.f;
+  const float inv_scale = -1.f / p.scale;
   auto fetch_ld = [&](int hh, int tt) __attribute__((always_inline)) {
     const int hq = hkv * p.G + hh, i = qfirst + tt * TR + c;
     const int64_t ri = ((int64_t)b * p.Hq + hq) * p.Sq + i;
     ld = i >= p.Sq ? (h == 0 ? -INFINITY : 0.f) : h == 0 ? p.lse[ri] : p.delta[ri];
   };
   auto put_ld = [&](int sl) __attribute__((always_inline)) {
-    // rows without keys (LSE = -inf) and padding rows get P = 0
-    sLD[sl][lane] = h != 0 ? ld : ld == -INFINITY ? INFINITY : ld * 1.4426950408889634f;
+    // rows without keys (LSE = -inf) and padding rows get P = 0 (their
+    // elements are masked; the +inf start keeps them out of any overflow)
+    sLD[sl][lane] = h != 0 ? -ld : ld == -INFINITY ? INFINITY : ld * inv_scale;
   };
   // A operands of an M phase: the rows of one tile and the transposed other.
   u32x4 ar[BD / 16], at[BD / 16];
@@ -338,14 +344,23 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
     // Phase 2s: M_P(s); phase 2s + 1: V_P(s) and the reads for M_P(s + 1).
     // DS: s < nsteps; DU: s > 0.
     auto step = [&](int s, auto DS, auto DU) __attribute__((always_inline)) {
-      if (DS) read_rows(sbuf[s & (NB - 1)][0]);
+      // S starts from -LSE / scale of its row, so that the exponent of P is
+      // S scale log2e as it leaves the MFMAs.
+      if (DS) {
+        const float* sL = sLD[s & (NB - 1)];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 l4 = *(const float4*)(sL + 8 * j + 4 * h);
+          sv[4 * j] = l4.x; sv[4 * j + 1] = l4.y; sv[4 * j + 2] = l4.z; sv[4 * j + 3] = l4.w;
+        }
+        read_rows(sbuf[s & (NB - 1)][0]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (DU) {
 #pragma unroll
         for (int ks = 0; ks < BD / 16; ++ks) acc[ks & 3] = T::mfma(at[ks], pb[ks >> 2], acc[ks & 3]);
       }
       if (DS) {
-        sv = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < BD / 16; ++ks) sv = T::mfma(ar[ks], kv_op[ks], sv);
       }
@@ -359,13 +374,6 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       if (s + 3 < nsteps) dma(h_ahd, t_ahd, (s + 3) & (NB - 1));
       if (DS) {
         const int q0 = qfirst + t_cur * TR;
-        const float* sL = sLD[s & (NB - 1)];
-        float lr[16];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 l4 = *(const float4*)(sL + 8 * j + 4 * h);
-          lr[4 * j] = l4.x; lr[4 * j + 1] = l4.y; lr[4 * j + 2] = l4.z; lr[4 * j + 3] = l4.w;
-        }
         read_tr(sbuf[s & (NB - 1)][1]);
         // Element i: query row q0 + r, r = 8 (i / 4) + 4 h + i % 4; key `key`.
         // A block every row and key of which exist and (causal) whose last
@@ -376,7 +384,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
         f32x16 pv;
         if (inside) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, -lr[i]));
+          for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(sv[i] * p.scale_log2);
         } else {
           const uint8_t* mk = MASK ? p.mask + (int64_t)b * p.m_sb + (int64_t)(hkv * p.G + h_cur) * p.m_sh + key : nullptr;
 #pragma unroll
@@ -385,7 +393,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
             bool ok = key < Lk && qi < Lq;
             if (CAUSAL) ok = ok && key <= qi + diag;
             if (MASK) ok = ok && mk[(int64_t)qi * p.m_ss] == 0;
-            pv[i] = ok ? fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, -lr[i])) : 0.f;
+            pv[i] = ok ? fast_exp2(sv[i] * p.scale_log2) : 0.f;
           }
         }
 #pragma unroll
@@ -412,34 +420,38 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       const bool ldw = w == 4 && s + 2 < nsteps;
       if (ldw) fetch_ld(h_ahd, t_ahd);
       if (DU) {
-        const float* sD = sLD[(s - 1) & (NB - 1)] + TR;
-        float4 d4[4], p4[4];
+        float4 p4[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          d4[j] = *(const float4*)(sD + 8 * j + 4 * h);
-          p4[j] = *(const float4*)pex[g][j][lane];
-        }
+        for (int j = 0; j < 4; ++j) p4[j] = *(const float4*)pex[g][j][lane];
         read_tr(sbuf[(s - 1) & (NB - 1)][0]);
-        f32x16 dsv;
+        f32x16 dsv;  // dp holds dP - Delta
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          dsv[4 * j] = p4[j].x * (dp[4 * j] - d4[j].x);
-          dsv[4 * j + 1] = p4[j].y * (dp[4 * j + 1] - d4[j].y);
-          dsv[4 * j + 2] = p4[j].z * (dp[4 * j + 2] - d4[j].z);
-          dsv[4 * j + 3] = p4[j].w * (dp[4 * j + 3] - d4[j].w);
+          dsv[4 * j] = p4[j].x * dp[4 * j];
+          dsv[4 * j + 1] = p4[j].y * dp[4 * j + 1];
+          dsv[4 * j + 2] = p4[j].z * dp[4 * j + 2];
+          dsv[4 * j + 3] = p4[j].w * dp[4 * j + 3];
         }
         db[0] = pack_b<T>(dsv, 0);
         db[1] = pack_b<T>(dsv, 1);
       }
       phase_end();
-      if (DS) read_rows(sbuf[s & (NB - 1)][1]);
+      // dP starts from -Delta of its row.
+      if (DS) {
+        const float* sD = sLD[s & (NB - 1)] + TR;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 d4 = *(const float4*)(sD + 8 * j + 4 * h);
+          dp[4 * j] = d4.x; dp[4 * j + 1] = d4.y; dp[4 * j + 2] = d4.z; dp[4 * j + 3] = d4.w;
+        }
+        read_rows(sbuf[s & (NB - 1)][1]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (DU) {
 #pragma unroll
         for (int ks = 0; ks < BD / 16; ++ks) acc[ks & 3] = T::mfma(at[ks], db[ks >> 2], acc[ks & 3]);
       }
       if (DS) {
-        dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < BD / 16; ++ks) dp = T::mfma(ar[ks], kv_op[ks], dp);
       }
