@@ -496,11 +496,14 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
   u32x4 qop[BD / 16], dop[BD / 16];
   load_bop(qop, qg, p.q_ss, min(qi, p.Sq - 1));
   load_bop(dop, dg, p.do_ss, min(qi, p.Sq - 1));
-  float l2 = INFINITY, del = 0.f;  // padding rows and rows without keys: P = 0
+  // S^T and dP^T start from -LSE / scale and -Delta of the lane's row, so
+  // that P = exp2(S^T scale log2e) and dS^T = P dP^T; padding rows and rows
+  // without keys start from +inf (their elements are masked).
+  float s_init = INFINITY, d_init = 0.f;
   if (qi < Lq) {
     const float l = p.lse[((int64_t)b * p.Hq + hq) * p.Sq + qi];
-    l2 = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
-    del = p.delta[((int64_t)b * p.Hq + hq) * p.Sq + qi];
+    s_init = l == -INFINITY ? INFINITY : -l / p.scale;
+    d_init = -p.delta[((int64_t)b * p.Hq + hq) * p.Sq + qi];
   }
   f32x16 dq_t[BD / 32];
 #pragma unroll
@@ -538,7 +541,12 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
     const uint16_t* sVr = sbuf[t & 1][1];
     // Two waves share each SIMD here (the register budget is 256), so the
     // operands are read as the MFMAs consume them.
-    f32x16 s0 = {}, dp0 = {};
+    f32x16 s0, dp0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[i] = s_init;
+      dp0[i] = d_init;
+    }
 #pragma unroll
     for (int ks = 0; ks < BD / 16; ++ks) {
       s0 = T::mfma(row_op(sKr, ks), qop[ks], s0);
@@ -553,7 +561,7 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
     f32x16 dsm;
     if (inside) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dsm[i] = fast_exp2(__builtin_fmaf(s0[i], p.scale_log2, -l2)) * (dp0[i] - del);
+      for (int i = 0; i < 16; ++i) dsm[i] = fast_exp2(s0[i] * p.scale_log2) * dp0[i];
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -561,8 +569,7 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
         bool ok = kj < Lk && qi < Lq;
         if (CAUSAL) ok = ok && kj <= qi + diag;
         if (MASK) ok = ok && mq[kj] == 0;
-        const float pv = ok ? fast_exp2(__builtin_fmaf(s0[i], p.scale_log2, -l2)) : 0.f;
-        dsm[i] = pv * (dp0[i] - del);
+        dsm[i] = ok ? fast_exp2(s0[i] * p.scale_log2) * dp0[i] : 0.f;
       }
     }
 #pragma unroll
