@@ -10,8 +10,8 @@
 // with dK and dV summed over the query heads of a KV head (BSA README,
 // section 1).
 //
-// Three kernels, none of them with atomics:
-//   * delta: Delta_i = dO_i . O_i in fp32, one row per 16 lanes.
+// Two kernels, none of them with atomics, dQ first (it also forms and stores
+// Delta_i = dO_i . O_i in fp32, which the dK/dV kernel reads):
 //   * dkdv: a workgroup owns 128 keys of one KV head (8 waves: for each 32
 //     keys one wave computes S and P and accumulates dV, with K of its keys
 //     resident as MFMA B operands, and one computes dP and dS and
@@ -136,38 +136,6 @@ __device__ __forceinline__ void store_t(uint16_t* base, int64_t stride, int r, c
 __device__ __forceinline__ void batch_lengths(const BwdParams& p, int b, int& lq, int& lk) {
   lq = p.seqlens_q ? max(0, min(p.seqlens_q[b], p.Sq)) : p.Sq;
   lk = p.seqlens_k ? max(0, min(p.seqlens_k[b], p.Skv)) : p.Skv;
-}
-
-template <class T>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
-  const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  float acc = 0.f;
-  if (row < rows) {
-    const int64_t i = row % p.Sq, bh = row / p.Sq, hq = bh % p.Hq, b = bh / p.Hq;
-    const uint16_t* o = (const uint16_t*)p.o + b * p.o_sb + hq * p.o_sh + i * p.o_ss + 8 * sub;
-    const uint16_t* d = (const uint16_t*)p.dout + b * p.do_sb + hq * p.do_sh + i * p.do_ss + 8 * sub;
-    const u32x4 ov = *(const u32x4*)o, dv = *(const u32x4*)d;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc = T::dot2(ov[e], dv[e], acc);
-    if (p.o_lo) {
-      // The forward's rounding residual: Delta from O + o_lo, the unrounded
-      // fp32 output (the precise dpsum of the sparse-MLA page).
-      const float* lo = p.o_lo + b * p.ol_sb + hq * p.ol_sh + i * p.ol_ss + 8 * sub;
-      const float4 l0 = *(const float4*)lo, l1 = *(const float4*)(lo + 4);
-      const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f32x2 dd = T::unpack2(dv[e]);
-        acc = __builtin_fmaf(dd[0], lv[2 * e], acc);
-        acc = __builtin_fmaf(dd[1], lv[2 * e + 1], acc);
-      }
-    }
-  }
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
-  if (row < rows && sub == 0) p.delta[row] = acc;
 }
 
 // End of a phase of the dK/dV kernel: the workgroup barrier, with no
@@ -499,11 +467,41 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
   // S^T and dP^T start from -LSE / scale and -Delta of the lane's row, so
   // that P = exp2(S^T scale log2e) and dS^T = P dP^T; padding rows and rows
   // without keys start from +inf (their elements are masked).
+  // Delta_i = dO_i . O_i in fp32 (from O + o_lo, the unrounded output, when
+  // the forward wrote its rounding residual: the precise dpsum of the
+  // sparse-MLA page): the lane's half of row qi's columns, the columns of its
+  // dO operands, then the two halves summed. It is stored for the dK/dV
+  // kernel, which runs after this one.
+  const int qc = min(qi, p.Sq - 1);
+  const uint16_t* og = (const uint16_t*)p.o + (int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + (int64_t)qc * p.o_ss;
+  float dacc = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < BD / 16; ++ks) {
+    const u32x4 ov = *(const u32x4*)(og + 16 * ks + 8 * h);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dacc = T::dot2(ov[e], dop[ks][e], dacc);
+  }
+  if (p.o_lo) {
+    const float* lo = p.o_lo + (int64_t)b * p.ol_sb + (int64_t)hq * p.ol_sh + (int64_t)qc * p.ol_ss;
+#pragma unroll
+    for (int ks = 0; ks < BD / 16; ++ks) {
+      const float4 l0 = *(const float4*)(lo + 16 * ks + 8 * h), l1 = *(const float4*)(lo + 16 * ks + 8 * h + 4);
+      const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 dd = T::unpack2(dop[ks][e]);
+        dacc = __builtin_fmaf(dd[0], lv[2 * e], dacc);
+        dacc = __builtin_fmaf(dd[1], lv[2 * e + 1], dacc);
+      }
+    }
+  }
+  const float delta = half_sum(dacc);
+  if (h == 0 && qi < p.Sq) p.delta[((int64_t)b * p.Hq + hq) * p.Sq + qi] = delta;
   float s_init = INFINITY, d_init = 0.f;
   if (qi < Lq) {
     const float l = p.lse[((int64_t)b * p.Hq + hq) * p.Sq + qi];
     s_init = l == -INFINITY ? INFINITY : -l / p.scale;
-    d_init = -p.delta[((int64_t)b * p.Hq + hq) * p.Sq + qi];
+    d_init = -delta;
   }
   f32x16 dq_t[BD / 32];
 #pragma unroll
@@ -584,21 +582,17 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
 
 template <class T, bool CAUSAL, bool MASK>
 hipError_t launch_bwd_t(BwdParams& p, hipStream_t st) {
+  // The dQ kernel also writes Delta, which the dK/dV kernel reads.
   const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
   if (rows > 0) {
-    hipLaunchKernelGGL((bwd_delta_kernel<T>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, CAUSAL, MASK>), dim3((unsigned)((p.Sq + BLKQ - 1) / BLKQ), (unsigned)(p.B * p.Hq)),
+                       dim3(64 * NWQ), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.Skv > 0 && p.B * p.Hkv > 0) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, CAUSAL, MASK>), dim3((unsigned)((p.Skv + BLK - 1) / BLK), (unsigned)(p.B * p.Hkv)),
                        dim3(512), 0, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (rows > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, CAUSAL, MASK>), dim3((unsigned)((p.Sq + BLKQ - 1) / BLKQ), (unsigned)(p.B * p.Hq)),
-                       dim3(64 * NWQ), 0, st, p);
   }
   return hipGetLastError();
 }
