@@ -42,7 +42,7 @@ namespace {
 
 constexpr int BD = 128;    // head dim
 constexpr int TR = 32;     // rows of an LDS tile
-constexpr int NWB = 4;     // waves per workgroup
+constexpr int NWB = 4;     // 32-key groups per dK/dV workgroup (two waves each)
 constexpr int BLK = 32 * NWB;  // keys per dK/dV workgroup
 constexpr int NWQ = 8;         // waves per dQ workgroup (two per SIMD)
 constexpr int BLKQ = 32 * NWQ;  // query rows per dQ workgroup
@@ -54,36 +54,6 @@ constexpr int BLKQ = 32 * NWQ;  // query rows per dQ workgroup
 // distinct positions since bits 2..3 of the XOR term differ between the
 // four rows of an aligned group.
 __device__ __forceinline__ int bsw(int row, int ch) { return ch ^ (((row & 3) << 2) | ((row >> 2) & 3)); }
-
-// Cooperative copy of rows r0 .. r0+31 (clamped to n - 1; n >= 1) of a
-// row-major [*, 128] 16-bit matrix into LDS, in two halves: fetch_tile loads
-// this thread's two 16-byte chunks into registers (issued before the
-// previous tile's MFMAs, so the load latency hides behind them), put_tile
-// stores them into LDS in the swizzled layout.
-template <int NT = 64 * NWB>
-struct TileRegs {
-  static constexpr int N = (TR * BD / 8) / NT;  // 16-byte chunks per thread
-  u32x4 v[N];
-};
-template <int NT>
-__device__ __forceinline__ void fetch_tile(TileRegs<NT>& r, const uint16_t* src, int64_t stride, int r0, int n) {
-#pragma unroll
-  for (int u = 0; u < TileRegs<NT>::N; ++u) {
-    const int id = (int)threadIdx.x + u * NT;
-    const int row = id >> 4, ch = id & 15;
-    const int gr = min(r0 + row, n - 1);
-    r.v[u] = *(const u32x4*)(src + (int64_t)gr * stride + ch * 8);
-  }
-}
-template <int NT>
-__device__ __forceinline__ void put_tile(const TileRegs<NT>& r, uint16_t* dst) {
-#pragma unroll
-  for (int u = 0; u < TileRegs<NT>::N; ++u) {
-    const int id = (int)threadIdx.x + u * NT;
-    const int row = id >> 4, ch = id & 15;
-    *(u32x4*)(dst + row * BD + bsw(row, ch) * 8) = r.v[u];
-  }
-}
 
 // A operand "rows": lane (c, h) holds tile row c, columns 16 ks + 8 h .. +7.
 __device__ __forceinline__ u32x4 row_op(const uint16_t* t, int ks) {
@@ -443,8 +413,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
 
 template <class T, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
-  // Two buffers of the K and V tiles (K read both ways, V by rows).
-  __shared__ __attribute__((aligned(16))) uint16_t sbuf[2][2][TR * BD];
+  // Three slots of the K and V tiles (K read both ways, V by rows).
+  __shared__ __attribute__((aligned(16))) uint16_t sbuf[3][2][TR * BD];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
   // Workgroups in order of decreasing work (under the causal mask the last
   // query blocks see the most keys), the (batch, head) index fastest.
@@ -511,32 +481,52 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
   // Keys any row of this block sees: j <= q0 + BLKQ - 1 + diag (causal).
   const int kend = q0 >= Lq ? 0 : CAUSAL ? max(0, min(Lk, q0 + BLKQ + diag)) : Lk;
   const int nkt = (kend + TR - 1) / TR;
-  TileRegs<64 * NWQ> rk, rv;
-  auto fetch = [&](int t) __attribute__((always_inline)) {
-    fetch_tile(rk, kg, p.k_ss, t * TR, p.Skv);
-    fetch_tile(rv, vg, p.v_ss, t * TR, p.Skv);
-  };
-  auto put = [&](int t) __attribute__((always_inline)) {
-    put_tile(rk, sbuf[t & 1][0]);
-    put_tile(rv, sbuf[t & 1][1]);
+  // K and V tiles: a three-deep LDS ring (slot t % 3) filled by LDS-DMA two
+  // tiles ahead: wave w copies 2 KB of tile t + 2 (K for w < 4, V for
+  // w >= 4; chunk positions 64 (2 (w % 4) + n) + lane, n = 0..1) at the
+  // start of step t into the slot of tile t - 1 (every wave passed the
+  // barrier that ended its step), and waits for its copies of tile t + 1 at
+  // the end of step t. Rows at or past Skv fetch row Skv - 1.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const bool c_v = wu >= 4;
+  int crow[2];
+  uint32_t cchunk[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int pos = 64 * (2 * (wu & 3) + n) + lane, row = pos >> 4;
+    crow[n] = row;
+    cchunk[n] = (uint32_t)(bsw(row, pos & 15) * 16);
+  }
+  const int64_t c_ss = c_v ? p.v_ss : p.k_ss;
+  const uint16_t* c_head = c_v ? vg : kg;
+  const uint32_t c_rb = (uint32_t)c_ss * 2u;
+  const uint32_t c_lds = lds_addr_of(sbuf[0][c_v ? 1 : 0]) + (wu & 3) * 2048;
+  auto dma = [&](int t, int sl) __attribute__((always_inline)) {
+    const int j0 = t * TR;
+    const uint16_t* base = c_head + (int64_t)j0 * c_ss;
+    const int rmax = p.Skv - 1 - j0;
+    const uint32_t l0 = c_lds + (uint32_t)sl * (2 * TR * BD * 2);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) lds_copy16(base, (uint32_t)min(crow[n], rmax) * c_rb + cchunk[n], l0 + n * 1024);
   };
   if (nkt > 0) {
-    fetch(0);
-    put(0);
-    if (nkt > 1) fetch(1);
+    dma(0, 0);
+    if (nkt > 1) {
+      dma(1, 1);
+      wait_vmem_below<2>();
+    } else {
+      wait_vmem();
+    }
   }
+  int sl = 0;  // slot of tile t
   for (int t = 0; t < nkt; ++t) {
     const int j0 = t * TR;
-    // One barrier per tile (see the dK/dV kernel); the loads of tile t + 2
-    // fly during this tile's MFMAs.
-    __syncthreads();
-    if (t + 1 < nkt) {
-      put(t + 1);
-      if (t + 2 < nkt) fetch(t + 2);
-    }
-    const uint16_t* sKr = sbuf[t & 1][0];
+    // Tile t is in LDS and every wave is done with tile t - 1.
+    barrier_keep_copies();
+    if (t + 2 < nkt) dma(t + 2, sl == 0 ? 2 : sl - 1);
+    const uint16_t* sKr = sbuf[sl][0];
     const uint16_t* sKt = sKr;
-    const uint16_t* sVr = sbuf[t & 1][1];
+    const uint16_t* sVr = sbuf[sl][1];
     // Two waves share each SIMD here (the register budget is 256), so the
     // operands are read as the MFMAs consume them.
     f32x16 s0, dp0;
@@ -576,6 +566,12 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int dt = 0; dt < BD / 32; ++dt) dq_t[dt] = T::mfma(tr_op(sKt, dt, ks), db, dq_t[dt]);
     }
+    // this wave's copies of tile t + 1 are complete (tile t + 2 may fly)
+    if (t + 2 < nkt)
+      wait_vmem_below<2>();
+    else
+      wait_vmem();
+    sl = sl == 2 ? 0 : sl + 1;
   }
   if (qi < p.Sq) store_t<T>((uint16_t*)p.dq + (int64_t)b * p.dq_sb + (int64_t)hq * p.dq_sh, p.dq_ss, qi, dq_t, p.scale);
 }
