@@ -173,7 +173,7 @@ def fa_fwd(q, k, v, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k
 def fa_bwd(q, k, v, o, lse, dout, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k=None, o_lo=None,
            dq=None, dk=None, dv=None, delta=None, stream=None):
     """Gradients (dq, dk, dv) of the dense/causal/masked/GQA forward given
-    its output o, its lse and the output gradient dout (f16/bf16, D = 128);
+    its output o, its lse and the output gradient dout (f16/bf16, D = 64 or 128);
     mask and sequence lengths as fa_fwd's; o_lo (the forward's rounding
     residual) makes Delta = dO . (o + o_lo).
     delta (fp32 [B,Hq,Sq]) is the kernels' workspace; it is allocated here

@@ -406,7 +406,8 @@ fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
   if ((s = check_seqlens("seqlens_k", seqlens_k, q->shape[0])) != FA_OK) return s;
   if ((s = check_o_lo(o_lo, o)) != FA_OK) return s;
   if (q->dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "the backward takes f16 or bf16");
-  if (q->shape[3] != 128) return fail(FA_ERR_UNSUPPORTED, "the backward supports head dim 128 only");
+  if (q->shape[3] != 64 && q->shape[3] != 128)
+    return fail(FA_ERR_UNSUPPORTED, "the backward supports head dim 64 or 128 (got %lld)", (long long)q->shape[3]);
   if ((s = check_tensor("dout", dout, 4, true)) != FA_OK) return s;
   if ((s = check_tensor("dq", dq, 4, true)) != FA_OK) return s;
   if ((s = check_tensor("dk", dk, 4, true)) != FA_OK) return s;
@@ -470,7 +471,7 @@ fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
   }
   if ((int64_t)p.B * p.Hq * p.Sq == 0 && (int64_t)p.B * p.Hkv * p.Skv == 0) return FA_OK;
   const bool has_mask = mask && numel(mask) > 0;
-  return hip_status(fa::launch_bwd(to_dt(q->dtype), causal != 0, has_mask, p, (hipStream_t)stream));
+  return hip_status(fa::launch_bwd(to_dt(q->dtype), (int)q->shape[3], causal != 0, has_mask, p, (hipStream_t)stream));
 }
 
 fa_status fa_fwd_varlen(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* cu_seqlens_q,

@@ -1,5 +1,5 @@
-// Attention backward for 16-bit inputs on gfx950 (D = 128; dense, causal,
-// GQA): dQ, dK, dV from Q, K, V, the forward's O and LSE, and dO.
+// Attention backward for 16-bit inputs on gfx950 (D = 64 or 128; dense,
+// causal, GQA): dQ, dK, dV from Q, K, V, the forward's O and LSE, and dO.
 //
 // Method: the backward formulas of the ops-transformer FlashAttentionScoreGrad
 // pytest page (section 5.2) with the recomputation strategy of the PyPTO BSA
@@ -25,7 +25,7 @@
 // The operands read transposed (dO^T, Q^T, K^T) come from row-major LDS tiles
 // through ds_read_b64_tr_b16, in the key (query) order in which the
 // accumulator holds P and dS, so the contraction pairs the right elements.
-// Each LDS tile is 32 rows x 128, stored once with its 16-byte chunks
+// Each LDS tile is 32 rows x D, stored once with its 16-byte chunks
 // XOR-swizzled so that both the row reads and the transposing reads are free
 // of bank conflicts (bsw below).
 #include <hip/hip_runtime.h>
@@ -40,40 +40,53 @@
 namespace fa {
 namespace {
 
-constexpr int BD = 128;    // head dim
 constexpr int TR = 32;     // rows of an LDS tile
 constexpr int NWB = 4;     // 32-key groups per dK/dV workgroup (two waves each)
 constexpr int BLK = 32 * NWB;  // keys per dK/dV workgroup
 constexpr int NWQ = 8;         // waves per dQ workgroup (two per SIMD)
 constexpr int BLKQ = 32 * NWQ;  // query rows per dQ workgroup
 
-// One chunk swizzle serves both read patterns of a tile: the row reads
-// (16 consecutive rows, one chunk each, per 256 bytes) see 16 distinct
-// chunk positions since the XOR term is a bijection of row & 15, and the
-// transposing reads (4 consecutive rows x 4 consecutive chunks) see 16
-// distinct positions since bits 2..3 of the XOR term differ between the
-// four rows of an aligned group.
-__device__ __forceinline__ int bsw(int row, int ch) { return ch ^ (((row & 3) << 2) | ((row >> 2) & 3)); }
+// One chunk swizzle serves both read patterns of a tile (256 bytes of LDS
+// banks, 16 chunk positions).
+// D = 128 (one row per 256 bytes): the row reads (16 consecutive rows, one
+// chunk each) see 16 distinct chunk positions since the XOR term is a
+// bijection of row & 15, and the transposing reads (4 consecutive rows x 4
+// consecutive chunks) see 16 distinct positions since bits 2..3 of the XOR
+// term differ between the four rows of an aligned group.
+// D = 64 (two rows per 256 bytes, row parity picks the half): among 16
+// consecutive rows the 8 of one parity get distinct XOR terms (a bijection
+// of (row >> 1) & 7), so the row reads see 16 distinct positions; in an
+// aligned group of 4 rows the two rows of one parity differ in bit 2 of the
+// XOR term, so their 4 consecutive chunks land in opposite halves of the
+// row and the transposing reads see 16 distinct positions too.
+template <int BD>
+__device__ __forceinline__ int bsw(int row, int ch) {
+  if constexpr (BD == 128) return ch ^ (((row & 3) << 2) | ((row >> 2) & 3));
+  return ch ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
 
 // A operand "rows": lane (c, h) holds tile row c, columns 16 ks + 8 h .. +7.
+template <int BD>
 __device__ __forceinline__ u32x4 row_op(const uint16_t* t, int ks) {
   const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
-  return *(const u32x4*)(t + c * BD + bsw(c, 2 * ks + h) * 8);
+  return *(const u32x4*)(t + c * BD + bsw<BD>(c, 2 * ks + h) * 8);
 }
 // A operand "transposed": M index = tile column 32 dt + (lane & 31); the 8 k
 // values of lane half h are tile rows 16 ks + 4 h + 0..3 and 16 ks + 8 + 4 h
 // + 0..3, the order in which a 32x32 accumulator holds its rows.
+template <int BD>
 __device__ __forceinline__ u32x4 tr_op(const uint16_t* t, int dt, int ks) {
   const int lane = threadIdx.x & 63, h = lane >> 5;
   const int vrow = 4 * h + ((lane & 15) >> 2);
   const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int r0 = 16 * ks + vrow, r1 = r0 + 8;
-  const u32x2 lo = lds_read_tr16(t + r0 * BD + bsw(r0, col >> 3) * 8 + (col & 7));
-  const u32x2 hi = lds_read_tr16(t + r1 * BD + bsw(r1, col >> 3) * 8 + (col & 7));
+  const u32x2 lo = lds_read_tr16(t + r0 * BD + bsw<BD>(r0, col >> 3) * 8 + (col & 7));
+  const u32x2 hi = lds_read_tr16(t + r1 * BD + bsw<BD>(r1, col >> 3) * 8 + (col & 7));
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 // B operand from global memory: lane (c, h) holds row r of a row-major
-// matrix, columns 16 ks + 8 h .. +7, for the 8 k-steps over the head dim.
+// matrix, columns 16 ks + 8 h .. +7, for the D / 16 k-steps over the head dim.
+template <int BD>
 __device__ __forceinline__ void load_bop(u32x4 (&op)[BD / 16], const uint16_t* base, int64_t stride, int r) {
   const int h = (threadIdx.x & 63) >> 5;
 #pragma unroll
@@ -89,7 +102,7 @@ __device__ __forceinline__ u32x4 pack_b(const f32x16& a, int ks) {
 // Stores accumulator tiles acc[dt] (rows = head dim 32 dt + ..., column =
 // lane's row r of the output) times mul as 16-bit values: 4 consecutive
 // elements per store.
-template <class T>
+template <class T, int BD>
 __device__ __forceinline__ void store_t(uint16_t* base, int64_t stride, int r, const f32x16 (&acc)[BD / 32], float mul) {
   const int h = (threadIdx.x & 63) >> 5;
 #pragma unroll
@@ -140,9 +153,9 @@ __device__ __forceinline__ void phase_end() {
 // 2s + 1; dO(s)^T in phase 2s + 1 (for M_P(s + 1)) and Q(s)^T in phase
 // 2s + 2 (for M_D(s + 1)). The tiles live in a four-deep
 // LDS ring (slot s % 4), copied HBM -> LDS by LDS-DMA (no register staging)
-// by the P waves: at the start of phase 2t + 1 P wave g issues 4 KB of the
-// tiles of step t + 3 (tile g / 2, chunk positions 64 (4 (g % 2) + n) +
-// lane, n = 0..3; the swizzle is an involution, so a lane fetches the
+// by the P waves: at the start of phase 2t + 1 P wave g issues half a tile
+// of step t + 3 (tile g / 2, chunk positions 64 (NPW (g % 2) + n) + lane,
+// n < NPW = D / 32; the swizzle is an involution, so a lane fetches the
 // logical chunk its position holds) into the slot of step t - 1, read last
 // in phase 2t, and at the end of phase 2t it waits for its copies of step
 // t + 1. S and dP start from -LSE / scale and -Delta of their rows (so V_P
@@ -150,9 +163,12 @@ __device__ __forceinline__ void phase_end() {
 // with no LDS read before them); these values of step s + 2 are loaded by
 // wave 4 into registers during step s, stored into their ring slot at its
 // end, and read at the start of the M phases of step s + 2.
-template <class T, bool CAUSAL, bool MASK>
+template <class T, int BD, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NB = 4;  // ring depth
+  constexpr int DT = BD / 32;   // 32-wide d tiles
+  constexpr int CPR = BD / 8;   // 16-byte chunks per tile row
+  constexpr int NPW = BD / 32;  // copy instructions per P wave and step (half a tile)
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[NB][2][TR * BD];
   __shared__ __attribute__((aligned(16))) float sLD[NB][2 * TR];  // -LSE / scale, then -Delta
   __shared__ __attribute__((aligned(16))) float pex[4][4][64][4];  // P of each key group
@@ -174,10 +190,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   const uint16_t* kg = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh;
   const uint16_t* vg = (const uint16_t*)p.v + (int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh;
   u32x4 kv_op[BD / 16];  // K (P wave) or V (dS wave) rows of the lane's key
-  load_bop(kv_op, dswave ? vg : kg, dswave ? p.v_ss : p.k_ss, min(key, p.Skv - 1));
-  f32x16 acc[BD / 32];  // dV^T (P wave) or dK^T (dS wave)
+  load_bop<BD>(kv_op, dswave ? vg : kg, dswave ? p.v_ss : p.k_ss, min(key, p.Skv - 1));
+  f32x16 acc[DT];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
-  for (int dt = 0; dt < BD / 32; ++dt)
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
   // Query rows that can see a key of this block: i >= k0 - diag (causal).
@@ -197,27 +213,27 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   // P wave copies: tile (w & 3) / 2 (0 Q, 1 dO); per instruction the tile
   // row and the byte offset of the logical chunk.
   const bool c_do = (wu & 2) != 0;
-  int crow[4];
-  uint32_t cchunk[4];
+  int crow[NPW];
+  uint32_t cchunk[NPW];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int pos = 64 * (4 * (wu & 1) + n) + lane, row = pos >> 4;
+  for (int n = 0; n < NPW; ++n) {
+    const int pos = 64 * (NPW * (wu & 1) + n) + lane, row = pos / CPR;
     crow[n] = row;
-    cchunk[n] = (uint32_t)(bsw(row, pos & 15) * 16);
+    cchunk[n] = (uint32_t)(bsw<BD>(row, pos % CPR) * 16);
   }
   const int64_t c_ss = c_do ? p.do_ss : p.q_ss, c_sh = c_do ? p.do_sh : p.q_sh;
   // the group's first query head
   const uint16_t* c_head = c_do ? (const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hkv * p.G * p.do_sh
                                 : (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hkv * p.G * p.q_sh;
   const uint32_t c_rb = (uint32_t)c_ss * 2u;
-  const uint32_t c_lds = lds_addr_of(sbuf[0][c_do ? 1 : 0]) + (wu & 1) * 4096;
+  const uint32_t c_lds = lds_addr_of(sbuf[0][c_do ? 1 : 0]) + (wu & 1) * (NPW * 1024);
   auto dma = [&](int hh, int tt, int sl) __attribute__((always_inline)) {
     const int q0 = qfirst + tt * TR;
     const uint16_t* base = c_head + (int64_t)hh * c_sh + (int64_t)q0 * c_ss;
     const int rmax = p.Sq - 1 - q0;  // rows past Sq fetch row Sq - 1
     const uint32_t l0 = c_lds + (uint32_t)sl * (2 * TR * BD * 2);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) lds_copy16(base, (uint32_t)min(crow[n], rmax) * c_rb + cchunk[n], l0 + n * 1024);
+    for (int n = 0; n < NPW; ++n) lds_copy16(base, (uint32_t)min(crow[n], rmax) * c_rb + cchunk[n], l0 + n * 1024);
   };
   // Wave 4: lane i < 32 loads LSE of row q0 + i, lane 32 + i Delta; the
   // stored values (-LSE / scale and -Delta, the initial values of the S and
@@ -239,11 +255,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   u32x4 ar[BD / 16], at[BD / 16];
   auto read_rows = [&](const uint16_t* t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < BD / 16; ++ks) ar[ks] = row_op(t, ks);
+    for (int ks = 0; ks < BD / 16; ++ks) ar[ks] = row_op<BD>(t, ks);
   };
   auto read_tr = [&](const uint16_t* t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < BD / 16; ++ks) at[ks] = tr_op(t, ks & 3, ks >> 2);
+    for (int ks = 0; ks < BD / 16; ++ks) at[ks] = tr_op<BD>(t, ks % DT, ks / DT);
   };
   if (nsteps > 0) {
     if (!dswave) {
@@ -255,9 +271,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
         }
       // h_ahd, t_ahd: step 3; the copies of step 0 are complete
       if (nsteps > 2)
-        wait_vmem_below<8>();
+        wait_vmem_below<2 * NPW>();
       else if (nsteps > 1)
-        wait_vmem_below<4>();
+        wait_vmem_below<NPW>();
       else
         wait_vmem();
     } else {
@@ -296,7 +312,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
       if (DU) {
 #pragma unroll
-        for (int ks = 0; ks < BD / 16; ++ks) acc[ks & 3] = T::mfma(at[ks], pb[ks >> 2], acc[ks & 3]);
+        for (int ks = 0; ks < BD / 16; ++ks) acc[ks % DT] = T::mfma(at[ks], pb[ks / DT], acc[ks % DT]);
       }
       if (DS) {
 #pragma unroll
@@ -305,7 +321,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       // This wave's copies of step s + 1 are complete (those of step s + 2
       // may still fly).
       if (s + 2 < nsteps)
-        wait_vmem_below<4>();
+        wait_vmem_below<NPW>();
       else
         wait_vmem();
       phase_end();
@@ -387,7 +403,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
       if (DU) {
 #pragma unroll
-        for (int ks = 0; ks < BD / 16; ++ks) acc[ks & 3] = T::mfma(at[ks], db[ks >> 2], acc[ks & 3]);
+        for (int ks = 0; ks < BD / 16; ++ks) acc[ks % DT] = T::mfma(at[ks], db[ks / DT], acc[ks % DT]);
       }
       if (DS) {
 #pragma unroll
@@ -405,14 +421,17 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   }
   if (key < p.Skv) {
     if (dswave)
-      store_t<T>((uint16_t*)p.dk + (int64_t)b * p.dk_sb + (int64_t)hkv * p.dk_sh, p.dk_ss, key, acc, p.scale);
+      store_t<T, BD>((uint16_t*)p.dk + (int64_t)b * p.dk_sb + (int64_t)hkv * p.dk_sh, p.dk_ss, key, acc, p.scale);
     else
-      store_t<T>((uint16_t*)p.dv + (int64_t)b * p.dv_sb + (int64_t)hkv * p.dv_sh, p.dv_ss, key, acc, 1.f);
+      store_t<T, BD>((uint16_t*)p.dv + (int64_t)b * p.dv_sb + (int64_t)hkv * p.dv_sh, p.dv_ss, key, acc, 1.f);
   }
 }
 
-template <class T, bool CAUSAL, bool MASK>
+template <class T, int BD, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
+  constexpr int DT = BD / 32;   // 32-wide d tiles
+  constexpr int CPR = BD / 8;   // 16-byte chunks per tile row
+  constexpr int NPQ = BD / 64;  // copy instructions per wave and tile (a quarter tile)
   // Three slots of the K and V tiles (K read both ways, V by rows).
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[3][2][TR * BD];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
@@ -432,8 +451,8 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
   const uint16_t* kg = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh;
   const uint16_t* vg = (const uint16_t*)p.v + (int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh;
   u32x4 qop[BD / 16], dop[BD / 16];
-  load_bop(qop, qg, p.q_ss, min(qi, p.Sq - 1));
-  load_bop(dop, dg, p.do_ss, min(qi, p.Sq - 1));
+  load_bop<BD>(qop, qg, p.q_ss, min(qi, p.Sq - 1));
+  load_bop<BD>(dop, dg, p.do_ss, min(qi, p.Sq - 1));
   // S^T and dP^T start from -LSE / scale and -Delta of the lane's row, so
   // that P = exp2(S^T scale log2e) and dS^T = P dP^T; padding rows and rows
   // without keys start from +inf (their elements are masked).
@@ -473,47 +492,47 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
     s_init = l == -INFINITY ? INFINITY : -l / p.scale;
     d_init = -delta;
   }
-  f32x16 dq_t[BD / 32];
+  f32x16 dq_t[DT];
 #pragma unroll
-  for (int dt = 0; dt < BD / 32; ++dt)
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dq_t[dt][i] = 0.f;
   // Keys any row of this block sees: j <= q0 + BLKQ - 1 + diag (causal).
   const int kend = q0 >= Lq ? 0 : CAUSAL ? max(0, min(Lk, q0 + BLKQ + diag)) : Lk;
   const int nkt = (kend + TR - 1) / TR;
   // K and V tiles: a three-deep LDS ring (slot t % 3) filled by LDS-DMA two
-  // tiles ahead: wave w copies 2 KB of tile t + 2 (K for w < 4, V for
-  // w >= 4; chunk positions 64 (2 (w % 4) + n) + lane, n = 0..1) at the
+  // tiles ahead: wave w copies a quarter of tile t + 2 (K for w < 4, V for
+  // w >= 4; chunk positions 64 (NPQ (w % 4) + n) + lane, n < NPQ) at the
   // start of step t into the slot of tile t - 1 (every wave passed the
   // barrier that ended its step), and waits for its copies of tile t + 1 at
   // the end of step t. Rows at or past Skv fetch row Skv - 1.
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const bool c_v = wu >= 4;
-  int crow[2];
-  uint32_t cchunk[2];
+  int crow[NPQ];
+  uint32_t cchunk[NPQ];
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int pos = 64 * (2 * (wu & 3) + n) + lane, row = pos >> 4;
+  for (int n = 0; n < NPQ; ++n) {
+    const int pos = 64 * (NPQ * (wu & 3) + n) + lane, row = pos / CPR;
     crow[n] = row;
-    cchunk[n] = (uint32_t)(bsw(row, pos & 15) * 16);
+    cchunk[n] = (uint32_t)(bsw<BD>(row, pos % CPR) * 16);
   }
   const int64_t c_ss = c_v ? p.v_ss : p.k_ss;
   const uint16_t* c_head = c_v ? vg : kg;
   const uint32_t c_rb = (uint32_t)c_ss * 2u;
-  const uint32_t c_lds = lds_addr_of(sbuf[0][c_v ? 1 : 0]) + (wu & 3) * 2048;
+  const uint32_t c_lds = lds_addr_of(sbuf[0][c_v ? 1 : 0]) + (wu & 3) * (NPQ * 1024);
   auto dma = [&](int t, int sl) __attribute__((always_inline)) {
     const int j0 = t * TR;
     const uint16_t* base = c_head + (int64_t)j0 * c_ss;
     const int rmax = p.Skv - 1 - j0;
     const uint32_t l0 = c_lds + (uint32_t)sl * (2 * TR * BD * 2);
 #pragma unroll
-    for (int n = 0; n < 2; ++n) lds_copy16(base, (uint32_t)min(crow[n], rmax) * c_rb + cchunk[n], l0 + n * 1024);
+    for (int n = 0; n < NPQ; ++n) lds_copy16(base, (uint32_t)min(crow[n], rmax) * c_rb + cchunk[n], l0 + n * 1024);
   };
   if (nkt > 0) {
     dma(0, 0);
     if (nkt > 1) {
       dma(1, 1);
-      wait_vmem_below<2>();
+      wait_vmem_below<NPQ>();
     } else {
       wait_vmem();
     }
@@ -537,8 +556,8 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int ks = 0; ks < BD / 16; ++ks) {
-      s0 = T::mfma(row_op(sKr, ks), qop[ks], s0);
-      dp0 = T::mfma(row_op(sVr, ks), dop[ks], dp0);
+      s0 = T::mfma(row_op<BD>(sKr, ks), qop[ks], s0);
+      dp0 = T::mfma(row_op<BD>(sVr, ks), dop[ks], dp0);
     }
     // Element i: key j0 + r, r = 8 (i / 4) + 4 h + i % 4; query row qi.
     // A block whose keys all exist and are seen by every row of the wave
@@ -564,30 +583,30 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
     for (int ks = 0; ks < TR / 16; ++ks) {
       const u32x4 db = pack_b<T>(dsm, ks);
 #pragma unroll
-      for (int dt = 0; dt < BD / 32; ++dt) dq_t[dt] = T::mfma(tr_op(sKt, dt, ks), db, dq_t[dt]);
+      for (int dt = 0; dt < DT; ++dt) dq_t[dt] = T::mfma(tr_op<BD>(sKt, dt, ks), db, dq_t[dt]);
     }
     // this wave's copies of tile t + 1 are complete (tile t + 2 may fly)
     if (t + 2 < nkt)
-      wait_vmem_below<2>();
+      wait_vmem_below<NPQ>();
     else
       wait_vmem();
     sl = sl == 2 ? 0 : sl + 1;
   }
-  if (qi < p.Sq) store_t<T>((uint16_t*)p.dq + (int64_t)b * p.dq_sb + (int64_t)hq * p.dq_sh, p.dq_ss, qi, dq_t, p.scale);
+  if (qi < p.Sq) store_t<T, BD>((uint16_t*)p.dq + (int64_t)b * p.dq_sb + (int64_t)hq * p.dq_sh, p.dq_ss, qi, dq_t, p.scale);
 }
 
-template <class T, bool CAUSAL, bool MASK>
+template <class T, int BD, bool CAUSAL, bool MASK>
 hipError_t launch_bwd_t(BwdParams& p, hipStream_t st) {
   // The dQ kernel also writes Delta, which the dK/dV kernel reads.
   const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
   if (rows > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, CAUSAL, MASK>), dim3((unsigned)((p.Sq + BLKQ - 1) / BLKQ), (unsigned)(p.B * p.Hq)),
+    hipLaunchKernelGGL((bwd_dq_kernel<T, BD, CAUSAL, MASK>), dim3((unsigned)((p.Sq + BLKQ - 1) / BLKQ), (unsigned)(p.B * p.Hq)),
                        dim3(64 * NWQ), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.Skv > 0 && p.B * p.Hkv > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, CAUSAL, MASK>), dim3((unsigned)((p.Skv + BLK - 1) / BLK), (unsigned)(p.B * p.Hkv)),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, BD, CAUSAL, MASK>), dim3((unsigned)((p.Skv + BLK - 1) / BLK), (unsigned)(p.B * p.Hkv)),
                        dim3(512), 0, st, p);
   }
   return hipGetLastError();
@@ -595,15 +614,16 @@ hipError_t launch_bwd_t(BwdParams& p, hipStream_t st) {
 
 }  // namespace
 
-template <class T>
+template <class T, int BD>
 hipError_t launch_bwd_m(bool causal, bool mask, BwdParams& p, hipStream_t st) {
-  if (mask) return causal ? launch_bwd_t<T, true, true>(p, st) : launch_bwd_t<T, false, true>(p, st);
-  return causal ? launch_bwd_t<T, true, false>(p, st) : launch_bwd_t<T, false, false>(p, st);
+  if (mask) return causal ? launch_bwd_t<T, BD, true, true>(p, st) : launch_bwd_t<T, BD, false, true>(p, st);
+  return causal ? launch_bwd_t<T, BD, true, false>(p, st) : launch_bwd_t<T, BD, false, false>(p, st);
 }
 
-hipError_t launch_bwd(Dt dt, bool causal, bool mask, BwdParams& p, hipStream_t stream) {
-  if (dt == Dt::BF16) return launch_bwd_m<BF16>(causal, mask, p, stream);
-  return launch_bwd_m<F16>(causal, mask, p, stream);
+hipError_t launch_bwd(Dt dt, int d, bool causal, bool mask, BwdParams& p, hipStream_t stream) {
+  if (dt == Dt::BF16)
+    return d == 64 ? launch_bwd_m<BF16, 64>(causal, mask, p, stream) : launch_bwd_m<BF16, 128>(causal, mask, p, stream);
+  return d == 64 ? launch_bwd_m<F16, 64>(causal, mask, p, stream) : launch_bwd_m<F16, 128>(causal, mask, p, stream);
 }
 
 }  // namespace fa

@@ -139,6 +139,6 @@ constexpr int kMaxDevices = 64;
 // up once per device, with that device current).
 hipError_t scratch_address(float** ptr);
 hipError_t launch_topk(Dt dt, TopkParams& p, hipStream_t stream);
-hipError_t launch_bwd(Dt dt, bool causal, bool mask, BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd(Dt dt, int d, bool causal, bool mask, BwdParams& p, hipStream_t stream);
 
 }  // namespace fa

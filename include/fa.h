@@ -188,7 +188,7 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
  * BSA README (section 3); dK and dV are summed over the query heads of each KV
  * head (BSA README, section 1).
  *
- *  q, k, v     as fa_fwd (f16 or bf16, D == Dv == 128)
+ *  q, k, v     as fa_fwd (f16 or bf16, D == Dv, 64 or 128)
  *  mask        NULL or a boolean mask in one of fa_fwd's forms (non-zero =
  *              excluded); P is 0 at excluded positions, so they receive no
  *              gradient (the atten_mask input of the FlashAttentionScoreGrad
@@ -214,8 +214,8 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
  *
  * Every tensor's rows must start 16-byte aligned (as fa_fwd). Rows without
  * keys (LSE = -inf) contribute nothing. Returns FA_ERR_UNSUPPORTED for other
- * head dims or fp32; the library allocates nothing and enqueues three kernels
- * on `stream`.
+ * head dims or fp32; the library allocates nothing and enqueues two kernels
+ * on `stream` (dQ with Delta, then dK and dV).
  */
 fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* mask,
                  const fa_tensor* seqlens_q, const fa_tensor* seqlens_k, const fa_tensor* o,

@@ -170,7 +170,8 @@ def test_bwd_validation(lib):
                                     0.1, R(delta), R(dq), R(dk), R(dv), None))
 
     assert bw(dt=fa.FA_F32) == "FA_ERR_UNSUPPORTED"
-    assert bw(D=64) == "FA_ERR_UNSUPPORTED"
+    assert bw(D=96) == "FA_ERR_UNSUPPORTED"
+    assert bw(D=64, B=0) == "FA_OK"  # head dim 64 is accepted
     assert bw(dq_shape=[2, 4, 63, 128]) == "FA_ERR_SHAPE"
     assert bw(delta_dt=fa.FA_BF16) == "FA_ERR_DTYPE"
     assert bw(causal=2) == "FA_ERR_VALUE"

@@ -1,4 +1,4 @@
-"""GPU parity of fa_bwd (dense, causal, boolean mask, GQA; f16 / bf16, D = 128) against the
+"""GPU parity of fa_bwd (dense, causal, boolean mask, GQA; f16 / bf16, D = 64 and 128) against the
 fp64 backward oracle, element by element, on seeded inputs.
 
 Per-element gate (no page states one for the backward; derived here): the GPU
@@ -48,12 +48,12 @@ def _check(case, got, ref, bound, dtype, n_terms):
     assert np.all(g[zero] == 0.0), case
 
 
-def run_bwd(case, B, Hq, Hkv, Sq, Skv, dtype, causal, seed, mask_fn=None, sq=None, sk=None):
-    g0, q, k, v = synth.dense_inputs(seed, B, Hq, Hkv, Sq, Skv, 128, 128, dtype)
+def run_bwd(case, B, Hq, Hkv, Sq, Skv, dtype, causal, seed, mask_fn=None, sq=None, sk=None, D=128):
+    g0, q, k, v = synth.dense_inputs(seed, B, Hq, Hkv, Sq, Skv, D, D, dtype)
     mask = mask_fn(g0) if mask_fn else None
     g = synth.rng(seed + 1000)
-    dout = synth.cast(synth.normal(g, (B, Hq, Sq, 128)), q.dtype)
-    scale = 1 / math.sqrt(128)
+    dout = synth.cast(synth.normal(g, (B, Hq, Sq, D)), q.dtype)
+    scale = 1 / math.sqrt(D)
     qg, kg, vg, dg, mg = gpu(q, k, v, dout, mask)
     sqg, skg = gpu(sq, sk)
     o, lse = fa.fa_fwd(qg, kg, vg, scale=scale, causal=causal, mask=mg, seqlens_q=sqg, seqlens_k=skg)
@@ -75,6 +75,28 @@ def test_bwd_ragged_gqa(dtype, causal):
     # 200 rows / keys: several 32-row tiles and a ragged tail in both
     # directions; two query heads per KV head.
     run_bwd("bwd_%s_causal%d" % (dtype, causal), 2, 4, 2, 200, 200, dtype, causal, 60 + causal)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_head_dim_64(dtype, causal):
+    # D = 64: its own tile swizzle and copy split; ragged rows and keys, two
+    # query heads per KV head, Sq != Skv.
+    run_bwd("bwd_d64_%s_causal%d" % (dtype, causal), 2, 4, 2, 170, 230, dtype, causal, 110 + causal, D=64)
+
+
+def test_bwd_head_dim_64_mask_and_lengths():
+    # D = 64 with a per-head boolean mask and per-batch lengths (padded rows
+    # and keys get exact zeros).
+    sq = torch.tensor([150, 61], dtype=torch.int32)
+    sk = torch.tensor([140, 200], dtype=torch.int32)
+
+    def mh(g):
+        return torch.from_numpy((g.random((1, 4, 150, 200)) < np.array([0.2, 0.4, 0.1, 0.6])[None, :, None, None])
+                                .astype(np.uint8))
+    dq, dk, dv = run_bwd("bwd_d64_mask_lengths", 2, 4, 2, 150, 200, "bf16", True, 113, mask_fn=mh, sq=sq, sk=sk,
+                         D=64)
+    assert torch.all(dq[1, :, 61:] == 0) and torch.all(dk[0, :, 140:] == 0) and torch.all(dv[0, :, 140:] == 0)
 
 
 @pytest.mark.parametrize("sq,skv", [(100, 300), (300, 100), (129, 129)])
