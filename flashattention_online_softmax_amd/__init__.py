@@ -12,7 +12,8 @@ Functions (same names as the C entry points):
   fa_fwd_blocksparse(q, k, v, block_idx, scale=..., block_q=128, block_k=128, seqlens=None,
                      rescale_threshold=0.0)
   fa_fwd_topk_gather(q, k, v, idx, scale=...)
-each returning (o, lse).
+each returning (o, lse); also fa_fwd_varlen, fa_fwd_splitkv(_noalloc) and the
+backward fa_bwd / fa_bwd_varlen, returning (dq, dk, dv).
 """
 import ctypes
 import os
@@ -68,6 +69,8 @@ def load():
                                ctypes.c_void_p]
         lib.fa_fwd_varlen.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float,
                                       P, P, ctypes.c_void_p]
+        lib.fa_bwd_varlen.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int, P, P, P, P, ctypes.c_int,
+                                      ctypes.c_float, P, P, P, P, ctypes.c_void_p]
         lib.fa_fwd_splitkv.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_int,
                                        P, P, P, ctypes.c_void_p]
         lib.fa_fwd_splitkv_noalloc.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_float, ctypes.c_float,
@@ -78,7 +81,7 @@ def load():
         lib.fa_fwd_splitkv_workspace_elems.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int]
         lib.fa_fwd_splitkv_workspace_elems.restype = ctypes.c_int64
         for f in (lib.fa_fwd, lib.fa_fwd_blocksparse, lib.fa_fwd_topk_gather, lib.fa_bwd, lib.fa_fwd_varlen,
-                  lib.fa_fwd_splitkv):
+                  lib.fa_fwd_splitkv, lib.fa_bwd_varlen):
             f.restype = ctypes.c_int
         lib.fa_status_str.argtypes = [ctypes.c_int]
         lib.fa_status_str.restype = ctypes.c_char_p
@@ -253,6 +256,30 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, *, scale, c
                              _ref(describe(cu_seqlens_k)), int(max_seqlen_q), int(bool(causal)), float(scale),
                              float(rescale_threshold), _ref(describe(out)), _ref(describe(lse)), _stream(stream)))
     return out, lse
+
+
+def fa_bwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, o, lse, dout, *, scale,
+                  causal=False, o_lo=None, dq=None, dk=None, dv=None, delta=None, stream=None):
+    """Gradients (dq, dk, dv) of the packed variable-length (TND) forward:
+    q [Tq,Hq,D], k/v [Tk,Hkv,D], cu_seqlens int32 [B+1] on the GPU, o / lse
+    from fa_fwd_varlen, dout [Tq,Hq,Dv]. Rows and keys outside every sequence
+    are not written (the outputs allocated here start as zeros)."""
+    lib = load()
+    _need_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, dout, o_lo)
+    if dq is None:
+        dq = torch.zeros_like(q)
+    if dk is None:
+        dk = torch.zeros_like(k)
+    if dv is None:
+        dv = torch.zeros_like(v)
+    if delta is None:
+        delta = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    _check(lib.fa_bwd_varlen(_ref(describe(q)), _ref(describe(k)), _ref(describe(v)), _ref(describe(cu_seqlens_q)),
+                             _ref(describe(cu_seqlens_k)), int(max_seqlen_q), int(max_seqlen_k), _ref(describe(o)),
+                             _ref(describe(o_lo)), _ref(describe(lse)), _ref(describe(dout)), int(bool(causal)),
+                             float(scale), _ref(describe(delta)), _ref(describe(dq)), _ref(describe(dk)),
+                             _ref(describe(dv)), _stream(stream)))
+    return dq, dk, dv
 
 
 def splitkv_splits(B, Hq, Sq, Skv, num_splits=0):

@@ -474,6 +474,102 @@ fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
   return hip_status(fa::launch_bwd(to_dt(q->dtype), (int)q->shape[3], causal != 0, has_mask, p, (hipStream_t)stream));
 }
 
+fa_status fa_bwd_varlen(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* cu_seqlens_q,
+                        const fa_tensor* cu_seqlens_k, int max_seqlen_q, int max_seqlen_k, const fa_tensor* o,
+                        const fa_tensor* o_lo, const fa_tensor* lse, const fa_tensor* dout, int causal, float scale,
+                        const fa_tensor* delta, const fa_tensor* dq, const fa_tensor* dk, const fa_tensor* dv,
+                        void* stream) {
+  clear_error();
+  fa_status s;
+  const char* names3[9] = {"q", "k", "v", "o", "dout", "dq", "dk", "dv", nullptr};
+  const fa_tensor* ts3[8] = {q, k, v, o, dout, dq, dk, dv};
+  for (int t = 0; t < 8; ++t)
+    if ((s = check_tensor(names3[t], ts3[t], 3, true)) != FA_OK) return s;
+  if ((s = check_tensor("lse", lse, 2, false)) != FA_OK) return s;
+  if ((s = check_tensor("delta", delta, 2, false)) != FA_OK) return s;
+  if ((s = check_tensor("cu_seqlens_q", cu_seqlens_q, 1, false)) != FA_OK) return s;
+  if ((s = check_tensor("cu_seqlens_k", cu_seqlens_k, 1, false)) != FA_OK) return s;
+  if (q->dtype != FA_F16 && q->dtype != FA_BF16)
+    return fail(FA_ERR_DTYPE, "q dtype must be f16 or bf16, got %s", dtype_name(q->dtype));
+  for (int t = 1; t < 8; ++t)
+    if ((s = check_dtype(names3[t], ts3[t], q->dtype)) != FA_OK) return s;
+  if ((s = check_dtype("lse", lse, FA_F32)) != FA_OK) return s;
+  if ((s = check_dtype("delta", delta, FA_F32)) != FA_OK) return s;
+  if ((s = check_dtype("cu_seqlens_q", cu_seqlens_q, FA_I32)) != FA_OK) return s;
+  if ((s = check_dtype("cu_seqlens_k", cu_seqlens_k, FA_I32)) != FA_OK) return s;
+  const int64_t Tq = q->shape[0], Hq = q->shape[1], D = q->shape[2];
+  const int64_t Tk = k->shape[0], Hkv = k->shape[1], Dv = v->shape[2];
+  const int64_t nb = cu_seqlens_q->shape[0];
+  if (nb < 1 || cu_seqlens_k->shape[0] != nb)
+    return fail(FA_ERR_SHAPE, "cu_seqlens_q and cu_seqlens_k must both have B + 1 >= 1 entries");
+  if (k->shape[2] != D) return fail(FA_ERR_SHAPE, "k head dim differs from q's");
+  if (v->shape[0] != Tk || v->shape[1] != Hkv) return fail(FA_ERR_SHAPE, "v must match k in rows and heads");
+  for (int i = 0; i < 3; ++i) {
+    const int64_t ow = i == 2 ? Dv : q->shape[i];
+    if (o->shape[i] != ow || dout->shape[i] != ow) return fail(FA_ERR_SHAPE, "o and dout must be [Tq, Hq, Dv]");
+    if (dq->shape[i] != q->shape[i]) return fail(FA_ERR_SHAPE, "dq must be shaped like q");
+    if (dk->shape[i] != k->shape[i]) return fail(FA_ERR_SHAPE, "dk must be shaped like k");
+    if (dv->shape[i] != v->shape[i]) return fail(FA_ERR_SHAPE, "dv must be shaped like v");
+  }
+  if (lse->shape[0] != Tq || lse->shape[1] != Hq) return fail(FA_ERR_SHAPE, "lse must be [Tq, Hq]");
+  if (delta->shape[0] != Tq || delta->shape[1] != Hq) return fail(FA_ERR_SHAPE, "delta must be [Tq, Hq]");
+  if ((s = check_contiguous("lse", lse)) != FA_OK) return s;
+  if ((s = check_contiguous("delta", delta)) != FA_OK) return s;
+  if ((s = check_o_lo(o_lo, o)) != FA_OK) return s;
+  if (Hkv == 0 && Tq * Hq > 0) return fail(FA_ERR_SHAPE, "k has no heads");
+  if (Hkv > 0 && Hq % Hkv != 0) return fail(FA_ERR_SHAPE, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_VALUE, "causal must be 0 or 1");
+  if (max_seqlen_q < 0 || max_seqlen_k < 0) return fail(FA_ERR_VALUE, "max_seqlen_q and max_seqlen_k must be >= 0");
+  if (!scale_ok(scale)) return fail(FA_ERR_VALUE, "scale must be finite and > 0");
+  if (D != Dv) return fail(FA_ERR_UNSUPPORTED, "D (%lld) != Dv (%lld) is not supported", (long long)D, (long long)Dv);
+  if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "the backward supports head dim 64 or 128 (got %lld)", (long long)D);
+  if (!fits_i32(Tq) || !fits_i32(Tk) || !fits_i32(nb * Hq) || !fits_i32(Tq * Hq))
+    return fail(FA_ERR_UNSUPPORTED, "problem too large for 32-bit row indexing");
+  // Tiles are fetched with 32-bit per-lane offsets from the tile start.
+  for (int t = 0; t < 5; ++t)
+    if (ts3[t]->stride[0] > (1 << 22))
+      return fail(FA_ERR_UNSUPPORTED, "%s row stride above 2^22 elements is not supported", names3[t]);
+  const int64_t B = nb - 1;
+  // (With keys but no query rows the kernels still run: dk and dv are zero.)
+  if (B * Hq == 0 || ((int64_t)max_seqlen_q == 0 && (int64_t)max_seqlen_k == 0)) return FA_OK;
+  fa::BwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q->data;
+  p.k = k->data;
+  p.v = v->data;
+  p.o = o->data;
+  p.dout = dout->data;
+  p.lse = (const float*)lse->data;
+  p.delta = (float*)delta->data;
+  p.dq = dq->data;
+  p.dk = dk->data;
+  p.dv = dv->data;
+  int64_t* st[8][2] = {{&p.q_sh, &p.q_ss},   {&p.k_sh, &p.k_ss},   {&p.v_sh, &p.v_ss},   {&p.o_sh, &p.o_ss},
+                       {&p.do_sh, &p.do_ss}, {&p.dq_sh, &p.dq_ss}, {&p.dk_sh, &p.dk_ss}, {&p.dv_sh, &p.dv_ss}};
+  for (int t = 0; t < 8; ++t) {
+    *st[t][0] = ts3[t]->stride[1];
+    *st[t][1] = ts3[t]->stride[0];
+  }
+  if (o_lo && numel(o_lo) > 0) {
+    p.o_lo = (const float*)o_lo->data;
+    p.ol_sh = o_lo->stride[1];
+    p.ol_ss = o_lo->stride[0];
+  }
+  p.B = (int32_t)B;
+  p.Hq = (int32_t)Hq;
+  p.Hkv = (int32_t)Hkv;
+  p.G = (int32_t)(Hq / Hkv);
+  p.Sq = max_seqlen_q;
+  p.Skv = max_seqlen_k;
+  p.Tq = (int32_t)Tq;
+  p.Tk = (int32_t)Tk;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.cu_q = (const int32_t*)cu_seqlens_q->data;
+  p.cu_k = (const int32_t*)cu_seqlens_k->data;
+  return hip_status(fa::launch_bwd_varlen(to_dt(q->dtype), (int)D, causal != 0, p, (hipStream_t)stream));
+}
+
 fa_status fa_fwd_varlen(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* cu_seqlens_q,
                         const fa_tensor* cu_seqlens_k, int max_seqlen_q, int causal, float scale,
                         float rescale_threshold, const fa_tensor* o, const fa_tensor* lse, void* stream) {

@@ -10,6 +10,12 @@
 // with dK and dV summed over the query heads of a KV head (BSA README,
 // section 1).
 //
+// Packed variable-length batches (PK): each batch's rows and keys are a range
+// of the packed [T, H, D] tensors given by cu_seqlens (the TND layout of the
+// FlashAttentionScoreGrad pytest page, section 5.4); LSE and Delta are
+// [Tq, Hq]. Rows and keys outside a batch's ranges are neither read as data
+// nor written.
+//
 // Two kernels, none of them with atomics, dQ first (it also forms and stores
 // Delta_i = dO_i . O_i in fp32, which the dK/dV kernel reads):
 //   * dkdv: a workgroup owns 128 keys of one KV head (8 waves: for each 32
@@ -121,6 +127,30 @@ __device__ __forceinline__ void batch_lengths(const BwdParams& p, int b, int& lq
   lk = p.seqlens_k ? max(0, min(p.seqlens_k[b], p.Skv)) : p.Skv;
 }
 
+// Batch b's lengths and its first query row and key in the tensors: 0 and
+// batch_lengths for the padded layout; from cu_seqlens for packed batches,
+// clamped to the tensors' rows (so that offsets past them never address
+// memory) and to the longest lengths the grid covers.
+template <bool PK>
+__device__ __forceinline__ void batch_geometry(const BwdParams& p, int b, int& lq, int& lk, int& qoff, int& koff) {
+  if constexpr (PK) {
+    qoff = min(max(p.cu_q[b], 0), p.Tq);
+    koff = min(max(p.cu_k[b], 0), p.Tk);
+    lq = max(0, min(min(p.cu_q[b + 1], p.Tq) - qoff, p.Sq));
+    lk = max(0, min(min(p.cu_k[b + 1], p.Tk) - koff, p.Skv));
+  } else {
+    qoff = 0;
+    koff = 0;
+    batch_lengths(p, b, lq, lk);
+  }
+}
+// Index of row i of query head hq of batch b in LSE and Delta: [B, Hq, Sq]
+// (padded) or [Tq, Hq] (packed, qoff = the batch's first row).
+template <bool PK>
+__device__ __forceinline__ int64_t ld_index(const BwdParams& p, int b, int hq, int qoff, int i) {
+  return PK ? (int64_t)(qoff + i) * p.Hq + hq : ((int64_t)b * p.Hq + hq) * p.Sq + i;
+}
+
 // End of a phase of the dK/dV kernel: the workgroup barrier, with no
 // instruction of the phase (MFMAs included, which touch no memory) moved
 // past it and none of the next phase moved before it.
@@ -163,7 +193,7 @@ __device__ __forceinline__ void phase_end() {
 // with no LDS read before them); these values of step s + 2 are loaded by
 // wave 4 into registers during step s, stored into their ring slot at its
 // end, and read at the start of the M phases of step s + 2.
-template <class T, int BD, bool CAUSAL, bool MASK>
+template <class T, int BD, bool CAUSAL, bool MASK, bool PK>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NB = 4;  // ring depth
   constexpr int DT = BD / 32;   // 32-wide d tiles
@@ -184,13 +214,18 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   const int bk = lin % nbk, b = bk / p.Hkv, hkv = bk % p.Hkv;
   const int k0 = (lin / nbk) * BLK;
   const int key = k0 + 32 * g + c;  // this lane's key (column of S)
-  int Lq, Lk;
-  batch_lengths(p, b, Lq, Lk);
+  int Lq, Lk, qoff, koff;
+  batch_geometry<PK>(p, b, Lq, Lk, qoff, koff);
+  // A packed batch's key block past its keys has nothing to compute or write
+  // (the rows there belong to the next batch).
+  if (PK && k0 >= Lk) return;
+  // Keys the lanes load and store: the padded tensors' rows, or the batch's.
+  const int klim = PK ? Lk : p.Skv;
   const int diag = Lk - Lq;  // key j is visible to row i iff j <= i + diag
-  const uint16_t* kg = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh;
-  const uint16_t* vg = (const uint16_t*)p.v + (int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh;
+  const uint16_t* kg = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh + (int64_t)koff * p.k_ss;
+  const uint16_t* vg = (const uint16_t*)p.v + (int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh + (int64_t)koff * p.v_ss;
   u32x4 kv_op[BD / 16];  // K (P wave) or V (dS wave) rows of the lane's key
-  load_bop<BD>(kv_op, dswave ? vg : kg, dswave ? p.v_ss : p.k_ss, min(key, p.Skv - 1));
+  load_bop<BD>(kv_op, dswave ? vg : kg, dswave ? p.v_ss : p.k_ss, min(key, klim - 1));
   f32x16 acc[DT];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -223,14 +258,16 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   }
   const int64_t c_ss = c_do ? p.do_ss : p.q_ss, c_sh = c_do ? p.do_sh : p.q_sh;
   // the group's first query head
-  const uint16_t* c_head = c_do ? (const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hkv * p.G * p.do_sh
-                                : (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hkv * p.G * p.q_sh;
+  const uint16_t* c_head =
+      c_do ? (const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hkv * p.G * p.do_sh + (int64_t)qoff * p.do_ss
+           : (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hkv * p.G * p.q_sh + (int64_t)qoff * p.q_ss;
+  const int rlim = PK ? Lq : p.Sq;  // query rows the copies may read
   const uint32_t c_rb = (uint32_t)c_ss * 2u;
   const uint32_t c_lds = lds_addr_of(sbuf[0][c_do ? 1 : 0]) + (wu & 1) * (NPW * 1024);
   auto dma = [&](int hh, int tt, int sl) __attribute__((always_inline)) {
     const int q0 = qfirst + tt * TR;
     const uint16_t* base = c_head + (int64_t)hh * c_sh + (int64_t)q0 * c_ss;
-    const int rmax = p.Sq - 1 - q0;  // rows past Sq fetch row Sq - 1
+    const int rmax = rlim - 1 - q0;  // rows past the last one fetch the last one
     const uint32_t l0 = c_lds + (uint32_t)sl * (2 * TR * BD * 2);
 #pragma unroll
     for (int n = 0; n < NPW; ++n) lds_copy16(base, (uint32_t)min(crow[n], rmax) * c_rb + cchunk[n], l0 + n * 1024);
@@ -243,8 +280,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   const float inv_scale = -1.f / p.scale;
   auto fetch_ld = [&](int hh, int tt) __attribute__((always_inline)) {
     const int hq = hkv * p.G + hh, i = qfirst + tt * TR + c;
-    const int64_t ri = ((int64_t)b * p.Hq + hq) * p.Sq + i;
-    ld = i >= p.Sq ? (h == 0 ? -INFINITY : 0.f) : h == 0 ? p.lse[ri] : p.delta[ri];
+    const int64_t ri = ld_index<PK>(p, b, hq, qoff, i);
+    ld = i >= rlim ? (h == 0 ? -INFINITY : 0.f) : h == 0 ? p.lse[ri] : p.delta[ri];
   };
   auto put_ld = [&](int sl) __attribute__((always_inline)) {
     // rows without keys (LSE = -inf) and padding rows get P = 0 (their
@@ -419,15 +456,17 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       step(nsteps, F{}, U{});
     }
   }
-  if (key < p.Skv) {
+  if (key < klim) {
     if (dswave)
-      store_t<T, BD>((uint16_t*)p.dk + (int64_t)b * p.dk_sb + (int64_t)hkv * p.dk_sh, p.dk_ss, key, acc, p.scale);
+      store_t<T, BD>((uint16_t*)p.dk + (int64_t)b * p.dk_sb + (int64_t)hkv * p.dk_sh + (int64_t)koff * p.dk_ss, p.dk_ss,
+                     key, acc, p.scale);
     else
-      store_t<T, BD>((uint16_t*)p.dv + (int64_t)b * p.dv_sb + (int64_t)hkv * p.dv_sh, p.dv_ss, key, acc, 1.f);
+      store_t<T, BD>((uint16_t*)p.dv + (int64_t)b * p.dv_sb + (int64_t)hkv * p.dv_sh + (int64_t)koff * p.dv_ss, p.dv_ss,
+                     key, acc, 1.f);
   }
 }
 
-template <class T, int BD, bool CAUSAL, bool MASK>
+template <class T, int BD, bool CAUSAL, bool MASK, bool PK>
 __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int DT = BD / 32;   // 32-wide d tiles
   constexpr int CPR = BD / 8;   // 16-byte chunks per tile row
@@ -441,18 +480,22 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
   const int bh = lin % nbh, b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.G;
   const int q0 = (CAUSAL ? (int)gridDim.x - 1 - lin / nbh : lin / nbh) * BLKQ;
   const int qi = q0 + 32 * w + c;  // this lane's query row (column of S^T)
-  int Lq, Lk;
-  batch_lengths(p, b, Lq, Lk);
+  int Lq, Lk, qoff, koff;
+  batch_geometry<PK>(p, b, Lq, Lk, qoff, koff);
+  // A packed batch's row block past its rows has nothing to compute or write.
+  if (PK && q0 >= Lq) return;
+  const int rlim = PK ? Lq : p.Sq;  // rows the lanes load and store
+  const int klim = PK ? Lk : p.Skv;  // keys the tile copies may read
   const int diag = Lk - Lq;
   // mask bytes of the lane's query row (read only where qi < Sq)
   const uint8_t* mq = MASK ? p.mask + (int64_t)b * p.m_sb + (int64_t)hq * p.m_sh + (int64_t)qi * p.m_ss : nullptr;
-  const uint16_t* qg = (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh;
-  const uint16_t* dg = (const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hq * p.do_sh;
-  const uint16_t* kg = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh;
-  const uint16_t* vg = (const uint16_t*)p.v + (int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh;
+  const uint16_t* qg = (const uint16_t*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh + (int64_t)qoff * p.q_ss;
+  const uint16_t* dg = (const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hq * p.do_sh + (int64_t)qoff * p.do_ss;
+  const uint16_t* kg = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh + (int64_t)koff * p.k_ss;
+  const uint16_t* vg = (const uint16_t*)p.v + (int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh + (int64_t)koff * p.v_ss;
   u32x4 qop[BD / 16], dop[BD / 16];
-  load_bop<BD>(qop, qg, p.q_ss, min(qi, p.Sq - 1));
-  load_bop<BD>(dop, dg, p.do_ss, min(qi, p.Sq - 1));
+  load_bop<BD>(qop, qg, p.q_ss, min(qi, rlim - 1));
+  load_bop<BD>(dop, dg, p.do_ss, min(qi, rlim - 1));
   // S^T and dP^T start from -LSE / scale and -Delta of the lane's row, so
   // that P = exp2(S^T scale log2e) and dS^T = P dP^T; padding rows and rows
   // without keys start from +inf (their elements are masked).
@@ -461,8 +504,9 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
   // sparse-MLA page): the lane's half of row qi's columns, the columns of its
   // dO operands, then the two halves summed. It is stored for the dK/dV
   // kernel, which runs after this one.
-  const int qc = min(qi, p.Sq - 1);
-  const uint16_t* og = (const uint16_t*)p.o + (int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + (int64_t)qc * p.o_ss;
+  const int qc = min(qi, rlim - 1);
+  const uint16_t* og =
+      (const uint16_t*)p.o + (int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + (int64_t)(qoff + qc) * p.o_ss;
   float dacc = 0.f;
 #pragma unroll
   for (int ks = 0; ks < BD / 16; ++ks) {
@@ -471,7 +515,7 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
     for (int e = 0; e < 4; ++e) dacc = T::dot2(ov[e], dop[ks][e], dacc);
   }
   if (p.o_lo) {
-    const float* lo = p.o_lo + (int64_t)b * p.ol_sb + (int64_t)hq * p.ol_sh + (int64_t)qc * p.ol_ss;
+    const float* lo = p.o_lo + (int64_t)b * p.ol_sb + (int64_t)hq * p.ol_sh + (int64_t)(qoff + qc) * p.ol_ss;
 #pragma unroll
     for (int ks = 0; ks < BD / 16; ++ks) {
       const float4 l0 = *(const float4*)(lo + 16 * ks + 8 * h), l1 = *(const float4*)(lo + 16 * ks + 8 * h + 4);
@@ -485,10 +529,10 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
     }
   }
   const float delta = half_sum(dacc);
-  if (h == 0 && qi < p.Sq) p.delta[((int64_t)b * p.Hq + hq) * p.Sq + qi] = delta;
+  if (h == 0 && qi < rlim) p.delta[ld_index<PK>(p, b, hq, qoff, qi)] = delta;
   float s_init = INFINITY, d_init = 0.f;
   if (qi < Lq) {
-    const float l = p.lse[((int64_t)b * p.Hq + hq) * p.Sq + qi];
+    const float l = p.lse[ld_index<PK>(p, b, hq, qoff, qi)];
     s_init = l == -INFINITY ? INFINITY : -l / p.scale;
     d_init = -delta;
   }
@@ -523,7 +567,7 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
   auto dma = [&](int t, int sl) __attribute__((always_inline)) {
     const int j0 = t * TR;
     const uint16_t* base = c_head + (int64_t)j0 * c_ss;
-    const int rmax = p.Skv - 1 - j0;
+    const int rmax = klim - 1 - j0;
     const uint32_t l0 = c_lds + (uint32_t)sl * (2 * TR * BD * 2);
 #pragma unroll
     for (int n = 0; n < NPQ; ++n) lds_copy16(base, (uint32_t)min(crow[n], rmax) * c_rb + cchunk[n], l0 + n * 1024);
@@ -592,21 +636,23 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
       wait_vmem();
     sl = sl == 2 ? 0 : sl + 1;
   }
-  if (qi < p.Sq) store_t<T, BD>((uint16_t*)p.dq + (int64_t)b * p.dq_sb + (int64_t)hq * p.dq_sh, p.dq_ss, qi, dq_t, p.scale);
+  if (qi < rlim)
+    store_t<T, BD>((uint16_t*)p.dq + (int64_t)b * p.dq_sb + (int64_t)hq * p.dq_sh + (int64_t)qoff * p.dq_ss, p.dq_ss, qi,
+                   dq_t, p.scale);
 }
 
-template <class T, int BD, bool CAUSAL, bool MASK>
+template <class T, int BD, bool CAUSAL, bool MASK, bool PK = false>
 hipError_t launch_bwd_t(BwdParams& p, hipStream_t st) {
   // The dQ kernel also writes Delta, which the dK/dV kernel reads.
   const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
   if (rows > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, BD, CAUSAL, MASK>), dim3((unsigned)((p.Sq + BLKQ - 1) / BLKQ), (unsigned)(p.B * p.Hq)),
+    hipLaunchKernelGGL((bwd_dq_kernel<T, BD, CAUSAL, MASK, PK>), dim3((unsigned)((p.Sq + BLKQ - 1) / BLKQ), (unsigned)(p.B * p.Hq)),
                        dim3(64 * NWQ), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.Skv > 0 && p.B * p.Hkv > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, BD, CAUSAL, MASK>), dim3((unsigned)((p.Skv + BLK - 1) / BLK), (unsigned)(p.B * p.Hkv)),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, BD, CAUSAL, MASK, PK>), dim3((unsigned)((p.Skv + BLK - 1) / BLK), (unsigned)(p.B * p.Hkv)),
                        dim3(512), 0, st, p);
   }
   return hipGetLastError();
@@ -618,6 +664,17 @@ template <class T, int BD>
 hipError_t launch_bwd_m(bool causal, bool mask, BwdParams& p, hipStream_t st) {
   if (mask) return causal ? launch_bwd_t<T, BD, true, true>(p, st) : launch_bwd_t<T, BD, false, true>(p, st);
   return causal ? launch_bwd_t<T, BD, true, false>(p, st) : launch_bwd_t<T, BD, false, false>(p, st);
+}
+
+template <class T, int BD>
+hipError_t launch_bwd_pk(bool causal, BwdParams& p, hipStream_t st) {
+  return causal ? launch_bwd_t<T, BD, true, false, true>(p, st) : launch_bwd_t<T, BD, false, false, true>(p, st);
+}
+
+hipError_t launch_bwd_varlen(Dt dt, int d, bool causal, BwdParams& p, hipStream_t stream) {
+  if (dt == Dt::BF16)
+    return d == 64 ? launch_bwd_pk<BF16, 64>(causal, p, stream) : launch_bwd_pk<BF16, 128>(causal, p, stream);
+  return d == 64 ? launch_bwd_pk<F16, 64>(causal, p, stream) : launch_bwd_pk<F16, 128>(causal, p, stream);
 }
 
 hipError_t launch_bwd(Dt dt, int d, bool causal, bool mask, BwdParams& p, hipStream_t stream) {

@@ -114,6 +114,13 @@ struct BwdParams {
   int32_t B, Hq, Hkv, G, Sq, Skv;
   float scale;
   float scale_log2;
+  // Packed variable-length batches (nullable): batch b's query rows are rows
+  // cu_q[b] .. cu_q[b+1]-1 of q, o, dout, dq (and of the [Tq, Hq] lse and
+  // delta), its keys rows cu_k[b] .. cu_k[b+1]-1 of k, v, dk, dv; Sq and Skv
+  // are then the longest lengths, Tq and Tk the tensors' row counts.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t Tq, Tk;
 };
 
 // Kernel `name` of the run-time loaded code object (the 16-bit dense,
@@ -140,5 +147,7 @@ constexpr int kMaxDevices = 64;
 hipError_t scratch_address(float** ptr);
 hipError_t launch_topk(Dt dt, TopkParams& p, hipStream_t stream);
 hipError_t launch_bwd(Dt dt, int d, bool causal, bool mask, BwdParams& p, hipStream_t stream);
+// The backward over packed variable-length batches (p.cu_q / p.cu_k set, no mask).
+hipError_t launch_bwd_varlen(Dt dt, int d, bool causal, BwdParams& p, hipStream_t stream);
 
 }  // namespace fa

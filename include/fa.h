@@ -224,6 +224,45 @@ fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
                  const fa_tensor* dv, void* stream);
 
 /*
+ * Attention backward over a batch of packed variable-length sequences (the
+ * TND layout in which the ops-transformer FlashAttentionScoreGrad pytest page,
+ * section 5.4, runs the gradient operator: unpad_input packs the sequences
+ * and cu_seqlens marks their bounds). Per sequence exactly fa_bwd on its own
+ * rows and keys, with the formulas of that page's section 5.2; the causal
+ * mask is bottom-right aligned per sequence.
+ *
+ *  q, k, v     [Tq, Hq, D], [Tk, Hkv, D], [Tk, Hkv, Dv] as fa_fwd_varlen
+ *              (f16 or bf16, D == Dv, 64 or 128)
+ *  cu_seqlens_q, cu_seqlens_k  device int32 [B + 1], as fa_fwd_varlen
+ *              (non-decreasing, first entry 0, last entry <= Tq / Tk;
+ *              unchecked, they live in device memory; offsets past the
+ *              tensors are clamped to their last row, so no memory outside
+ *              them is touched)
+ *  max_seqlen_q, max_seqlen_k  >= the longest query and key sequence
+ *              (rows or keys of a longer sequence past them are treated as
+ *              absent)
+ *  o, o_lo, lse  the forward's outputs for these inputs (fa_fwd_varlen's
+ *              o [Tq, Hq, Dv] and lse fp32 [Tq, Hq], contiguous; o_lo NULL
+ *              or fp32 shaped like o, for the precise Delta as fa_bwd)
+ *  dout        [Tq, Hq, Dv], q's dtype
+ *  causal, scale  as fa_fwd_varlen
+ *  delta       fp32 [Tq, Hq], contiguous, caller-owned workspace (holds
+ *              Delta per row on return)
+ *  dq, dk, dv  outputs shaped like q, k, v in q's dtype (written, not
+ *              accumulated into)
+ *
+ * Rows and keys outside every sequence are not written. A sequence without
+ * keys gets dq = 0 for its rows, one without rows dk = dv = 0 for its keys.
+ * No boolean mask in this form. The library allocates nothing and enqueues
+ * two kernels on `stream`.
+ */
+fa_status fa_bwd_varlen(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                        const fa_tensor* cu_seqlens_q, const fa_tensor* cu_seqlens_k, int max_seqlen_q,
+                        int max_seqlen_k, const fa_tensor* o, const fa_tensor* o_lo, const fa_tensor* lse,
+                        const fa_tensor* dout, int causal, float scale, const fa_tensor* delta,
+                        const fa_tensor* dq, const fa_tensor* dk, const fa_tensor* dv, void* stream);
+
+/*
  * Dense attention forward over a batch of packed variable-length sequences
  * (the TND layout of the ops-transformer FlashAttentionScoreGrad pytest page,
  * section 5.4, where unpad_input packs the sequences and cu_seqlens marks

@@ -57,8 +57,8 @@ def good(B=2, Hq=4, Hkv=2, S=64, D=128, dt=fa.FA_BF16):
 
 def test_exports_every_declared_function(lib):
     names = fa.declared_functions()
-    assert {"fa_fwd", "fa_fwd_blocksparse", "fa_fwd_topk_gather", "fa_bwd", "fa_fwd_varlen", "fa_fwd_splitkv",
-            "fa_fwd_splitkv_splits", "fa_fwd_splitkv_workspace_elems", "fa_status_str", "fa_last_error",
+    assert {"fa_fwd", "fa_fwd_blocksparse", "fa_fwd_topk_gather", "fa_bwd", "fa_fwd_varlen", "fa_bwd_varlen",
+            "fa_fwd_splitkv", "fa_fwd_splitkv_splits", "fa_fwd_splitkv_workspace_elems", "fa_status_str", "fa_last_error",
             "fa_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -204,6 +204,41 @@ def test_varlen_validation(lib):
     assert vl(q=T([100, 4, 96]), k=T([120, 2, 96]), v=T([120, 2, 96]), o=T([100, 4, 96])) == "FA_ERR_UNSUPPORTED"
     assert vl(maxq=0) == "FA_OK"  # no rows: nothing launched
     assert vl(cq=T([1], fa.FA_I32), ck=T([1], fa.FA_I32)) == "FA_OK"  # B = 0
+
+
+def test_bwd_varlen_validation(lib):
+    def bv(Tq=100, Tk=120, Hq=4, Hkv=2, D=128, dt=fa.FA_BF16, nb=4, nbk=None, maxq=50, maxk=60, causal=1,
+           scale=0.1, lse=None, delta=None, o_lo=None, dk=None, q_stride=None):
+        q = T([Tq, Hq, D], dt, stride=q_stride)
+        kk = T([Tk, Hkv, D], dt)
+        lse = T([Tq, Hq], fa.FA_F32) if lse is None else lse
+        delta = T([Tq, Hq], fa.FA_F32) if delta is None else delta
+        dk = T([Tk, Hkv, D], dt) if dk is None else dk
+        return name(lib, lib.fa_bwd_varlen(R(q), R(kk), R(T([Tk, Hkv, D], dt)), R(T([nb], fa.FA_I32)),
+                                           R(T([nb if nbk is None else nbk], fa.FA_I32)), maxq, maxk,
+                                           R(T([Tq, Hq, D], dt)), R(o_lo), R(lse), R(T([Tq, Hq, D], dt)), causal,
+                                           scale, R(delta), R(T([Tq, Hq, D], dt)), R(dk), R(T([Tk, Hkv, D], dt)),
+                                           None))
+
+    assert bv(dt=fa.FA_F32) == "FA_ERR_DTYPE"
+    assert bv(nbk=5) == "FA_ERR_SHAPE"
+    assert bv(nb=0, nbk=0) == "FA_ERR_SHAPE"
+    assert bv(Hkv=3) == "FA_ERR_SHAPE"
+    assert bv(lse=T([100, 3], fa.FA_F32)) == "FA_ERR_SHAPE"
+    assert bv(delta=T([100, 4], fa.FA_BF16)) == "FA_ERR_DTYPE"
+    assert bv(delta=T([100, 4], fa.FA_F32, stride=[8, 1])) == "FA_ERR_STRIDE"
+    assert bv(dk=T([119, 2, 128])) == "FA_ERR_SHAPE"
+    assert bv(o_lo=T([100, 4, 128], fa.FA_BF16)) == "FA_ERR_DTYPE"
+    assert bv(o_lo=T([99, 4, 128], fa.FA_F32)) == "FA_ERR_SHAPE"
+    assert bv(maxq=-1) == "FA_ERR_VALUE"
+    assert bv(maxk=-1) == "FA_ERR_VALUE"
+    assert bv(causal=2) == "FA_ERR_VALUE"
+    assert bv(scale=float("inf")) == "FA_ERR_VALUE"
+    assert bv(D=96) == "FA_ERR_UNSUPPORTED"
+    assert bv(q_stride=[(1 << 22) + 128, 128, 1]) == "FA_ERR_UNSUPPORTED"
+    assert bv(maxq=0, maxk=0) == "FA_OK"  # no rows and no keys: nothing launched
+    assert bv(nb=1) == "FA_OK"  # B = 0
+    assert bv(D=64, nb=1) == "FA_OK"
 
 
 def test_splitkv_sizing_and_validation(lib):
