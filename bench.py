@@ -137,9 +137,12 @@ def workload_flops(w):
     return topk_work(w, w["idx_a"])[0]
 
 
-def make_bwd_call(w):
+def make_bwd_call(w, path="auto"):
     """Launcher of one backward (fa_bwd) of a dense workload: dO seeded and
-    synthetic, O and LSE from one forward with the exact running max."""
+    synthetic, O and LSE from one forward with the exact running max. path:
+    "ds" (dQ from the stored dS, its workspace allocated once here), "rc" (dQ
+    recomputing S and dP) or "auto" (the binding's choice for these sizes).
+    Returns (launcher, the path taken)."""
     import flashattention_online_softmax_amd as fa
     import synth
     q, k, v = (w[n].to("cuda") for n in ("q", "k", "v"))
@@ -147,8 +150,11 @@ def make_bwd_call(w):
     o, lse = fa.fa_fwd(q, k, v, scale=w["scale"], causal=w["causal"], rescale_threshold=0.0)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
-    return lambda: fa.fa_bwd(q, k, v, o, lse, dout, scale=w["scale"], causal=w["causal"], dq=dq, dk=dk, dv=dv,
-                             delta=delta)
+    B, H, S = q.shape[:3]
+    ws = fa._ds_work(q, B, H, S, k.shape[2], {"auto": "auto", "ds": True, "rc": None}[path], w["causal"])
+    call = lambda: fa.fa_bwd(q, k, v, o, lse, dout, scale=w["scale"], causal=w["causal"], dq=dq, dk=dk, dv=dv,
+                             delta=delta, ds_workspace=ws)
+    return call, ("ds" if ws is not None else "rc")
 
 
 def time_calls(call, steps, warmup, warm_seconds=1.0):
@@ -341,6 +347,8 @@ def main():
                          "for profiling one kernel")
     ap.add_argument("--threshold", type=float, default=0.0, help="rescale threshold of --only (log2 units)")
     ap.add_argument("--backward", action="store_true", help="with --only (a dense workload): time the backward")
+    ap.add_argument("--recompute", action="store_true",
+                    help="with --backward: the dQ path that recomputes S and dP instead of reading the stored dS")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the benchmark, run --steps plain device copies of this many "
                          "bytes (the reference kernel for scaling HBM byte counters)")
@@ -373,11 +381,12 @@ def main():
         fl = workload_flops(w)
         if args.backward:
             fl *= 2.5  # five products over the pairs against the forward's two
-            c = make_bwd_call(w)
+            c, _ = make_bwd_call(w, "rc" if args.recompute else "ds")
         else:
             c = make_call(w, rescale_threshold=args.threshold)
         wall, km = time_calls(c, args.steps, args.warmup, 0.3)
-        out = {"workload": args.only + ("_bwd" if args.backward else ""), "kernel_ms": round(km, 4),
+        tag = ("_bwd_recompute" if args.recompute else "_bwd") if args.backward else ""
+        out = {"workload": args.only + tag, "kernel_ms": round(km, 4),
                "tflops": round(fl / (km * 1e-3) / 1e12, 2), "rescale_threshold_log2": args.threshold}
         if w["kind"] == "topk":
             out["gbs"] = round(topk_work(w, w["idx_a"])[1] / (km * 1e-3) / 1e9, 1)
@@ -461,13 +470,21 @@ def main():
         # The backward of the headline workload (dQ, dK, dV from dO), counted
         # as five products over the causal pairs: 2.5 times the forward's flop.
         log("secondary %s backward" % args.workload)
-        cb = make_bwd_call(w)
+        names = {"ds": "stored dS", "rc": "S and dP recomputed"}
+        cb, taken = make_bwd_call(w, "auto")
         _, kmb = time_calls(cb, max(5, args.steps // 10), 2, 0.3)
         del cb
         torch.cuda.empty_cache()
+        other = "rc" if taken == "ds" else "ds"
+        cb, _ = make_bwd_call(w, other)
+        _, kmo = time_calls(cb, max(5, args.steps // 10), 2, 0.3)
+        del cb
+        torch.cuda.empty_cache()
         flb = 2.5 * flops
-        sec[args.workload + "_bwd"] = {"tflops": round(flb / (kmb * 1e-3) / 1e12, 2), "kernel_ms": round(kmb, 4),
-                                       "frac_mfma_peak": round(flb / (kmb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        for key, km_, pth in (("_bwd", kmb, taken), ("_bwd_other_path", kmo, other)):
+            sec[args.workload + key] = {"tflops": round(flb / (km_ * 1e-3) / 1e12, 2), "kernel_ms": round(km_, 4),
+                                        "frac_mfma_peak": round(flb / (km_ * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                        "dq_path": names[pth]}
         result["secondary"] = sec
         result["page_figures"] = {
             "exact_max_fwd_cost_gb200": "+~4% (sparse-MLA training forward, T=S=16384, W=2048, H=128; NVIDIA GB200)",

@@ -65,12 +65,14 @@ def load():
         lib.fa_fwd_blocksparse.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int, P, ctypes.c_float,
                                            ctypes.c_float, P, P, ctypes.c_void_p]
         lib.fa_fwd_topk_gather.argtypes = [P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_void_p]
-        lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P, P, P, P,
+        lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_float, P, P, P, P, P,
                                ctypes.c_void_p]
         lib.fa_fwd_varlen.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float,
                                       P, P, ctypes.c_void_p]
         lib.fa_bwd_varlen.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int, P, P, P, P, ctypes.c_int,
-                                      ctypes.c_float, P, P, P, P, ctypes.c_void_p]
+                                      ctypes.c_float, P, P, P, P, P, ctypes.c_void_p]
+        lib.fa_bwd_ds_workspace_elems.argtypes = [ctypes.c_int64] * 4
+        lib.fa_bwd_ds_workspace_elems.restype = ctypes.c_int64
         lib.fa_fwd_splitkv.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_int,
                                        P, P, P, ctypes.c_void_p]
         lib.fa_fwd_splitkv_noalloc.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_float, ctypes.c_float,
@@ -173,16 +175,54 @@ def fa_fwd(q, k, v, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k
     return (out, lse) if lo is None else (out, lse, lo)
 
 
+# The stored-dS backward path pays a round trip of dS through memory instead
+# of recomputing S and dP in the dQ kernel. Measured on MI355X (causal bf16,
+# D = 128) it is faster while the dS it touches stays within the 256 MB
+# last-level cache (B=2 H=16: S = 1024 -16%, S = 2048 -9%) and slower
+# beyond (S = 4096 +3%, S = 8192 +5%). "auto" takes it up to this many
+# touched bytes.
+DS_AUTO_TOUCHED_BYTES = 160 << 20
+
+
+def _ds_work(q, B, Hq, Sq, Skv, ws, causal):
+    """The dS workspace argument of the backward: "auto" allocates one when
+    the stored-dS path is the faster one for these sizes, True always, None
+    or False never (the dQ kernel recomputes S and dP); a tensor is passed
+    through."""
+    if ws is None or ws is False:
+        return None
+    if ws is True or isinstance(ws, str):
+        if ws is not True and ws != "auto":
+            raise ValueError("ds_workspace must be 'auto', True, None or a tensor")
+        n = load().fa_bwd_ds_workspace_elems(B, Hq, Sq, Skv)
+        if n <= 0:
+            return None
+        touched = 2 * B * Hq * ((Sq + 255) // 256 * 256) * ((Skv + 31) // 32 * 32) // (2 if causal else 1)
+        if ws == "auto" and touched > DS_AUTO_TOUCHED_BYTES:
+            return None
+        return torch.empty(n, dtype=q.dtype, device=q.device)
+    return ws
+
+
+def ds_workspace_elems(B, Hq, Sq, Skv):
+    """Elements of the backward's dS workspace for these sizes."""
+    return load().fa_bwd_ds_workspace_elems(B, Hq, Sq, Skv)
+
+
 def fa_bwd(q, k, v, o, lse, dout, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k=None, o_lo=None,
-           dq=None, dk=None, dv=None, delta=None, stream=None):
+           dq=None, dk=None, dv=None, delta=None, ds_workspace="auto", stream=None):
     """Gradients (dq, dk, dv) of the dense/causal/masked/GQA forward given
     its output o, its lse and the output gradient dout (f16/bf16, D = 64 or 128);
     mask and sequence lengths as fa_fwd's; o_lo (the forward's rounding
     residual) makes Delta = dO . (o + o_lo).
     delta (fp32 [B,Hq,Sq]) is the kernels' workspace; it is allocated here
-    when not given."""
+    when not given. ds_workspace: "auto" (the faster dQ path for these
+    sizes), True (dQ from the stored dS, its workspace allocated here), None
+    (dQ recomputes S and dP) or a tensor of fa_bwd_ds_workspace_elems
+    elements in q's dtype."""
     lib = load()
     _need_gpu(q, k, v, o, lse, dout, mask, seqlens_q, seqlens_k, o_lo)
+    ws = _ds_work(q, q.shape[0], q.shape[1], q.shape[2], k.shape[2], ds_workspace, causal)
     if dq is None:
         dq = torch.empty_like(q)
     if dk is None:
@@ -197,7 +237,7 @@ def fa_bwd(q, k, v, o, lse, dout, *, scale, causal=False, mask=None, seqlens_q=N
                       _ref(describe(seqlens_q)), _ref(describe(seqlens_k)), _ref(describe(o)), _ref(describe(o_lo)),
                       _ref(describe(lse)), _ref(describe(dout)), int(bool(causal)), float(scale),
                       _ref(describe(delta)), _ref(describe(dq)), _ref(describe(dk)), _ref(describe(dv)),
-                      _stream(stream)))
+                      _ref(describe(ws)), _stream(stream)))
     return dq, dk, dv
 
 
@@ -259,13 +299,16 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, *, scale, c
 
 
 def fa_bwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, o, lse, dout, *, scale,
-                  causal=False, o_lo=None, dq=None, dk=None, dv=None, delta=None, stream=None):
+                  causal=False, o_lo=None, dq=None, dk=None, dv=None, delta=None, ds_workspace="auto", stream=None):
     """Gradients (dq, dk, dv) of the packed variable-length (TND) forward:
     q [Tq,Hq,D], k/v [Tk,Hkv,D], cu_seqlens int32 [B+1] on the GPU, o / lse
     from fa_fwd_varlen, dout [Tq,Hq,Dv]. Rows and keys outside every sequence
-    are not written (the outputs allocated here start as zeros)."""
+    are not written (the outputs allocated here start as zeros).
+    ds_workspace as fa_bwd's (sized for B sequences of the longest lengths)."""
     lib = load()
     _need_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, dout, o_lo)
+    ws = _ds_work(q, cu_seqlens_q.shape[0] - 1, q.shape[1], int(max_seqlen_q), int(max_seqlen_k), ds_workspace,
+                  causal)
     if dq is None:
         dq = torch.zeros_like(q)
     if dk is None:
@@ -278,7 +321,7 @@ def fa_bwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_
                              _ref(describe(cu_seqlens_k)), int(max_seqlen_q), int(max_seqlen_k), _ref(describe(o)),
                              _ref(describe(o_lo)), _ref(describe(lse)), _ref(describe(dout)), int(bool(causal)),
                              float(scale), _ref(describe(delta)), _ref(describe(dq)), _ref(describe(dk)),
-                             _ref(describe(dv)), _stream(stream)))
+                             _ref(describe(dv)), _ref(describe(ws)), _stream(stream)))
     return dq, dk, dv
 
 

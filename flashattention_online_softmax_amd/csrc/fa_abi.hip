@@ -116,6 +116,27 @@ fa_status check_o_lo(const fa_tensor* o_lo, const fa_tensor* o) {
   return FA_OK;
 }
 
+// Optional dS^T workspace of the backward: rank 1, q's dtype, contiguous,
+// 16-byte aligned, at least fa_bwd_ds_workspace_elems(B, Hq, Sq, Skv)
+// elements. Sets p.ds and its block counts when one is given.
+fa_status check_ds_work(const fa_tensor* ds, int32_t dtype, int64_t B, int64_t Hq, int64_t Sq, int64_t Skv,
+                        fa::BwdParams& p) {
+  if (!ds || numel(ds) == 0) return FA_OK;
+  fa_status s = check_tensor("ds_workspace", ds, 1, true);
+  if (s != FA_OK) return s;
+  if ((s = check_dtype("ds_workspace", ds, dtype)) != FA_OK) return s;
+  const int64_t need = fa::bwd_ds_elems(B, Hq, Sq, Skv);
+  if (ds->shape[0] < need)
+    return fail(FA_ERR_SHAPE, "ds_workspace holds %lld elements, %lld needed", (long long)ds->shape[0],
+                (long long)need);
+  p.ds = (uint16_t*)ds->data;
+  p.ds_nrb = (int32_t)((Sq + 255) / 256);
+  p.ds_nkt = (int32_t)((Skv + 31) / 32);
+  p.ds_qp = (int32_t)((Sq + 31) / 32 * 32);
+  p.ldrec = (float*)(p.ds + fa::bwd_ds_blocks_elems(B, Hq, Sq, Skv));
+  return FA_OK;
+}
+
 fa_status hip_status(hipError_t e) {
   if (e == hipSuccess) return FA_OK;
   return fail(FA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
@@ -397,7 +418,7 @@ fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
                  const fa_tensor* seqlens_q, const fa_tensor* seqlens_k, const fa_tensor* o,
                  const fa_tensor* o_lo, const fa_tensor* lse, const fa_tensor* dout, int causal, float scale,
                  const fa_tensor* delta, const fa_tensor* dq, const fa_tensor* dk,
-                 const fa_tensor* dv, void* stream) {
+                 const fa_tensor* dv, const fa_tensor* ds_workspace, void* stream) {
   clear_error();
   fa_status s = check_bnsd(q, k, v, o, lse, scale, 0.f);
   if (s != FA_OK) return s;
@@ -469,6 +490,7 @@ fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
     p.ol_sh = o_lo->stride[1];
     p.ol_ss = o_lo->stride[2];
   }
+  if ((s = check_ds_work(ds_workspace, q->dtype, p.B, p.Hq, p.Sq, p.Skv, p)) != FA_OK) return s;
   if ((int64_t)p.B * p.Hq * p.Sq == 0 && (int64_t)p.B * p.Hkv * p.Skv == 0) return FA_OK;
   const bool has_mask = mask && numel(mask) > 0;
   return hip_status(fa::launch_bwd(to_dt(q->dtype), (int)q->shape[3], causal != 0, has_mask, p, (hipStream_t)stream));
@@ -478,7 +500,7 @@ fa_status fa_bwd_varlen(const fa_tensor* q, const fa_tensor* k, const fa_tensor*
                         const fa_tensor* cu_seqlens_k, int max_seqlen_q, int max_seqlen_k, const fa_tensor* o,
                         const fa_tensor* o_lo, const fa_tensor* lse, const fa_tensor* dout, int causal, float scale,
                         const fa_tensor* delta, const fa_tensor* dq, const fa_tensor* dk, const fa_tensor* dv,
-                        void* stream) {
+                        const fa_tensor* ds_workspace, void* stream) {
   clear_error();
   fa_status s;
   const char* names3[9] = {"q", "k", "v", "o", "dout", "dq", "dk", "dv", nullptr};
@@ -530,10 +552,11 @@ fa_status fa_bwd_varlen(const fa_tensor* q, const fa_tensor* k, const fa_tensor*
     if (ts3[t]->stride[0] > (1 << 22))
       return fail(FA_ERR_UNSUPPORTED, "%s row stride above 2^22 elements is not supported", names3[t]);
   const int64_t B = nb - 1;
-  // (With keys but no query rows the kernels still run: dk and dv are zero.)
-  if (B * Hq == 0 || ((int64_t)max_seqlen_q == 0 && (int64_t)max_seqlen_k == 0)) return FA_OK;
   fa::BwdParams p;
   memset(&p, 0, sizeof(p));
+  if ((s = check_ds_work(ds_workspace, q->dtype, B, Hq, max_seqlen_q, max_seqlen_k, p)) != FA_OK) return s;
+  // (With keys but no query rows the kernels still run: dk and dv are zero.)
+  if (B * Hq == 0 || ((int64_t)max_seqlen_q == 0 && (int64_t)max_seqlen_k == 0)) return FA_OK;
   p.q = q->data;
   p.k = k->data;
   p.v = v->data;
@@ -644,6 +667,11 @@ fa_status fa_fwd_varlen(const fa_tensor* q, const fa_tensor* k, const fa_tensor*
 
 int fa_fwd_splitkv_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int num_splits) {
   return split_plan(B, Hq, Sq, Skv, num_splits, nullptr);
+}
+
+int64_t fa_bwd_ds_workspace_elems(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv) {
+  if (B < 0 || Hq < 0 || Sq < 0 || Skv < 0) return -1;
+  return fa::bwd_ds_elems(B, Hq, Sq, Skv);
 }
 
 int64_t fa_fwd_splitkv_workspace_elems(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int64_t Dv, int num_splits) {

@@ -193,7 +193,7 @@ __device__ __forceinline__ void phase_end() {
 // with no LDS read before them); these values of step s + 2 are loaded by
 // wave 4 into registers during step s, stored into their ring slot at its
 // end, and read at the start of the M phases of step s + 2.
-template <class T, int BD, bool CAUSAL, bool MASK, bool PK>
+template <class T, int BD, bool CAUSAL, bool MASK, bool PK, bool DSW>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NB = 4;  // ring depth
   constexpr int DT = BD / 32;   // 32-wide d tiles
@@ -231,8 +231,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
-  // Query rows that can see a key of this block: i >= k0 - diag (causal).
-  const int qfirst = CAUSAL ? max(0, k0 - diag) : 0;
+  // Query rows that can see a key of this block: i >= k0 - diag (causal),
+  // swept from the multiple of 32 at or below, so that every 32 x 32 block
+  // of dS that holds a visible element is stored whole (with the dS store)
+  // and both dQ paths accumulate dK and dV in the same order.
+  const int qfirst = CAUSAL ? max(0, k0 - diag) & ~(TR - 1) : 0;
   const int nqt = (k0 < Lk && Lq > qfirst) ? (Lq - qfirst + TR - 1) / TR : 0;
   // The sweep: step s = (query head hkv G + s / nqt, tile s % nqt).
   const int nsteps = p.G * nqt;
@@ -271,6 +274,19 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
     const uint32_t l0 = c_lds + (uint32_t)sl * (2 * TR * BD * 2);
 #pragma unroll
     for (int n = 0; n < NPW; ++n) lds_copy16(base, (uint32_t)min(crow[n], rmax) * c_rb + cchunk[n], l0 + n * 1024);
+    // With the dS store, wave 0 also copies the step's 256-byte record of S
+    // and dP start values (16 lanes of 16 bytes) into the LSE / Delta ring.
+    if (DSW && wu == 0 && lane < 16)
+      lds_copy16(p.ldrec + ((int64_t)(b * p.Hq + hkv * p.G + hh) * (p.ds_qp / TR) + q0 / TR) * (2 * TR),
+                 (uint32_t)lane * 16u, lds_addr_of(sLD[sl]));
+  };
+  // Waits until this wave's copies of all but the last k issued steps are
+  // complete (wave 0 issues one more copy per step with the dS store).
+  auto wait_copies_below = [&](auto k) __attribute__((always_inline)) {
+    if (DSW && wu == 0)
+      wait_vmem_below<decltype(k)::value * (NPW + 1)>();
+    else
+      wait_vmem_below<decltype(k)::value * NPW>();
   };
   // Wave 4: lane i < 32 loads LSE of row q0 + i, lane 32 + i Delta; the
   // stored values (-LSE / scale and -Delta, the initial values of the S and
@@ -308,13 +324,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
         }
       // h_ahd, t_ahd: step 3; the copies of step 0 are complete
       if (nsteps > 2)
-        wait_vmem_below<2 * NPW>();
+        wait_copies_below(std::integral_constant<int, 2>{});
       else if (nsteps > 1)
-        wait_vmem_below<NPW>();
+        wait_copies_below(std::integral_constant<int, 1>{});
       else
         wait_vmem();
     } else {
-      if (w == 4) {
+      if (!DSW && w == 4) {
         fetch_ld(0, 0);
         put_ld(0);
         if (nsteps > 1) {
@@ -358,7 +374,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
       // This wave's copies of step s + 1 are complete (those of step s + 2
       // may still fly).
       if (s + 2 < nsteps)
-        wait_vmem_below<NPW>();
+        wait_copies_below(std::integral_constant<int, 1>{});
       else
         wait_vmem();
       phase_end();
@@ -405,10 +421,14 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
   } else {
     u32x4 db[2];  // dS(s - 1) as the B operand of the dK update
     f32x16 dp;
+    // (query head, tile) of the step whose dS is formed; only 32-key groups
+    // that hold keys of the batch are stored (the dQ product reads no other).
+    int h_ds = 0, t_ds = 0;
+    const bool ds_store = DSW && k0 + 32 * g < Lk;
     // Phase 2s: V_D(s - 1) and the reads for M_D(s); phase 2s + 1: M_D(s).
     // DS: s < nsteps; DU: s > 0.
     auto step = [&](int s, auto DS, auto DU) __attribute__((always_inline)) {
-      const bool ldw = w == 4 && s + 2 < nsteps;
+      const bool ldw = !DSW && w == 4 && s + 2 < nsteps;
       if (ldw) fetch_ld(h_ahd, t_ahd);
       if (DU) {
         float4 p4[4];
@@ -425,6 +445,18 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
         }
         db[0] = pack_b<T>(dsv, 0);
         db[1] = pack_b<T>(dsv, 1);
+        if (ds_store) {
+          // The step's 32 x 32 block of dS (one contiguous 2 KB block, key
+          // c at 64 bytes per key): rows 8 j + 4 h .. +3 of the lane's key
+          // are elements 4 j .. 4 j + 3.
+          const int q0s = qfirst + t_ds * TR;
+          const int64_t blk = (((int64_t)(b * p.Hq + hkv * p.G + h_ds) * p.ds_nrb + (q0s >> 8)) * p.ds_nkt +
+                               (k0 >> 5) + g) * 8 + ((q0s >> 5) & 7);
+          uint16_t* dst = p.ds + blk * 1024 + c * 32 + 4 * h;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) *(u32x2*)(dst + 8 * j) = u32x2{db[j >> 1][2 * (j & 1)], db[j >> 1][2 * (j & 1) + 1]};
+        }
+        advance(h_ds, t_ds);
       }
       phase_end();
       // dP starts from -Delta of its row.
@@ -641,20 +673,205 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dq_kernel(BwdParams p) {
                    dq_t, p.scale);
 }
 
+// Delta_i = dO_i . O_i (or dO_i . (O_i + o_lo_i)) in fp32 for every row the
+// dK/dV kernel reads, ahead of it, with the per-tile records of its
+// accumulator start values (the dS-store path; the other path forms Delta in
+// its dQ kernel and the dK/dV kernel loads LSE and Delta itself). BD / 8
+// consecutive lanes share a row, 8 columns each.
+template <class T, int BD, bool PK>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
+  constexpr int LPR = BD / 8;     // lanes per row
+  constexpr int RPB = 256 / LPR;  // rows per workgroup
+  const int bh = blockIdx.y, b = bh / p.Hq, hq = bh % p.Hq;
+  int Lq, Lk, qoff, koff;
+  batch_geometry<PK>(p, b, Lq, Lk, qoff, koff);
+  const int rlim = PK ? Lq : p.Sq;
+  const int rlim32 = (rlim + TR - 1) & ~(TR - 1);  // rows of the batch's start-value records
+  if ((int)blockIdx.x * RPB >= rlim32) return;
+  const int sub = threadIdx.x % LPR, i = blockIdx.x * RPB + threadIdx.x / LPR;
+  const int ic = min(i, rlim - 1);
+  const u32x4 ov = *(const u32x4*)((const uint16_t*)p.o + (int64_t)b * p.o_sb + (int64_t)hq * p.o_sh +
+                                   (int64_t)(qoff + ic) * p.o_ss + 8 * sub);
+  const u32x4 dv = *(const u32x4*)((const uint16_t*)p.dout + (int64_t)b * p.do_sb + (int64_t)hq * p.do_sh +
+                                   (int64_t)(qoff + ic) * p.do_ss + 8 * sub);
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = T::dot2(ov[e], dv[e], acc);
+  if (p.o_lo) {
+    const float* lo = p.o_lo + (int64_t)b * p.ol_sb + (int64_t)hq * p.ol_sh + (int64_t)(qoff + ic) * p.ol_ss + 8 * sub;
+    const float4 l0 = *(const float4*)lo, l1 = *(const float4*)(lo + 4);
+    const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f32x2 dd = T::unpack2(dv[e]);
+      acc = __builtin_fmaf(dd[0], lv[2 * e], acc);
+      acc = __builtin_fmaf(dd[1], lv[2 * e + 1], acc);
+    }
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (sub == 0 && i < rlim) p.delta[ld_index<PK>(p, b, hq, qoff, i)] = acc;
+  // The dK/dV kernel's start values of S (-LSE / scale; +inf for rows
+  // without keys and past the batch, whose elements it masks) and of dP
+  // (-Delta).
+  if (sub == 0 && i < rlim32) {
+    float* rec = p.ldrec + ((int64_t)(b * p.Hq + hq) * (p.ds_qp / TR) + i / TR) * (2 * TR) + i % TR;
+    const float l = i < rlim ? p.lse[ld_index<PK>(p, b, hq, qoff, i)] : -INFINITY;
+    rec[0] = l == -INFINITY ? INFINITY : l * (-1.f / p.scale);
+    rec[TR] = -(i < rlim ? acc : 0.f);
+  }
+}
+
+// dQ = scale dS K from the dS the dK/dV kernel stored: a workgroup of 8
+// waves owns 256 query rows of one head (32 per wave) and sweeps the 32-key
+// tiles its rows see. Per tile, the K tile (32 x D) and the 16 KB of dS
+// blocks of the 256 rows (contiguous in the workspace) come by LDS DMA into
+// a six-deep ring five tiles ahead; dQ^T += K^T dS^T takes both operands
+// through transposing reads, K^T as in the recomputing dQ kernel and the
+// wave's own 32 x 32 dS block (64 bytes per key, so the four keys of a
+// transposing read span all banks) in the same key order. A wave skips the
+// tiles none of its rows sees (the dK/dV kernel did not write them); masked
+// and padded elements were stored as zeros.
+template <class T, int BD, bool CAUSAL, bool PK>
+__global__ __launch_bounds__(64 * NWQ, 1) void bwd_dqg_kernel(BwdParams p) {
+  constexpr int DT = BD / 32;
+  constexpr int CK = 4 * BD;           // 16-byte chunks of a K tile (32 rows x BD)
+  constexpr int CS = 32 * BLKQ / 8;    // chunks of a dS^T tile (32 keys x 256 rows)
+  constexpr int NI = (CK + CS) / 64;   // wave copy instructions per tile (8 waves share them)
+  constexpr int SLOT = (CK + CS) * 8;  // 16-bit elements per ring slot
+  constexpr int NS = 6;                // ring slots (tiles t + 1 .. t + NS - 1 in flight)
+  __shared__ __attribute__((aligned(16))) uint16_t sbuf[NS][SLOT];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 31, h = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int lin = blockIdx.x + blockIdx.y * gridDim.x, nbh = p.B * p.Hq;
+  const int bh = lin % nbh, b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.G;
+  const int q0 = (CAUSAL ? (int)gridDim.x - 1 - lin / nbh : lin / nbh) * BLKQ;
+  int Lq, Lk, qoff, koff;
+  batch_geometry<PK>(p, b, Lq, Lk, qoff, koff);
+  if (PK && q0 >= Lq) return;
+  const int rlim = PK ? Lq : p.Sq;
+  const int klim = PK ? Lk : p.Skv;
+  const int diag = Lk - Lq;
+  const int kend = q0 >= Lq ? 0 : CAUSAL ? max(0, min(Lk, q0 + BLKQ + diag)) : Lk;
+  const int nkt = (kend + TR - 1) / TR;
+  const uint16_t* kg = (const uint16_t*)p.k + (int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh + (int64_t)koff * p.k_ss;
+  const uint16_t* dsg = p.ds + ((int64_t)(b * p.Hq + hq) * p.ds_nrb + (q0 >> 8)) * p.ds_nkt * (8 * 1024);
+  // This wave's copy instructions: u = w, w + 8, w + 16 (< NI); u < CK / 64
+  // copies K chunks 64 u + lane, the others dS^T chunks.
+  uint32_t coff[3];
+  bool cisk[3];
+  int crow[3];
+#pragma unroll
+  for (int n = 0; n < 3; ++n) {
+    const int u = wu + 8 * n, pos = 64 * u + lane;
+    cisk[n] = u < CK / 64;
+    if (cisk[n]) {
+      const int row = pos / (BD / 8);
+      crow[n] = row;
+      coff[n] = (uint32_t)(bsw<BD>(row, pos % (BD / 8)) * 16);
+    } else {
+      crow[n] = 0;
+      coff[n] = (uint32_t)(pos - CK) * 16u;
+    }
+  }
+  const int ncw = (NI - wu + 7) / 8;  // copy instructions of this wave per tile
+  const uint32_t k_rb = (uint32_t)p.k_ss * 2u;
+  const uint32_t l_base = lds_addr_of(sbuf[0]);
+  auto dma = [&](int t, int sl) __attribute__((always_inline)) {
+    const int j0 = t * TR;
+    const uint32_t l0 = l_base + (uint32_t)sl * (SLOT * 2);
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+      const int u = wu + 8 * n;
+      if (u < NI) {
+        if (cisk[n])
+          lds_copy16(kg + (int64_t)j0 * p.k_ss, (uint32_t)min(crow[n], klim - 1 - j0) * k_rb + coff[n], l0 + u * 1024);
+        else
+          lds_copy16(dsg + (int64_t)t * (8 * 1024), coff[n], l0 + u * 1024);
+      }
+    }
+  };
+  // Waits for the oldest tile in flight while NS - 2 later ones may still
+  // fly (all of them near the end of the sweep).
+  auto wait_tile = [&](bool keep_next) __attribute__((always_inline)) {
+    if (!keep_next)
+      wait_vmem();
+    else if (ncw == 3)
+      wait_vmem_below<3 * (NS - 2)>();
+    else
+      wait_vmem_below<2 * (NS - 2)>();
+  };
+  for (int t = 0; t < NS - 1 && t < nkt; ++t) dma(t, t);
+  if (nkt > 0) wait_tile(nkt >= NS - 1);
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+  const int qw0 = q0 + 32 * wu;
+  // transposing reads of the wave's dS block: keys 16 ks + 4 h + (lane &
+  // 15) / 4 and +8, rows 16 ((lane >> 4) & 1) + 4 (lane & 3) .. +3
+  const int vrow = 4 * h + ((lane & 15) >> 2);
+  const int col = 1024 * wu + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int sl = 0;
+  for (int t = 0; t < nkt; ++t) {
+    const int j0 = t * TR;
+    barrier_keep_copies();
+    // into the slot of tile t - 1, which every wave has finished
+    if (t + NS - 1 < nkt) dma(t + NS - 1, sl == 0 ? NS - 1 : sl - 1);
+    const bool active = qw0 < Lq && (!CAUSAL || j0 <= qw0 + 31 + diag);
+    if (active) {
+      const uint16_t* sK = sbuf[sl];
+      const uint16_t* sS = sbuf[sl] + CK * 8;
+#pragma unroll
+      for (int ks = 0; ks < TR / 16; ++ks) {
+        const int r0 = 16 * ks + vrow, r1 = r0 + 8;
+        const u32x2 lo = lds_read_tr16(sS + col + r0 * 32);
+        const u32x2 hi = lds_read_tr16(sS + col + r1 * 32);
+        const u32x4 bop = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] = T::mfma(tr_op<BD>(sK, dt, ks), bop, acc[dt]);
+      }
+    }
+    wait_tile(t + NS - 1 < nkt);
+    sl = sl == NS - 1 ? 0 : sl + 1;
+  }
+  const int qi = qw0 + c;
+  if (qi < rlim)
+    store_t<T, BD>((uint16_t*)p.dq + (int64_t)b * p.dq_sb + (int64_t)hq * p.dq_sh + (int64_t)qoff * p.dq_ss, p.dq_ss, qi,
+                   acc, p.scale);
+}
+
 template <class T, int BD, bool CAUSAL, bool MASK, bool PK = false>
 hipError_t launch_bwd_t(BwdParams& p, hipStream_t st) {
-  // The dQ kernel also writes Delta, which the dK/dV kernel reads.
   const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
+  const dim3 gq((unsigned)((p.Sq + BLKQ - 1) / BLKQ), (unsigned)(p.B * p.Hq));
+  const dim3 gk((unsigned)((p.Skv + BLK - 1) / BLK), (unsigned)(p.B * p.Hkv));
+  const bool keys = p.Skv > 0 && p.B * p.Hkv > 0;
+  if (p.ds) {
+    // Delta, then dK / dV storing dS, then dQ from dS.
+    if (rows > 0) {
+      constexpr int RPB = 256 / (BD / 8);
+      hipLaunchKernelGGL((bwd_delta_kernel<T, BD, PK>), dim3((unsigned)((p.ds_qp + RPB - 1) / RPB), (unsigned)(p.B * p.Hq)),
+                         dim3(256), 0, st, p);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (keys) {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, BD, CAUSAL, MASK, PK, true>), gk, dim3(512), 0, st, p);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (rows > 0) hipLaunchKernelGGL((bwd_dqg_kernel<T, BD, CAUSAL, PK>), gq, dim3(64 * NWQ), 0, st, p);
+    return hipGetLastError();
+  }
+  // The dQ kernel also writes Delta, which the dK/dV kernel reads.
   if (rows > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, BD, CAUSAL, MASK, PK>), dim3((unsigned)((p.Sq + BLKQ - 1) / BLKQ), (unsigned)(p.B * p.Hq)),
-                       dim3(64 * NWQ), 0, st, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, BD, CAUSAL, MASK, PK>), gq, dim3(64 * NWQ), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (p.Skv > 0 && p.B * p.Hkv > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, BD, CAUSAL, MASK, PK>), dim3((unsigned)((p.Skv + BLK - 1) / BLK), (unsigned)(p.B * p.Hkv)),
-                       dim3(512), 0, st, p);
-  }
+  if (keys) hipLaunchKernelGGL((bwd_dkdv_kernel<T, BD, CAUSAL, MASK, PK, false>), gk, dim3(512), 0, st, p);
   return hipGetLastError();
 }
 

@@ -121,7 +121,31 @@ struct BwdParams {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int32_t Tq, Tk;
+  // Nullable dS workspace in the input dtype, tile-major: for (batch b,
+  // query head hq), 256-row block rb, 32-key tile kt and 32-row sub-block
+  // sb, one contiguous 32 x 32 block, key-major (dS of key j, row i at
+  // element 32 (j % 32) + i % 32):
+  //   block (((b Hq + hq) ds_nrb + rb) ds_nkt + kt) 8 + sb, 1024 elements
+  // with ds_nrb = ceil(Sq / 256) and ds_nkt = ceil(Skv / 32). When set, the
+  // dK/dV kernel stores dS there and dQ = scale dS K is formed from it
+  // instead of recomputing S and dP; ds_qp = Sq rounded up to 32.
+  uint16_t* ds;
+  int32_t ds_nrb, ds_nkt, ds_qp;
+  // With ds: fp32 start values of the S and dP accumulators per 32-row tile,
+  // after the dS region of the workspace: at ((b Hq + hq) ds_qp / 32 + t) 64,
+  // 32 values -LSE / scale (+inf for rows without keys or past the batch),
+  // then 32 values -Delta.
+  float* ldrec;
 };
+
+// Elements (16-bit) of the backward's workspace for (B, Hq, Sq, Skv): the
+// dS blocks, then the per-tile start values (two fp32 per row).
+inline int64_t bwd_ds_blocks_elems(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv) {
+  return B * Hq * ((Sq + 255) / 256 * 256) * ((Skv + 31) / 32 * 32);
+}
+inline int64_t bwd_ds_elems(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv) {
+  return bwd_ds_blocks_elems(B, Hq, Sq, Skv) + B * Hq * ((Sq + 31) / 32 * 32) * 4;
+}
 
 // Kernel `name` of the run-time loaded code object (the 16-bit dense,
 // block-sparse and top-k kernels) on the current device (loaded on first use).

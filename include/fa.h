@@ -211,17 +211,35 @@ fa_status fa_fwd_topk_gather(const fa_tensor* q, const fa_tensor* k, const fa_te
  *              o_lo)
  *  dq, dk, dv  outputs shaped like q, k, v in q's dtype (written, not
  *              accumulated into)
+ *  ds_workspace  NULL, or a caller-owned rank-1 tensor in q's dtype, 16-byte
+ *              aligned, of at least fa_bwd_ds_workspace_elems(B, Hq, Sq, Skv)
+ *              elements (contents on return unspecified). With it the dK/dV
+ *              kernel stores dS (rounded to q's dtype, as it enters the dK
+ *              product) and dQ = scale dS K is a product over that stored
+ *              dS; without it the dQ kernel recomputes S and dP. The results
+ *              agree up to rounding (dV is identical).
  *
  * Every tensor's rows must start 16-byte aligned (as fa_fwd). Rows without
  * keys (LSE = -inf) contribute nothing. Returns FA_ERR_UNSUPPORTED for other
- * head dims or fp32; the library allocates nothing and enqueues two kernels
- * on `stream` (dQ with Delta, then dK and dV).
+ * head dims or fp32; the library allocates nothing. It enqueues on `stream`
+ * two kernels without ds_workspace (dQ with Delta, then dK and dV), three
+ * with it (Delta, dK and dV storing dS, then dQ).
  */
 fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* mask,
                  const fa_tensor* seqlens_q, const fa_tensor* seqlens_k, const fa_tensor* o,
                  const fa_tensor* o_lo, const fa_tensor* lse, const fa_tensor* dout, int causal, float scale,
                  const fa_tensor* delta, const fa_tensor* dq, const fa_tensor* dk,
-                 const fa_tensor* dv, void* stream);
+                 const fa_tensor* dv, const fa_tensor* ds_workspace, void* stream);
+
+/*
+ * Elements of fa_bwd's optional dS workspace for these sizes (for
+ * fa_bwd_varlen: B = number of sequences, Sq / Skv = max_seqlen_q /
+ * max_seqlen_k): B * Hq * (Sq256 * Skv32 + 4 * Sq32), with SqN and Skv32 the
+ * lengths rounded up to a multiple of N and 32: dS of every query head in
+ * contiguous 32 x 32 blocks, then two fp32 values per row (the dK/dV
+ * kernel's start values of S and dP). -1 for negative sizes.
+ */
+int64_t fa_bwd_ds_workspace_elems(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv);
 
 /*
  * Attention backward over a batch of packed variable-length sequences (the
@@ -250,17 +268,21 @@ fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
  *              Delta per row on return)
  *  dq, dk, dv  outputs shaped like q, k, v in q's dtype (written, not
  *              accumulated into)
+ *  ds_workspace  NULL, or as fa_bwd's, sized by fa_bwd_ds_workspace_elems(B,
+ *              Hq, max_seqlen_q, max_seqlen_k) (each sequence's dS is stored
+ *              padded to the longest lengths)
  *
  * Rows and keys outside every sequence are not written. A sequence without
  * keys gets dq = 0 for its rows, one without rows dk = dv = 0 for its keys.
  * No boolean mask in this form. The library allocates nothing and enqueues
- * two kernels on `stream`.
+ * two kernels on `stream` (three with ds_workspace, as fa_bwd).
  */
 fa_status fa_bwd_varlen(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
                         const fa_tensor* cu_seqlens_q, const fa_tensor* cu_seqlens_k, int max_seqlen_q,
                         int max_seqlen_k, const fa_tensor* o, const fa_tensor* o_lo, const fa_tensor* lse,
                         const fa_tensor* dout, int causal, float scale, const fa_tensor* delta,
-                        const fa_tensor* dq, const fa_tensor* dk, const fa_tensor* dv, void* stream);
+                        const fa_tensor* dq, const fa_tensor* dk, const fa_tensor* dv,
+                        const fa_tensor* ds_workspace, void* stream);
 
 /*
  * Dense attention forward over a batch of packed variable-length sequences

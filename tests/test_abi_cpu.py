@@ -58,8 +58,8 @@ def good(B=2, Hq=4, Hkv=2, S=64, D=128, dt=fa.FA_BF16):
 def test_exports_every_declared_function(lib):
     names = fa.declared_functions()
     assert {"fa_fwd", "fa_fwd_blocksparse", "fa_fwd_topk_gather", "fa_bwd", "fa_fwd_varlen", "fa_bwd_varlen",
-            "fa_fwd_splitkv", "fa_fwd_splitkv_splits", "fa_fwd_splitkv_workspace_elems", "fa_status_str", "fa_last_error",
-            "fa_version"} <= set(names)
+            "fa_bwd_ds_workspace_elems", "fa_fwd_splitkv", "fa_fwd_splitkv_splits",
+            "fa_fwd_splitkv_workspace_elems", "fa_status_str", "fa_last_error", "fa_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert lib.fa_version() == 300
@@ -158,16 +158,32 @@ def test_topk_validation(lib):
               lse=T([0, 128], fa.FA_F32)) == "FA_OK"
 
 
+def test_bwd_ds_workspace_policy(lib):
+    # "auto" takes the stored-dS path while the dS it touches (half of the
+    # blocks under the causal mask) stays within 160 MB; True always, None
+    # never. (CPU tensors: only the sizing decision is exercised here.)
+    q = torch.empty(0, dtype=torch.bfloat16)
+    assert fa._ds_work(q, 2, 16, 1024, 1024, "auto", True) is not None
+    assert fa._ds_work(q, 2, 16, 2048, 2048, "auto", True) is not None    # 134 MB touched
+    assert fa._ds_work(q, 4, 16, 2048, 2048, "auto", True) is None        # 268 MB touched
+    assert fa._ds_work(q, 2, 16, 2048, 2048, "auto", False) is None       # 268 MB touched
+    w = fa._ds_work(q, 1, 2, 100, 70, True, False)
+    assert w.numel() == lib.fa_bwd_ds_workspace_elems(1, 2, 100, 70) and w.dtype == torch.bfloat16
+    assert fa._ds_work(q, 1, 2, 100, 70, None, False) is None
+    with pytest.raises(ValueError):
+        fa._ds_work(q, 1, 2, 100, 70, "always", False)
+
+
 def test_bwd_validation(lib):
     def bw(dt=fa.FA_BF16, D=128, dq_shape=None, delta_dt=fa.FA_F32, B=2, causal=1, mask=None, sq=None, sk=None,
-           o_lo=None):
+           o_lo=None, ds=None):
         q, k, v, o, lse = good(B=B, D=D, dt=dt)
         dout = T([B, 4, 64, D], dt)
         dq = T(dq_shape or [B, 4, 64, D], dt)
         dk, dv = T([B, 2, 64, D], dt), T([B, 2, 64, D], dt)
         delta = T([B, 4, 64], delta_dt)
         return name(lib, lib.fa_bwd(R(q), R(k), R(v), R(mask), R(sq), R(sk), R(o), R(o_lo), R(lse), R(dout), causal,
-                                    0.1, R(delta), R(dq), R(dk), R(dv), None))
+                                    0.1, R(delta), R(dq), R(dk), R(dv), R(ds), None))
 
     assert bw(dt=fa.FA_F32) == "FA_ERR_UNSUPPORTED"
     assert bw(D=96) == "FA_ERR_UNSUPPORTED"
@@ -183,6 +199,17 @@ def test_bwd_validation(lib):
     assert bw(o_lo=T([2, 4, 64, 128], fa.FA_BF16)) == "FA_ERR_DTYPE"
     assert bw(o_lo=T([2, 4, 63, 128], fa.FA_F32)) == "FA_ERR_SHAPE"
     assert bw(B=0) == "FA_OK"  # nothing to do: no launch
+    # dS workspace: B * Hq * (Sq256 * Skv32 + 4 * Sq32) elements (dS blocks,
+    # then two fp32 start values per row)
+    n = lib.fa_bwd_ds_workspace_elems(2, 4, 64, 64)
+    assert n == 2 * 4 * (256 * 64 + 4 * 64)
+    assert lib.fa_bwd_ds_workspace_elems(1, 1, 33, 70) == 256 * 96 + 4 * 64
+    assert lib.fa_bwd_ds_workspace_elems(-1, 1, 1, 1) == -1
+    assert bw(ds=T([n - 1])) == "FA_ERR_SHAPE"
+    assert b"ds_workspace holds" in lib.fa_last_error()
+    assert bw(ds=T([n], fa.FA_F16)) == "FA_ERR_DTYPE"
+    assert bw(ds=T([n], data=FAKE + 8)) == "FA_ERR_STRIDE"
+    assert bw(ds=T([n]), B=0) == "FA_OK"
 
 
 def test_varlen_validation(lib):
@@ -208,7 +235,7 @@ def test_varlen_validation(lib):
 
 def test_bwd_varlen_validation(lib):
     def bv(Tq=100, Tk=120, Hq=4, Hkv=2, D=128, dt=fa.FA_BF16, nb=4, nbk=None, maxq=50, maxk=60, causal=1,
-           scale=0.1, lse=None, delta=None, o_lo=None, dk=None, q_stride=None):
+           scale=0.1, lse=None, delta=None, o_lo=None, dk=None, q_stride=None, ds=None):
         q = T([Tq, Hq, D], dt, stride=q_stride)
         kk = T([Tk, Hkv, D], dt)
         lse = T([Tq, Hq], fa.FA_F32) if lse is None else lse
@@ -218,7 +245,7 @@ def test_bwd_varlen_validation(lib):
                                            R(T([nb if nbk is None else nbk], fa.FA_I32)), maxq, maxk,
                                            R(T([Tq, Hq, D], dt)), R(o_lo), R(lse), R(T([Tq, Hq, D], dt)), causal,
                                            scale, R(delta), R(T([Tq, Hq, D], dt)), R(dk), R(T([Tk, Hkv, D], dt)),
-                                           None))
+                                           R(ds), None))
 
     assert bv(dt=fa.FA_F32) == "FA_ERR_DTYPE"
     assert bv(nbk=5) == "FA_ERR_SHAPE"
@@ -239,6 +266,10 @@ def test_bwd_varlen_validation(lib):
     assert bv(maxq=0, maxk=0) == "FA_OK"  # no rows and no keys: nothing launched
     assert bv(nb=1) == "FA_OK"  # B = 0
     assert bv(D=64, nb=1) == "FA_OK"
+    # dS workspace sized by (sequences, Hq, max_seqlen_q, max_seqlen_k)
+    assert bv(ds=T([3 * 4 * (256 * 64 + 4 * 64) - 1])) == "FA_ERR_SHAPE"
+    assert bv(ds=T([3 * 4 * (256 * 64 + 4 * 64)], fa.FA_F16)) == "FA_ERR_DTYPE"
+    assert bv(ds=T([1]), nb=1, maxq=0, maxk=0) == "FA_OK"  # B = 0: no dS to hold
 
 
 def test_splitkv_sizing_and_validation(lib):

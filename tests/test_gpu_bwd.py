@@ -1,5 +1,6 @@
-"""GPU parity of fa_bwd (dense, causal, boolean mask, GQA; f16 / bf16, D = 64 and 128) against the
-fp64 backward oracle, element by element, on seeded inputs.
+"""GPU parity of fa_bwd and fa_bwd_varlen (dense, causal, boolean mask, GQA, packed batches; f16 /
+bf16, D = 64 and 128) against the fp64 backward oracle, element by element, on seeded inputs, for
+both dQ paths: from the dS the dK/dV kernel stores, and recomputing S and dP.
 
 Per-element gate (no page states one for the backward; derived here): the GPU
 path rounds P to the 16-bit input type before dV = P^T dO, rounds dS before
@@ -74,18 +75,23 @@ def run_bwd(case, B, Hq, Hkv, Sq, Skv, dtype, causal, seed, mask_fn=None, sq=Non
     qg, kg, vg, dg, mg = gpu(q, k, v, dout, mask)
     sqg, skg = gpu(sq, sk)
     o, lse = fa.fa_fwd(qg, kg, vg, scale=scale, causal=causal, mask=mg, seqlens_q=sqg, seqlens_k=skg)
-    dq, dk, dv = fa.fa_bwd(qg, kg, vg, o, lse, dg, scale=scale, causal=causal, mask=mg, seqlens_q=sqg,
-                           seqlens_k=skg)
-    torch.cuda.synchronize()
     kw = dict(scale=scale, causal=causal, mask=mask, seqlens_q=sq, seqlens_k=sk)
     rq, rk, rv = oracle.attn_dense_bwd(q, k, v, dout, **kw)
     bq, bk, bv = oracle.attn_dense_bwd_bound(q, k, v, dout, **kw)
     G = Hq // Hkv
     aq, ak, av = underflow_scales(q, k, dout, scale)
-    for name, got, ref, bnd, n, a in (("dq", dq, rq, bq, Skv, aq), ("dk", dk, rk, bk, G * Sq, ak),
-                                      ("dv", dv, rv, bv, G * Sq, av)):
-        _check("%s_%s" % (case, name), got, ref, bnd, q.dtype, n, a)
-    return dq, dk, dv
+    out = {}
+    # both paths: dQ from the stored dS ("ds") and dQ recomputing S and dP
+    for path, ws in (("ds", True), ("rc", None)):
+        dq, dk, dv = fa.fa_bwd(qg, kg, vg, o, lse, dg, scale=scale, causal=causal, mask=mg, seqlens_q=sqg,
+                               seqlens_k=skg, ds_workspace=ws)
+        torch.cuda.synchronize()
+        for name, got, ref, bnd, n, a in (("dq", dq, rq, bq, Skv, aq), ("dk", dk, rk, bk, G * Sq, ak),
+                                          ("dv", dv, rv, bv, G * Sq, av)):
+            _check("%s_%s_%s" % (case, path, name), got, ref, bnd, q.dtype, n, a)
+        out[path] = (dq, dk, dv)
+    assert torch.equal(out["ds"][2], out["rc"][2]), case  # dV does not depend on the path
+    return out["ds"]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -170,8 +176,15 @@ def test_bwd_full_size_heads_sampled():
     scale = 1 / math.sqrt(128)
     qg, kg, vg, dg = gpu(q, k, v, dout)
     o, lse = fa.fa_fwd(qg, kg, vg, scale=scale, causal=True, rescale_threshold=0.0)
-    dq, dk, dv = fa.fa_bwd(qg, kg, vg, o, lse, dg, scale=scale, causal=True)
+    dq, dk, dv = fa.fa_bwd(qg, kg, vg, o, lse, dg, scale=scale, causal=True, ds_workspace=True)
+    dq1, dk1, dv1 = fa.fa_bwd(qg, kg, vg, o, lse, dg, scale=scale, causal=True, ds_workspace=None)
     torch.cuda.synchronize()
+    assert torch.equal(dv, dv1)
+    # the two paths differ only by rounding (Delta's summation order, dQ's)
+    for name, x, y in (("dq", dq, dq1), ("dk", dk, dk1)):
+        r = float((x.float() - y.float()).norm() / y.float().norm())
+        log("bwd_full_paths_" + name, {"rel_l2_between_paths": r})
+        assert r <= 2.0 ** -8, (name, r)
     for b, h in ((0, 0), (1, 15)):
         sl = (slice(b, b + 1), slice(h, h + 1))
         rq, rk, rv = oracle.attn_dense_bwd(q[sl], k[sl], v[sl], dout[sl], scale=scale, causal=True)
@@ -195,7 +208,8 @@ def test_bwd_sequence_lengths(causal):
     assert torch.all(dk[1, :, 150:] == 0) and torch.all(dv[2] == 0) and torch.all(dk[2] == 0)
 
 
-def test_bwd_precise_delta_from_o_lo():
+@pytest.mark.parametrize("ws", [True, None])
+def test_bwd_precise_delta_from_o_lo(ws):
     # Delta = dO . (o + o_lo) instead of dO . o: the forward's output rounding
     # no longer enters Delta (the precise dpsum of the sparse-MLA page). Peaked
     # rows (q scaled up) make Delta's error matter for dQ.
@@ -208,8 +222,9 @@ def test_bwd_precise_delta_from_o_lo():
     o, lse, lo = fa.fa_fwd(qg, kg, vg, scale=scale, causal=True, return_o_lo=True)
     d_plain = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
     d_prec = torch.empty_like(d_plain)
-    dq0, dk0, dv0 = fa.fa_bwd(qg, kg, vg, o, lse, dg, scale=scale, causal=True, delta=d_plain)
-    dq1, dk1, dv1 = fa.fa_bwd(qg, kg, vg, o, lse, dg, scale=scale, causal=True, o_lo=lo, delta=d_prec)
+    dq0, dk0, dv0 = fa.fa_bwd(qg, kg, vg, o, lse, dg, scale=scale, causal=True, delta=d_plain, ds_workspace=ws)
+    dq1, dk1, dv1 = fa.fa_bwd(qg, kg, vg, o, lse, dg, scale=scale, causal=True, o_lo=lo, delta=d_prec,
+                              ds_workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(dv0, dv1)  # dV does not use Delta
     o_ref, _ = oracle.attn_dense(q, k, v, scale=scale, causal=True)
@@ -219,7 +234,7 @@ def test_bwd_precise_delta_from_o_lo():
     rq, _, _ = oracle.attn_dense_bwd(q, k, v, dout, scale=scale, causal=True)
     r0 = float(np.linalg.norm(dq0.float().cpu().numpy() - rq) / np.linalg.norm(rq))
     r1 = float(np.linalg.norm(dq1.float().cpu().numpy() - rq) / np.linalg.norm(rq))
-    log("bwd_precise_delta", {"delta_rms_err_plain": e_plain, "delta_rms_err_o_lo": e_prec,
+    log("bwd_precise_delta_%s" % ("ds" if ws else "rc"), {"delta_rms_err_plain": e_plain, "delta_rms_err_o_lo": e_prec,
                               "dq_rel_l2_plain": r0, "dq_rel_l2_o_lo": r1})
     assert e_prec < 0.75 * e_plain
     assert r1 < r0
@@ -227,7 +242,7 @@ def test_bwd_precise_delta_from_o_lo():
 
 # ---------------------------------------------------------------- packed varlen
 
-def run_bwd_varlen(case, w, extra=3, o_lo_seed=None):
+def run_bwd_varlen(case, w, extra=3, o_lo_seed=None, ws=True):
     """fa_fwd_varlen then fa_bwd_varlen on a packed (TND) workload whose
     buffers carry `extra` trailing rows outside every sequence; each sequence
     is checked against the oracle's backward of that sequence alone (B = 1),
@@ -260,7 +275,7 @@ def run_bwd_varlen(case, w, extra=3, o_lo_seed=None):
     dv = torch.full((Tk + extra, Hkv, D), sentinel, dtype=q.dtype, device="cuda")
     delta = torch.full((Tq + extra, Hq), sentinel, dtype=torch.float32, device="cuda")
     fa.fa_bwd_varlen(qg, kg, vg, cqg, ckg, w["max_q"], max(int(lk.max()), 1), o, lse, dg, scale=w["scale"],
-                     causal=w["causal"], o_lo=lo, dq=dq, dk=dk, dv=dv, delta=delta)
+                     causal=w["causal"], o_lo=lo, dq=dq, dk=dk, dv=dv, delta=delta, ds_workspace=ws)
     torch.cuda.synchronize()
     assert torch.all(dq[Tq:] == sentinel) and torch.all(delta[Tq:] == sentinel)
     assert torch.all(dk[Tk:] == sentinel) and torch.all(dv[Tk:] == sentinel)
@@ -295,27 +310,30 @@ def run_bwd_varlen(case, w, extra=3, o_lo_seed=None):
     return dq, dk, dv
 
 
-def test_bwd_varlen_tnd_fp16_causal():
+@pytest.mark.parametrize("ws", [True, None])
+def test_bwd_varlen_tnd_fp16_causal(ws):
     # The packed TND case of the FlashAttentionScoreGrad pytest page (section
     # 5.4): four sequences of 114, 132, 14 and 287 tokens, 16 heads, D = 128,
     # fp16, causal; the gradients follow per sequence.
     w = synth.varlen(140, 4, 1, 300, 16, 16, 128, dtype="f16", causal=True, lens_q=[114, 132, 14, 287])
     w["seed"] = 140
-    run_bwd_varlen("bwd_varlen_tnd06", w)
+    run_bwd_varlen("bwd_varlen_tnd06_%s" % ("ds" if ws else "rc"), w, ws=ws)
 
 
+@pytest.mark.parametrize("ws", [True, None])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_varlen_gqa_cross_lengths(causal):
+def test_bwd_varlen_gqa_cross_lengths(causal, ws):
     # bf16, two query heads per KV head, query and key lengths that differ
     # per sequence (bottom-right causal: the first rows of the 300 / 120
     # sequence see no key), a sequence without rows and a one-row sequence.
     w = synth.varlen(150 + causal, 5, 1, 300, 8, 4, 128, dtype="bf16", causal=causal,
                      lens_q=[300, 0, 1, 200, 77], lens_k=[120, 90, 40, 200, 260])
     w["seed"] = 150 + causal
-    run_bwd_varlen("bwd_varlen_gqa_causal%d" % causal, w)
+    run_bwd_varlen("bwd_varlen_gqa_causal%d_%s" % (causal, "ds" if ws else "rc"), w, ws=ws)
 
 
-def test_bwd_varlen_d64_keyless_sequence_and_o_lo():
+@pytest.mark.parametrize("ws", [True, None])
+def test_bwd_varlen_d64_keyless_sequence_and_o_lo(ws):
     # D = 64 (its own swizzle and copy split) with a sequence that has rows
     # but no keys (LSE = -inf: dq = 0 there); then Delta read through a
     # seeded o_lo at the packed offsets (dV, which does not use Delta, must
@@ -323,6 +341,7 @@ def test_bwd_varlen_d64_keyless_sequence_and_o_lo():
     w = synth.varlen(160, 4, 1, 300, 4, 2, 64, dtype="f16", causal=False, lens_q=[150, 40, 233, 9],
                      lens_k=[170, 0, 100, 64])
     w["seed"] = 160
-    _, _, dv0 = run_bwd_varlen("bwd_varlen_d64", w)
-    _, _, dv1 = run_bwd_varlen("bwd_varlen_d64_o_lo", w, o_lo_seed=161)
+    tag = "ds" if ws else "rc"
+    _, _, dv0 = run_bwd_varlen("bwd_varlen_d64_" + tag, w, ws=ws)
+    _, _, dv1 = run_bwd_varlen("bwd_varlen_d64_o_lo_" + tag, w, o_lo_seed=161, ws=ws)
     assert torch.equal(dv0, dv1)
