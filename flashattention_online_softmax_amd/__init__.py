@@ -175,20 +175,21 @@ def fa_fwd(q, k, v, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k
     return (out, lse) if lo is None else (out, lse, lo)
 
 
-# The stored-dS backward path pays a round trip of dS through memory instead
-# of recomputing S and dP in the dQ kernel. Measured on MI355X (causal bf16,
-# D = 128) it is faster while the dS it touches stays within the 256 MB
-# last-level cache (B=2 H=16: S = 1024 -16%, S = 2048 -9%) and slower
-# beyond (S = 4096 +3%, S = 8192 +5%). "auto" takes it up to this many
-# touched bytes.
+# The stored-dS backward path (dQ from the dS the dK/dV kernel stores)
+# against the recomputing one, measured on MI355X (causal bf16, D = 128,
+# B = 2, H = 16): S = 1024 -18%, S = 2048 -11%, while the dS the sweep
+# touches fits the 256 MB last-level cache; beyond it (S = 4096, 8192, GQA,
+# non-causal) the two are within the 2-4% the hosts differ by. "auto" takes
+# the stored-dS path up to this many touched bytes (half of the blocks under
+# the causal mask) and otherwise saves the workspace.
 DS_AUTO_TOUCHED_BYTES = 160 << 20
 
 
 def _ds_work(q, B, Hq, Sq, Skv, ws, causal):
-    """The dS workspace argument of the backward: "auto" allocates one when
-    the stored-dS path is the faster one for these sizes, True always, None
-    or False never (the dQ kernel recomputes S and dP); a tensor is passed
-    through."""
+    """The dS workspace argument of the backward: "auto" allocates one while
+    the dS the sweep touches is at most DS_AUTO_TOUCHED_BYTES, True always,
+    None or False never (the dQ kernel recomputes S and dP); a tensor is
+    passed through."""
     if ws is None or ws is False:
         return None
     if ws is True or isinstance(ws, str):
@@ -216,10 +217,10 @@ def fa_bwd(q, k, v, o, lse, dout, *, scale, causal=False, mask=None, seqlens_q=N
     mask and sequence lengths as fa_fwd's; o_lo (the forward's rounding
     residual) makes Delta = dO . (o + o_lo).
     delta (fp32 [B,Hq,Sq]) is the kernels' workspace; it is allocated here
-    when not given. ds_workspace: "auto" (the faster dQ path for these
-    sizes), True (dQ from the stored dS, its workspace allocated here), None
-    (dQ recomputes S and dP) or a tensor of fa_bwd_ds_workspace_elems
-    elements in q's dtype."""
+    when not given. ds_workspace: "auto" (dQ from the stored dS while the
+    dS touched is at most DS_AUTO_TOUCHED_BYTES), True (always), None (dQ
+    recomputes S and dP) or a tensor of fa_bwd_ds_workspace_elems elements
+    in q's dtype."""
     lib = load()
     _need_gpu(q, k, v, o, lse, dout, mask, seqlens_q, seqlens_k, o_lo)
     ws = _ds_work(q, q.shape[0], q.shape[1], q.shape[2], k.shape[2], ds_workspace, causal)

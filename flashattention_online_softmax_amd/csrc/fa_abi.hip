@@ -116,11 +116,18 @@ fa_status check_o_lo(const fa_tensor* o_lo, const fa_tensor* o) {
   return FA_OK;
 }
 
-// Optional dS^T workspace of the backward: rank 1, q's dtype, contiguous,
+// Bytes of stored dS beyond which the dK/dV kernel stores it non-temporally
+// (measured on MI355X, causal bf16 D = 128: at 134 MB touched the cached
+// stores let the dQ kernel read dS from the 256 MB last-level cache and win
+// by 9%; at 269 MB they lose and the non-temporal ones win).
+constexpr int64_t kDsCachedBytes = (int64_t)192 << 20;
+
+// Optional dS workspace of the backward: rank 1, q's dtype, contiguous,
 // 16-byte aligned, at least fa_bwd_ds_workspace_elems(B, Hq, Sq, Skv)
-// elements. Sets p.ds and its block counts when one is given.
+// elements. Sets p.ds, its block counts and the store kind when one is
+// given (causal: half of the blocks are touched).
 fa_status check_ds_work(const fa_tensor* ds, int32_t dtype, int64_t B, int64_t Hq, int64_t Sq, int64_t Skv,
-                        fa::BwdParams& p) {
+                        bool causal, fa::BwdParams& p) {
   if (!ds || numel(ds) == 0) return FA_OK;
   fa_status s = check_tensor("ds_workspace", ds, 1, true);
   if (s != FA_OK) return s;
@@ -134,6 +141,8 @@ fa_status check_ds_work(const fa_tensor* ds, int32_t dtype, int64_t B, int64_t H
   p.ds_nkt = (int32_t)((Skv + 31) / 32);
   p.ds_qp = (int32_t)((Sq + 31) / 32 * 32);
   p.ldrec = (float*)(p.ds + fa::bwd_ds_blocks_elems(B, Hq, Sq, Skv));
+  const int64_t touched = 2 * fa::bwd_ds_blocks_elems(B, Hq, Sq, Skv) / (causal ? 2 : 1);
+  p.ds_nt = touched > kDsCachedBytes ? 1 : 0;
   return FA_OK;
 }
 
@@ -490,7 +499,7 @@ fa_status fa_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, con
     p.ol_sh = o_lo->stride[1];
     p.ol_ss = o_lo->stride[2];
   }
-  if ((s = check_ds_work(ds_workspace, q->dtype, p.B, p.Hq, p.Sq, p.Skv, p)) != FA_OK) return s;
+  if ((s = check_ds_work(ds_workspace, q->dtype, p.B, p.Hq, p.Sq, p.Skv, causal != 0, p)) != FA_OK) return s;
   if ((int64_t)p.B * p.Hq * p.Sq == 0 && (int64_t)p.B * p.Hkv * p.Skv == 0) return FA_OK;
   const bool has_mask = mask && numel(mask) > 0;
   return hip_status(fa::launch_bwd(to_dt(q->dtype), (int)q->shape[3], causal != 0, has_mask, p, (hipStream_t)stream));
@@ -554,7 +563,8 @@ fa_status fa_bwd_varlen(const fa_tensor* q, const fa_tensor* k, const fa_tensor*
   const int64_t B = nb - 1;
   fa::BwdParams p;
   memset(&p, 0, sizeof(p));
-  if ((s = check_ds_work(ds_workspace, q->dtype, B, Hq, max_seqlen_q, max_seqlen_k, p)) != FA_OK) return s;
+  if ((s = check_ds_work(ds_workspace, q->dtype, B, Hq, max_seqlen_q, max_seqlen_k, causal != 0, p)) != FA_OK)
+    return s;
   // (With keys but no query rows the kernels still run: dk and dv are zero.)
   if (B * Hq == 0 || ((int64_t)max_seqlen_q == 0 && (int64_t)max_seqlen_k == 0)) return FA_OK;
   p.q = q->data;

@@ -425,6 +425,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
     // that hold keys of the batch are stored (the dQ product reads no other).
     int h_ds = 0, t_ds = 0;
     const bool ds_store = DSW && k0 + 32 * g < Lk;
+    const bool ds_nt = __builtin_amdgcn_readfirstlane(p.ds_nt) != 0;
     // Phase 2s: V_D(s - 1) and the reads for M_D(s); phase 2s + 1: M_D(s).
     // DS: s < nsteps; DU: s > 0.
     auto step = [&](int s, auto DS, auto DU) __attribute__((always_inline)) {
@@ -446,15 +447,24 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdParams p) {
         db[0] = pack_b<T>(dsv, 0);
         db[1] = pack_b<T>(dsv, 1);
         if (ds_store) {
-          // The step's 32 x 32 block of dS (one contiguous 2 KB block, key
-          // c at 64 bytes per key): rows 8 j + 4 h .. +3 of the lane's key
-          // are elements 4 j .. 4 j + 3.
+          // The step's 32 x 32 block of dS: one contiguous 2 KB block, 64
+          // bytes per key, the lane's 16 rows (accumulator order: element i
+          // is row 8 (i / 4) + 4 h + i % 4) at positions 16 h + i, so each
+          // lane stores 32 contiguous bytes. Non-temporal when the stored dS
+          // outgrows the last-level cache: then it must not evict this
+          // kernel's tiles from the L2 on its way to memory; below that the
+          // dQ kernel finds it in the cache.
           const int q0s = qfirst + t_ds * TR;
           const int64_t blk = (((int64_t)(b * p.Hq + hkv * p.G + h_ds) * p.ds_nrb + (q0s >> 8)) * p.ds_nkt +
                                (k0 >> 5) + g) * 8 + ((q0s >> 5) & 7);
-          uint16_t* dst = p.ds + blk * 1024 + c * 32 + 4 * h;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) *(u32x2*)(dst + 8 * j) = u32x2{db[j >> 1][2 * (j & 1)], db[j >> 1][2 * (j & 1) + 1]};
+          u32x4* dst = (u32x4*)(p.ds + blk * 1024 + c * 32 + 16 * h);
+          if (ds_nt) {
+            __builtin_nontemporal_store(db[0], dst);
+            __builtin_nontemporal_store(db[1], dst + 1);
+          } else {
+            dst[0] = db[0];
+            dst[1] = db[1];
+          }
         }
         advance(h_ds, t_ds);
       }
@@ -729,7 +739,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 // a six-deep ring five tiles ahead; dQ^T += K^T dS^T takes both operands
 // through transposing reads, K^T as in the recomputing dQ kernel and the
 // wave's own 32 x 32 dS block (64 bytes per key, so the four keys of a
-// transposing read span all banks) in the same key order. A wave skips the
+// transposing read span all banks) in the same key order. The block holds
+// row 8 ((p % 16) / 4) + 4 (p / 16) + p % 4 at position p, so accumulator
+// column n (the lane's) is that row for p = n. A wave skips the
 // tiles none of its rows sees (the dK/dV kernel did not write them); masked
 // and padded elements were stored as zeros.
 template <class T, int BD, bool CAUSAL, bool PK>
@@ -810,7 +822,7 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dqg_kernel(BwdParams p) {
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
   const int qw0 = q0 + 32 * wu;
   // transposing reads of the wave's dS block: keys 16 ks + 4 h + (lane &
-  // 15) / 4 and +8, rows 16 ((lane >> 4) & 1) + 4 (lane & 3) .. +3
+  // 15) / 4 and +8, positions 16 ((lane >> 4) & 1) + 4 (lane & 3) .. +3
   const int vrow = 4 * h + ((lane & 15) >> 2);
   const int col = 1024 * wu + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   int sl = 0;
@@ -836,7 +848,7 @@ __global__ __launch_bounds__(64 * NWQ, 1) void bwd_dqg_kernel(BwdParams p) {
     wait_tile(t + NS - 1 < nkt);
     sl = sl == NS - 1 ? 0 : sl + 1;
   }
-  const int qi = qw0 + c;
+  const int qi = qw0 + 8 * ((c & 15) >> 2) + 4 * (c >> 4) + (c & 3);
   if (qi < rlim)
     store_t<T, BD>((uint16_t*)p.dq + (int64_t)b * p.dq_sb + (int64_t)hq * p.dq_sh + (int64_t)qoff * p.dq_ss, p.dq_ss, qi,
                    acc, p.scale);

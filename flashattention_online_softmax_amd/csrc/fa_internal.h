@@ -124,13 +124,17 @@ struct BwdParams {
   // Nullable dS workspace in the input dtype, tile-major: for (batch b,
   // query head hq), 256-row block rb, 32-key tile kt and 32-row sub-block
   // sb, one contiguous 32 x 32 block, key-major (dS of key j, row i at
-  // element 32 (j % 32) + i % 32):
+  // element 32 (j % 32) + 16 ((r >> 2) & 1) + 4 (r >> 3) + (r & 3), r = i %
+  // 32: the order in which a lane holds its rows in the accumulator):
   //   block (((b Hq + hq) ds_nrb + rb) ds_nkt + kt) 8 + sb, 1024 elements
   // with ds_nrb = ceil(Sq / 256) and ds_nkt = ceil(Skv / 32). When set, the
   // dK/dV kernel stores dS there and dQ = scale dS K is formed from it
   // instead of recomputing S and dP; ds_qp = Sq rounded up to 32.
   uint16_t* ds;
   int32_t ds_nrb, ds_nkt, ds_qp;
+  // Non-zero: store dS non-temporally (the blocks the sweep touches exceed
+  // what the last-level cache would keep for the dQ kernel).
+  int32_t ds_nt;
   // With ds: fp32 start values of the S and dP accumulators per 32-row tile,
   // after the dS region of the workspace: at ((b Hq + hq) ds_qp / 32 + t) 64,
   // 32 values -LSE / scale (+inf for rows without keys or past the batch),

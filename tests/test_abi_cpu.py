@@ -160,8 +160,8 @@ def test_topk_validation(lib):
 
 def test_bwd_ds_workspace_policy(lib):
     # "auto" takes the stored-dS path while the dS it touches (half of the
-    # blocks under the causal mask) stays within 160 MB; True always, None
-    # never. (CPU tensors: only the sizing decision is exercised here.)
+    # blocks under the causal mask) stays within DS_AUTO_TOUCHED_BYTES; True
+    # always, None never. (CPU tensors: only the sizing decision is exercised.)
     q = torch.empty(0, dtype=torch.bfloat16)
     assert fa._ds_work(q, 2, 16, 1024, 1024, "auto", True) is not None
     assert fa._ds_work(q, 2, 16, 2048, 2048, "auto", True) is not None    # 134 MB touched
