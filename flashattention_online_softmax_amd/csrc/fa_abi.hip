@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include "../../include/fa.h"
+#include "fa_bwd_params.h"
 #include "fa_internal.h"
 
 namespace {

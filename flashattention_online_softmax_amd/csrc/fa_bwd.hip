@@ -41,6 +41,7 @@
 
 #include "fa_asm.h"
 #include "fa_device.h"
+#include "fa_bwd_params.h"
 #include "fa_internal.h"
 
 namespace fa {
