@@ -348,7 +348,9 @@ def main():
     ap.add_argument("--threshold", type=float, default=0.0, help="rescale threshold of --only (log2 units)")
     ap.add_argument("--backward", action="store_true", help="with --only (a dense workload): time the backward")
     ap.add_argument("--recompute", action="store_true",
-                    help="with --backward: the dQ path that recomputes S and dP instead of reading the stored dS")
+                    help="with --backward: the dQ path that recomputes S and dP (default: the binding's choice)")
+    ap.add_argument("--stored-ds", action="store_true",
+                    help="with --backward: the dQ path that reads the dS the dK/dV kernel stores")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the benchmark, run --steps plain device copies of this many "
                          "bytes (the reference kernel for scaling HBM byte counters)")
@@ -381,15 +383,17 @@ def main():
         fl = workload_flops(w)
         if args.backward:
             fl *= 2.5  # five products over the pairs against the forward's two
-            c, _ = make_bwd_call(w, "rc" if args.recompute else "ds")
+            c, taken = make_bwd_call(w, "rc" if args.recompute else "ds" if args.stored_ds else "auto")
         else:
             c = make_call(w, rescale_threshold=args.threshold)
         wall, km = time_calls(c, args.steps, args.warmup, 0.3)
-        tag = ("_bwd_recompute" if args.recompute else "_bwd") if args.backward else ""
+        tag = "_bwd" if args.backward else ""
         out = {"workload": args.only + tag, "kernel_ms": round(km, 4),
                "tflops": round(fl / (km * 1e-3) / 1e12, 2), "rescale_threshold_log2": args.threshold}
         if w["kind"] == "topk":
             out["gbs"] = round(topk_work(w, w["idx_a"])[1] / (km * 1e-3) / 1e9, 1)
+        if args.backward:
+            out["dq_path"] = {"ds": "stored dS", "rc": "S and dP recomputed"}[taken]
         print(json.dumps(out), flush=True)
         return
 
