@@ -16,8 +16,10 @@
 // [Tq, Hq]. Rows and keys outside a batch's ranges are neither read as data
 // nor written.
 //
-// Two kernels, none of them with atomics, dQ first (it also forms and stores
-// Delta_i = dO_i . O_i in fp32, which the dK/dV kernel reads):
+// No atomics. Without a dS workspace two kernels, dQ first (it also forms
+// and stores Delta_i = dO_i . O_i in fp32, which the dK/dV kernel reads);
+// with one, three: Delta (and the dK/dV kernel's per-tile start values),
+// dK/dV storing dS, then dQ = scale dS K from the stored dS (bwd_dqg):
 //   * dkdv: a workgroup owns 128 keys of one KV head (8 waves: for each 32
 //     keys one wave computes S and P and accumulates dV, with K of its keys
 //     resident as MFMA B operands, and one computes dP and dS and
