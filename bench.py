@@ -151,7 +151,7 @@ def make_bwd_call(w, path="auto"):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
     B, H, S = q.shape[:3]
-    ws = fa._ds_work(q, B, H, S, k.shape[2], {"auto": "auto", "ds": True, "rc": None}[path], w["causal"])
+    ws = fa._ds_work(q, B, H, k.shape[1], S, k.shape[2], {"auto": "auto", "ds": True, "rc": None}[path], w["causal"])
     call = lambda: fa.fa_bwd(q, k, v, o, lse, dout, scale=w["scale"], causal=w["causal"], dq=dq, dk=dk, dv=dv,
                              delta=delta, ds_workspace=ws)
     return call, ("ds" if ws is not None else "rc")

@@ -176,20 +176,26 @@ def fa_fwd(q, k, v, *, scale, causal=False, mask=None, seqlens_q=None, seqlens_k
 
 
 # The stored-dS backward path (dQ from the dS the dK/dV kernel stores)
-# against the recomputing one, measured on MI355X (causal bf16, D = 128,
-# B = 2, H = 16): S = 1024 -18%, S = 2048 -11%, while the dS the sweep
-# touches fits the 256 MB last-level cache; beyond it (S = 4096, 8192, GQA,
-# non-causal) the two are within the 2-4% the hosts differ by. "auto" takes
-# the stored-dS path up to this many touched bytes (half of the blocks under
-# the causal mask) and otherwise saves the workspace.
+# against the recomputing one, measured on MI355X (causal bf16, D = 128):
+# faster while the dS the sweep touches fits the 256 MB last-level cache
+# (B = 2, H = 16: S = 1024 -18%, S = 2048 -11%) and while batch x heads is too
+# small to fill the GPU several times, where the longest workgroups set the
+# time (B = 1: H = 8 S = 4096 -23%, H = 4 S = 8192 -22%); on large, full
+# problems (B = 2, H = 16, S = 4096 / 8192) the two are within the 2-4% the
+# hosts differ by. "auto" takes it when the touched dS (half of the blocks
+# under the causal mask) is at most DS_AUTO_TOUCHED_BYTES or the dK/dV grid
+# (B Hkv ceil(Skv / 128) workgroups) is below DS_AUTO_FULL_GRID, and the
+# workspace stays within DS_WORKSPACE_MAX_BYTES.
 DS_AUTO_TOUCHED_BYTES = 160 << 20
+DS_AUTO_FULL_GRID = 1024
+DS_WORKSPACE_MAX_BYTES = 8 << 30
 
 
-def _ds_work(q, B, Hq, Sq, Skv, ws, causal):
-    """The dS workspace argument of the backward: "auto" allocates one while
-    the dS the sweep touches is at most DS_AUTO_TOUCHED_BYTES, True always,
-    None or False never (the dQ kernel recomputes S and dP); a tensor is
-    passed through."""
+def _ds_work(q, B, Hq, Hkv, Sq, Skv, ws, causal):
+    """The dS workspace argument of the backward: "auto" allocates one when
+    the stored-dS path is expected to be the faster one (see above), True
+    always, None or False never (the dQ kernel recomputes S and dP); a tensor
+    is passed through."""
     if ws is None or ws is False:
         return None
     if ws is True or isinstance(ws, str):
@@ -198,9 +204,11 @@ def _ds_work(q, B, Hq, Sq, Skv, ws, causal):
         n = load().fa_bwd_ds_workspace_elems(B, Hq, Sq, Skv)
         if n <= 0:
             return None
-        touched = 2 * B * Hq * ((Sq + 255) // 256 * 256) * ((Skv + 31) // 32 * 32) // (2 if causal else 1)
-        if ws == "auto" and touched > DS_AUTO_TOUCHED_BYTES:
-            return None
+        if ws == "auto":
+            touched = 2 * B * Hq * ((Sq + 255) // 256 * 256) * ((Skv + 31) // 32 * 32) // (2 if causal else 1)
+            grid = B * Hkv * ((Skv + 127) // 128)
+            if 2 * n > DS_WORKSPACE_MAX_BYTES or (touched > DS_AUTO_TOUCHED_BYTES and grid >= DS_AUTO_FULL_GRID):
+                return None
         return torch.empty(n, dtype=q.dtype, device=q.device)
     return ws
 
@@ -217,13 +225,13 @@ def fa_bwd(q, k, v, o, lse, dout, *, scale, causal=False, mask=None, seqlens_q=N
     mask and sequence lengths as fa_fwd's; o_lo (the forward's rounding
     residual) makes Delta = dO . (o + o_lo).
     delta (fp32 [B,Hq,Sq]) is the kernels' workspace; it is allocated here
-    when not given. ds_workspace: "auto" (dQ from the stored dS while the
-    dS touched is at most DS_AUTO_TOUCHED_BYTES), True (always), None (dQ
-    recomputes S and dP) or a tensor of fa_bwd_ds_workspace_elems elements
-    in q's dtype."""
+    when not given. ds_workspace: "auto" (dQ from the stored dS where that
+    path is the faster one, see DS_AUTO_TOUCHED_BYTES), True (always), None
+    (dQ recomputes S and dP) or a tensor of fa_bwd_ds_workspace_elems
+    elements in q's dtype."""
     lib = load()
     _need_gpu(q, k, v, o, lse, dout, mask, seqlens_q, seqlens_k, o_lo)
-    ws = _ds_work(q, q.shape[0], q.shape[1], q.shape[2], k.shape[2], ds_workspace, causal)
+    ws = _ds_work(q, q.shape[0], q.shape[1], k.shape[1], q.shape[2], k.shape[2], ds_workspace, causal)
     if dq is None:
         dq = torch.empty_like(q)
     if dk is None:
@@ -308,8 +316,8 @@ def fa_bwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_
     ds_workspace as fa_bwd's (sized for B sequences of the longest lengths)."""
     lib = load()
     _need_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, dout, o_lo)
-    ws = _ds_work(q, cu_seqlens_q.shape[0] - 1, q.shape[1], int(max_seqlen_q), int(max_seqlen_k), ds_workspace,
-                  causal)
+    ws = _ds_work(q, cu_seqlens_q.shape[0] - 1, q.shape[1], k.shape[1], int(max_seqlen_q), int(max_seqlen_k),
+                  ds_workspace, causal)
     if dq is None:
         dq = torch.zeros_like(q)
     if dk is None:

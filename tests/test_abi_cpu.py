@@ -160,18 +160,22 @@ def test_topk_validation(lib):
 
 def test_bwd_ds_workspace_policy(lib):
     # "auto" takes the stored-dS path while the dS it touches (half of the
-    # blocks under the causal mask) stays within DS_AUTO_TOUCHED_BYTES; True
-    # always, None never. (CPU tensors: only the sizing decision is exercised.)
+    # blocks under the causal mask) fits the cache or the dK/dV grid is below
+    # four rounds of the GPU; True always, None never. (CPU tensors: only the
+    # sizing decision is exercised here.)
     q = torch.empty(0, dtype=torch.bfloat16)
-    assert fa._ds_work(q, 2, 16, 1024, 1024, "auto", True) is not None
-    assert fa._ds_work(q, 2, 16, 2048, 2048, "auto", True) is not None    # 134 MB touched
-    assert fa._ds_work(q, 4, 16, 2048, 2048, "auto", True) is None        # 268 MB touched
-    assert fa._ds_work(q, 2, 16, 2048, 2048, "auto", False) is None       # 268 MB touched
-    w = fa._ds_work(q, 1, 2, 100, 70, True, False)
+    assert fa._ds_work(q, 2, 16, 16, 1024, 1024, "auto", True) is not None
+    assert fa._ds_work(q, 2, 16, 16, 2048, 2048, "auto", True) is not None    # 134 MB touched
+    assert fa._ds_work(q, 4, 16, 16, 2048, 2048, "auto", True) is None        # 268 MB, 1024 workgroups
+    assert fa._ds_work(q, 2, 16, 16, 4096, 4096, "auto", True) is None        # 537 MB, 1024 workgroups
+    assert fa._ds_work(q, 1, 4, 4, 8192, 8192, "auto", True) is not None      # 268 MB, 256 workgroups
+    assert fa._ds_work(q, 2, 32, 8, 4096, 4096, "auto", True) is not None     # GQA: 512 workgroups
+    assert fa._ds_work(q, 1, 2, 2, 100000, 100000, "auto", True) is None      # workspace above the cap
+    w = fa._ds_work(q, 1, 2, 2, 100, 70, True, False)
     assert w.numel() == lib.fa_bwd_ds_workspace_elems(1, 2, 100, 70) and w.dtype == torch.bfloat16
-    assert fa._ds_work(q, 1, 2, 100, 70, None, False) is None
+    assert fa._ds_work(q, 1, 2, 2, 100, 70, None, False) is None
     with pytest.raises(ValueError):
-        fa._ds_work(q, 1, 2, 100, 70, "always", False)
+        fa._ds_work(q, 1, 2, 2, 100, 70, "always", False)
 
 
 def test_bwd_validation(lib):
