@@ -780,6 +780,6 @@ const char* fa_status_str(fa_status s) {
 
 const char* fa_last_error(void) { return g_err; }
 
-int fa_version(void) { return 300; }
+int fa_version(void) { return 400; }
 
 }  // extern "C"
