@@ -279,6 +279,10 @@ def run_bwd_varlen(case, w, extra=3, o_lo_seed=None, ws=True):
     torch.cuda.synchronize()
     assert torch.all(dq[Tq:] == sentinel) and torch.all(delta[Tq:] == sentinel)
     assert torch.all(dk[Tk:] == sentinel) and torch.all(dv[Tk:] == sentinel)
+    for b in range(len(lq)):
+        if lq[b] > 0 and lk[b] == 0:  # the forward of a sequence without keys: O = 0, LSE = -inf
+            a0, a1 = int(cu_q[b]), int(cu_q[b + 1])
+            assert torch.all(o[a0:a1] == 0) and torch.all(lse[a0:a1] == float("-inf")), case
     # Delta: an fp32 sum of the D products dO O (exact in fp32) and, with
     # o_lo, D more rounded ones: within 2 D 2^-24 of the sum of magnitudes.
     ov = o[:Tq].cpu().double()
