@@ -57,6 +57,18 @@ def test_gqa_causal_mask(dtype, thr):
     run_dense("gqa_mask_%s_thr%g" % (dtype, thr), q, k, v, 1 / math.sqrt(128), True, mask, thr=thr)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_mask_gqa(D, causal):
+    # The fp32 kernel with a boolean mask that differs per query head
+    # ([1, Hq, Sq, Skv]), two query heads per KV head, Sq != Skv (bottom-right
+    # causal) and a ragged tail in both directions.
+    g, q, k, v = synth.dense_inputs(40 + causal + D, 1, 4, 2, 150, 230, D, D, "f32")
+    dens = np.array([0.05, 0.3, 0.15, 0.6])[None, :, None, None]
+    m = torch.from_numpy((g.random((1, 4, 150, 230)) < dens).astype(np.uint8))
+    run_dense("f32_mask_gqa_d%d_causal%d" % (D, causal), q, k, v, 1 / math.sqrt(D), causal, m)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_gqa_head_groups_unequal_lengths(causal):
     # Eight (batch, KV head) pairs and two query heads per KV head: the work
