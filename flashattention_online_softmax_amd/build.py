@@ -47,16 +47,17 @@ def _agprs(kernel: str) -> int:
 
 
 def _sched_strategy(kernel: str):
-    """Machine scheduler strategy of a code-object kernel, or None for the
-    default. "max-ilp" measured 0.7-0.9% faster on the dense causal BNSD
-    kernels, 2% on block-sparse and 0.4% on top-k, but 0.6-0.9% slower with a
-    boolean mask or split-KV ranges (A/B on one MI355X host), so it is set
-    on the BNSD kernels without a mask (fields m0, x0) and on top-k only."""
-    if kernel.startswith("fa_topk16_"):
-        return "max-ilp"
+    """Machine scheduler strategy of a code-object kernel. Interleaved A/B
+    on one MI355X host, against the default: "max-ilp" measured 0.7-0.9%
+    faster on the dense causal BNSD kernels and 2% on block-sparse, but
+    0.6-0.9% slower with a boolean mask or split-KV ranges; "iterative-ilp"
+    measured 0.2-1.1% faster on the masked, split-KV and packed kernels, 1.3-
+    1.5% faster than "max-ilp" on top-k and 1% slower than it on dense causal
+    S = 8192. "max-ilp" therefore goes to the BNSD kernels without a mask
+    (fields m0, x0), "iterative-ilp" to all others."""
     if re.search(r"m0s\dx0$", kernel):
         return "max-ilp"
-    return None
+    return "iterative-ilp"
 
 
 def _run(cmd, what):
