@@ -280,12 +280,13 @@ def test_splitkv_sizing_and_validation(lib):
     # sizing: ranges are multiples of 192 keys; the default fills the GPU
     assert lib.fa_fwd_splitkv_splits(1, 1, 100, 1000, 8) == 6   # 125 -> 192 keys per range
     assert lib.fa_fwd_splitkv_splits(1, 1, 100, 100, 8) == 1
-    assert lib.fa_fwd_splitkv_splits(2, 16, 4096, 4096, 0) == 1  # already >= 512 workgroups
-    assert lib.fa_fwd_splitkv_splits(1, 32, 512, 65536, 0) == 8
+    assert lib.fa_fwd_splitkv_splits(2, 16, 4096, 4096, 0) == 1  # already >= 256 workgroups
+    assert lib.fa_fwd_splitkv_splits(1, 32, 512, 65536, 0) == 4  # 64 row blocks x 4 ranges fill 256 CUs once
+    assert lib.fa_fwd_splitkv_splits(1, 32, 128, 32768, 0) == 8
     assert lib.fa_fwd_splitkv_splits(1, 1, 1, 1 << 20, 0) == 64
     assert lib.fa_fwd_splitkv_splits(1, 1, 1, 1000, 0) == 2     # at least 384 keys per range
     assert lib.fa_fwd_splitkv_splits(-1, 1, 1, 1, 0) == -1
-    assert lib.fa_fwd_splitkv_workspace_elems(1, 32, 512, 65536, 128, 0) == 8 * 32 * 512 * 129
+    assert lib.fa_fwd_splitkv_workspace_elems(1, 32, 512, 65536, 128, 0) == 4 * 32 * 512 * 129
     assert lib.fa_fwd_splitkv_workspace_elems(1, 1, 100, 100, 128, 0) == 0
     q, k, v, o, lse = good(S=2000)
 
