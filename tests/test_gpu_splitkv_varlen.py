@@ -44,6 +44,17 @@ def test_splitkv_small(dtype, causal, D):
               expect_splits=4)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,Sq,Skv,expect", [(1, 1, 30000, 32), (2, 3, 20000, 15)])
+def test_splitkv_decode_rows_default_ranges(B, Sq, Skv, expect, causal):
+    # few query rows (decode-like) with the library's range count: 8 query
+    # heads give 8 (16) workgroups per range, so 32 ranges of 960 keys (15 of
+    # 1344, the last one ragged) put one workgroup on each of 256 CUs
+    _, q, k, v = synth.dense_inputs(620 + Sq + causal, B, 8, 2, Sq, Skv, 128, 128, "bf16")
+    run_split("splitkv_decode_B%d_Sq%d_causal%d" % (B, Sq, causal), q, k, v, 1 / math.sqrt(128), causal,
+              expect_splits=expect)
+
+
 def test_splitkv_lengths_and_empty_ranges():
     # per-batch lengths: batch 1 has 700 keys, so its ranges past them are
     # empty (LSE -inf, weight 0 in the merge); batch 2 has no rows at all
