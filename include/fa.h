@@ -360,7 +360,11 @@ fa_status fa_fwd_splitkv_noalloc(const fa_tensor* q, const fa_tensor* k, const f
                                  const fa_tensor* o, const fa_tensor* lse, void* stream);
 
 /* Number of key ranges fa_fwd_splitkv uses for these sizes and num_splits
- * (-1 for negative sizes). */
+ * (-1 for negative sizes). With num_splits = 0: ceil(256 / W) ranges, W =
+ * ceil(Sq / 256) * B * Hq the workgroups of one range, so that each of the
+ * 256 compute units gets one workgroup; at most max(1, Skv / 384) and 64.
+ * Ranges are then rounded up to multiples of 192 keys and those past the
+ * keys dropped. */
 int fa_fwd_splitkv_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int num_splits);
 
 /* fp32 elements of the workspace fa_fwd_splitkv needs (0 when a single key
