@@ -6,6 +6,7 @@ import math
 import os
 
 import pytest
+import numpy as np
 import torch
 
 import flashattention_online_softmax_amd as fa
@@ -274,6 +275,23 @@ def test_bwd_varlen_validation(lib):
     assert bv(ds=T([3 * 4 * (256 * 64 + 4 * 64) - 1])) == "FA_ERR_SHAPE"
     assert bv(ds=T([3 * 4 * (256 * 64 + 4 * 64)], fa.FA_F16)) == "FA_ERR_DTYPE"
     assert bv(ds=T([1]), nb=1, maxq=0, maxk=0) == "FA_OK"  # B = 0: no dS to hold
+
+
+def test_splitkv_default_count_follows_the_documented_rule(lib):
+    # the header's rule, restated: ceil(256 / W) ranges (W = ceil(Sq / 256)
+    # B Hq workgroups per range), at most max(1, Skv / 384) and 64, ranges
+    # rounded up to multiples of 192 keys, those past the keys dropped
+    rng = np.random.default_rng(5)
+    for _ in range(400):
+        B, Hq = int(rng.integers(1, 5)), int(rng.integers(1, 65))
+        Sq, Skv = int(rng.integers(1, 3000)), int(rng.integers(1, 200000))
+        W = -(-Sq // 256) * B * Hq
+        ns = min(64, -(-256 // W), max(1, Skv // 384))
+        length = -(-(-(-Skv // ns)) // 192) * 192
+        want = -(-Skv // length)
+        got = lib.fa_fwd_splitkv_splits(B, Hq, Sq, Skv, 0)
+        assert got == want, (B, Hq, Sq, Skv, got, want)
+        assert (got - 1) * length < Skv <= got * length
 
 
 def test_splitkv_sizing_and_validation(lib):
